@@ -1,0 +1,387 @@
+// gdn_api.hip -- the C ABI of include/gdn.h: argument validation, workspace
+// carving, the packed-batch chunk table and the kernel launches.
+//
+// Data flow of gdn_chunk_fwd (all on the caller's stream):
+//   [packed batches only] chunk table  <- cu_seqlens
+//   prep   (chunk slot, head)            g, W, U          (independent chunks)
+//   scan   (Dv slice, head, sequence)    V', h, S_T       (serial over chunks)
+//   output (chunk slot, head, Dv slice)  O                (independent chunks)
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/gdn.h"
+#include "gdn_device.h"
+#include "gdn_output.h"
+#include "gdn_prep.h"
+#include "gdn_scan.h"
+#include "gdn_step.h"
+
+namespace gdn {
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool debug_sync() {
+    static const bool on = [] {
+        const char* e = std::getenv("GDN_DEBUG_SYNC");
+        return e && e[0] && e[0] != '0';
+    }();
+    return on;
+}
+
+gdn_status check_launch(hipStream_t stream) {
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+    if (debug_sync()) {
+        if (hipStreamSynchronize(stream) != hipSuccess) return GDN_ERR_HIP;
+        if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+    }
+    return GDN_OK;
+}
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta, *S0;
+    const int32_t* cu;
+    int n_seqs;
+    void* O;
+    float* S_T;
+    int B, T, H, Dk, Dv, C;
+    gdn_dtype dt;
+    unsigned char* ws;
+    hipStream_t stream;
+};
+
+// Workspace regions, in order; every region starts on a 256-byte boundary.
+struct Layout {
+    int64_t slots, N;
+    size_t g, W, U, Vp, hs, bounds, seq_slot, table, total;
+};
+
+Layout make_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C,
+                   bool varlen, int64_t n_seqs, size_t es) {
+    Layout L{};
+    const int64_t cps = (T + C - 1) / C;
+    L.N = varlen ? n_seqs : B;
+    L.slots = varlen ? cps + n_seqs : B * cps;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
+    const size_t u = (size_t)(L.slots * H);
+    L.g = take(u * C * sizeof(float));
+    L.W = take(u * C * Dk * es);
+    L.U = take(u * C * Dv * es);
+    L.Vp = take(u * Dv * C * es);
+    L.hs = take(u * Dv * Dk * es);
+    if (varlen) {
+        L.bounds = take((size_t)(n_seqs + 1) * sizeof(int));
+        L.seq_slot = take((size_t)(n_seqs + 1) * sizeof(int));
+        L.table = take((size_t)L.slots * 4 * sizeof(int));
+    }
+    L.total = off;
+    return L;
+}
+
+// Raises the dynamic LDS limit of one kernel instantiation once (gfx950
+// allows up to 160 KB per workgroup).
+template <auto Kernel>
+void allow_smem(size_t bytes) {
+    static const bool done = [bytes] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        return true;
+    }();
+    (void)done;
+}
+
+// Optional per-kernel timing: events recorded on the launch stream around each
+// kernel (table, prep, scan, output).
+struct KernelTimer {
+    hipEvent_t ev[8];
+    int n = 0;
+    bool on = false;
+    void mark(hipStream_t s) {
+        if (on && n < 8) (void)hipEventRecord(ev[n++], s);
+    }
+};
+
+template <typename T, int DK, int DV, int C>
+gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
+    const bool varlen = a.cu != nullptr;
+    const Layout L = make_layout(a.B, a.T, a.H, DK, DV, C, varlen, a.n_seqs, sizeof(T));
+    float* g_ws = reinterpret_cast<float*>(a.ws + L.g);
+    T* W_ws = reinterpret_cast<T*>(a.ws + L.W);
+    T* U_ws = reinterpret_cast<T*>(a.ws + L.U);
+    T* Vp_ws = reinterpret_cast<T*>(a.ws + L.Vp);
+    T* h_ws = reinterpret_cast<T*>(a.ws + L.hs);
+
+    SeqGeom geom{};
+    geom.C = C;
+    geom.T = a.T;
+    geom.chunks_per_seq = (a.T + C - 1) / C;
+    if (varlen) {
+        int* bounds = reinterpret_cast<int*>(a.ws + L.bounds);
+        int* seq_slot = reinterpret_cast<int*>(a.ws + L.seq_slot);
+        int* table = reinterpret_cast<int*>(a.ws + L.table);
+        tm->mark(a.stream);
+        hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(kTableThreads), 0, a.stream,
+                           a.cu, a.n_seqs, a.T, C, (int)L.slots, bounds, seq_slot, table);
+        if (gdn_status s = check_launch(a.stream)) return s;
+        tm->mark(a.stream);
+        geom.table = table;
+        geom.seq_slot = seq_slot;
+    }
+    const T* q = static_cast<const T*>(a.q);
+    const T* k = static_cast<const T*>(a.k);
+    const T* v = static_cast<const T*>(a.v);
+
+    if (L.slots > 0) {
+        using P = PrepCfg<T, DK, DV, C>;
+        constexpr auto kp = gdn_prep_kernel<T, DK, DV, C>;
+        allow_smem<kp>(P::SMEM);
+        tm->mark(a.stream);
+        hipLaunchKernelGGL(kp, dim3((unsigned)L.slots, a.H), dim3(kThreads), P::SMEM, a.stream,
+                           k, v, a.log_alpha, a.beta, geom, a.H, g_ws, W_ws, U_ws);
+        if (gdn_status s = check_launch(a.stream)) return s;
+        tm->mark(a.stream);
+    }
+    {
+        constexpr int DVT = DV >= 32 ? 32 : 16;
+        using S = ScanCfg<T, DK, DV, C, DVT>;
+        constexpr auto ks = gdn_scan_kernel<T, DK, DV, C, DVT>;
+        allow_smem<ks>(S::SMEM);
+        tm->mark(a.stream);
+        hipLaunchKernelGGL(ks, dim3(DV / DVT, a.H, (unsigned)L.N), dim3(kThreads), S::SMEM, a.stream,
+                           k, a.S0, geom, a.H, g_ws, W_ws, U_ws, Vp_ws, h_ws, a.S_T);
+        if (gdn_status s = check_launch(a.stream)) return s;
+        tm->mark(a.stream);
+    }
+    if (L.slots > 0) {
+        constexpr int DVO = DV >= 64 ? 64 : DV;
+        using O = OutCfg<T, DK, DV, C, DVO>;
+        constexpr auto ko = gdn_output_kernel<T, DK, DV, C, DVO>;
+        allow_smem<ko>(O::SMEM);
+        tm->mark(a.stream);
+        hipLaunchKernelGGL(ko, dim3((unsigned)L.slots, a.H, DV / DVO), dim3(kThreads), O::SMEM,
+                           a.stream, q, k, geom, a.H, g_ws, Vp_ws, h_ws, static_cast<T*>(a.O));
+        if (gdn_status s = check_launch(a.stream)) return s;
+        tm->mark(a.stream);
+    }
+    return GDN_OK;
+}
+
+typedef gdn_status (*FwdFn)(const FwdArgs&, KernelTimer*);
+struct Variant {
+    int dk, dv, c;
+    gdn_dtype dt;
+    FwdFn fn;
+};
+
+const Variant kVariants[] = {
+    {16, 16, 16, GDN_F32, launch_fwd<float, 16, 16, 16>},
+    {64, 64, 16, GDN_F32, launch_fwd<float, 64, 64, 16>},
+    {64, 64, 64, GDN_F32, launch_fwd<float, 64, 64, 64>},
+    {128, 128, 64, GDN_F32, launch_fwd<float, 128, 128, 64>},
+    {128, 256, 64, GDN_F32, launch_fwd<float, 128, 256, 64>},
+    {128, 128, 64, GDN_BF16, launch_fwd<bf16, 128, 128, 64>},
+    {128, 256, 64, GDN_BF16, launch_fwd<bf16, 128, 256, 64>},
+};
+
+const Variant* find_variant(int dk, int dv, int c, gdn_dtype dt) {
+    for (const Variant& v : kVariants)
+        if (v.dk == dk && v.dv == dv && v.c == c && v.dt == dt) return &v;
+    return nullptr;
+}
+
+size_t elem_size(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxElems = 0x7fffffffLL;
+
+// Host-side checks shared by the size query and the forward call.
+gdn_status check_sizes(int B, int T, int H, int Dk, int Dv, int C, bool varlen, int n_seqs,
+                       gdn_dtype dt) {
+    if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (B < 1 || T < 0 || H < 1 || H > 65535 || Dk < 1 || Dv < 1 || C < 1) return GDN_ERR_SHAPE;
+    if (varlen && (B != 1 || n_seqs < 1 || n_seqs > 65535)) return GDN_ERR_SHAPE;
+    if (!varlen && B > 65535) return GDN_ERR_SHAPE;
+    const int64_t tokens = (int64_t)B * T;
+    const int64_t dmax = Dk > Dv ? Dk : Dv;
+    if (tokens * H * dmax > kMaxElems) return GDN_ERR_SHAPE;
+    const int64_t N = varlen ? n_seqs : B;
+    if (N * H * (int64_t)Dv * Dk > kMaxElems) return GDN_ERR_SHAPE;
+    if (!find_variant(Dk, Dv, C, dt)) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" int gdn_chunk_fwd_supported(int Dk, int Dv, int C, gdn_dtype dt) {
+    return find_variant(Dk, Dv, C, dt) ? 1 : 0;
+}
+
+extern "C" size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
+                                                int n_seqs, gdn_dtype dt) {
+    const bool varlen = n_seqs > 0;
+    if (check_sizes(B, T, H, Dk, Dv, C, varlen, n_seqs, dt) != GDN_OK) return 0;
+    return make_layout(B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt)).total;
+}
+
+namespace {
+gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, const float* S0, const int32_t* cu_seqlens,
+                          int n_seqs, void* O, float* S_T, int B, int T, int H, int Dk, int Dv,
+                          int C, gdn_dtype dt, void* workspace, size_t workspace_bytes,
+                          void* stream, KernelTimer* tm) {
+    const bool varlen = cu_seqlens != nullptr;
+    // with no tokens the token tensors are never read (empty tensors may be NULL)
+    const bool has_tokens = T > 0;
+    if (has_tokens && (!q || !k || !v || !beta || !O)) return GDN_ERR_NULL;
+    if (gdn_status s = check_sizes(B, T, H, Dk, Dv, C, varlen, n_seqs, dt)) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(workspace))
+        return GDN_ERR_SHAPE;
+    const Layout L = make_layout(B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt));
+    if (L.total > 0 && !workspace) return GDN_ERR_NULL;
+    if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+    FwdArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, varlen ? n_seqs : B, O, S_T,
+              B, T, H, Dk, Dv, C, dt, static_cast<unsigned char*>(workspace),
+              static_cast<hipStream_t>(stream)};
+    (void)hipGetLastError();   // report only errors raised by this call's launches
+    return find_variant(Dk, Dv, C, dt)->fn(a, tm);
+}
+}  // namespace
+
+extern "C" gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                                    const float* log_alpha, const float* beta, const float* S0,
+                                    const int32_t* cu_seqlens, int n_seqs, void* O, float* S_T,
+                                    int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        KernelTimer off;
+        return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O, S_T, B, T, H,
+                              Dk, Dv, C, dt, workspace, workspace_bytes, stream, &off);
+    } catch (...) {
+        return GDN_ERR_INTERNAL;
+    }
+}
+
+extern "C" gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v,
+                                             const float* log_alpha, const float* beta,
+                                             const float* S0, const int32_t* cu_seqlens,
+                                             int n_seqs, void* O, float* S_T, int B, int T,
+                                             int H, int Dk, int Dv, int C, gdn_dtype dt,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream, float* kernel_ms) {
+    if (!kernel_ms) return GDN_ERR_NULL;
+    for (int i = 0; i < 4; ++i) kernel_ms[i] = 0.f;
+    try {
+        KernelTimer tm;
+        tm.on = true;
+        for (int i = 0; i < 8; ++i) {
+            if (hipEventCreate(&tm.ev[i]) != hipSuccess) {
+                for (int j = 0; j < i; ++j) (void)hipEventDestroy(tm.ev[j]);
+                return GDN_ERR_HIP;
+            }
+        }
+        gdn_status s = chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O, S_T,
+                                      B, T, H, Dk, Dv, C, dt, workspace, workspace_bytes, stream,
+                                      &tm);
+        if (s == GDN_OK && hipEventSynchronize(tm.ev[tm.n - 1]) != hipSuccess) s = GDN_ERR_HIP;
+        if (s == GDN_OK) {
+            // pairs of marks: [table], prep, scan, output (prep/output absent when T = 0)
+            const bool varlen = cu_seqlens != nullptr;
+            const bool has_chunks = tm.n >= (varlen ? 8 : 6);
+            int slot[4] = {-1, -1, -1, -1};
+            int m = 0;
+            if (varlen) slot[0] = m++;
+            if (has_chunks) slot[1] = m++;
+            slot[2] = m++;
+            if (has_chunks) slot[3] = m++;
+            for (int i = 0; i < 4; ++i) {
+                if (slot[i] < 0) continue;
+                float ms = 0.f;
+                if (hipEventElapsedTime(&ms, tm.ev[2 * slot[i]], tm.ev[2 * slot[i] + 1]) != hipSuccess)
+                    s = GDN_ERR_HIP;
+                kernel_ms[i] = ms;
+            }
+        }
+        for (int i = 0; i < 8; ++i) (void)hipEventDestroy(tm.ev[i]);
+        return s;
+    } catch (...) {
+        return GDN_ERR_INTERNAL;
+    }
+}
+
+namespace gdn {
+namespace {
+template <typename T, int DK, int DV>
+gdn_status launch_step(const void* q, const void* k, const void* v, const float* la,
+                       const float* beta, float* S, void* o, int N, int H, hipStream_t st) {
+    hipLaunchKernelGGL((gdn_step_kernel<T, DK, DV>), dim3(DV / 16, H, N), dim3(kThreads), 0, st,
+                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                       la, beta, S, static_cast<T*>(o), H);
+    return check_launch(st);
+}
+
+typedef gdn_status (*StepFn)(const void*, const void*, const void*, const float*, const float*,
+                             float*, void*, int, int, hipStream_t);
+
+template <typename T, int DK>
+StepFn pick_dv(int dv) {
+    switch (dv) {
+        case 16: return launch_step<T, DK, 16>;
+        case 64: return launch_step<T, DK, 64>;
+        case 128: return launch_step<T, DK, 128>;
+        case 256: return launch_step<T, DK, 256>;
+        default: return nullptr;
+    }
+}
+
+template <typename T>
+StepFn pick_step(int dk, int dv) {
+    switch (dk) {
+        case 16: return pick_dv<T, 16>(dv);
+        case 64: return pick_dv<T, 64>(dv);
+        case 128: return pick_dv<T, 128>(dv);
+        case 256: return pick_dv<T, 256>(dv);
+        default: return nullptr;
+    }
+}
+}  // namespace
+}  // namespace gdn
+
+extern "C" gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
+                                         const float* log_alpha, const float* beta, float* S,
+                                         void* o, int N, int H, int Dk, int Dv, gdn_dtype dt,
+                                         void* stream) {
+    try {
+        if (!q || !k || !v || !beta || !S || !o) return GDN_ERR_NULL;
+        if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+        if (N < 1 || N > 65535 || H < 1 || H > 65535 || Dk < 1 || Dv < 1) return GDN_ERR_SHAPE;
+        if ((int64_t)N * H * Dv * Dk > kMaxElems) return GDN_ERR_SHAPE;
+        StepFn fn = dt == GDN_BF16 ? pick_step<bf16>(Dk, Dv) : pick_step<float>(Dk, Dv);
+        if (!fn) return GDN_ERR_UNSUPPORTED;
+        (void)hipGetLastError();
+        return fn(q, k, v, log_alpha, beta, S, o, N, H, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return GDN_ERR_INTERNAL;
+    }
+}
+
+extern "C" const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "success";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "inconsistent, out-of-range or misaligned sizes";
+        case GDN_ERR_UNSUPPORTED: return "no compiled kernel for this (Dk, Dv, chunk, dtype)";
+        case GDN_ERR_WORKSPACE: return "workspace is smaller than required";
+        case GDN_ERR_HIP: return "a HIP launch or runtime call failed";
+        case GDN_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}

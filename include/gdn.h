@@ -1,0 +1,144 @@
+/*
+ * gdn.h -- C ABI of the chunkwise gated delta rule forward for AMD MI355X (gfx950).
+ *
+ * The operation (per independent unit = one sequence x one head):
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t
+ * with the state S of shape [Dv][Dk] (o = S q).  DeltaNet is the case alpha = 1.
+ * Definition: Qiita article by Nyysyyan on the Linear Attention lineage, section
+ * "Gated-DeltaNet" (update of S_i and the read h_i = S_i q_i); the same step order
+ * (gate, predict, delta, write, read) is spelled out in the kkkzoz blog post
+ * "linear-attention", sections "Gated DeltaNet" and "Workflow".
+ *
+ * gdn_chunk_fwd evaluates it chunk by chunk in the WY form: inside a chunk of C
+ * tokens the coupled writes are resolved by one unit-lower-triangular solve
+ * (LinearAttention系列解读(六)：DeltaNet的Chunkwise Form推导, sections 4.2-4.5; the
+ * Qiita article, sections "Gated-DeltaNet" (triangular systems for W and U) and
+ * "Chunk Computation"), and the state is carried serially from chunk to chunk.
+ * The result equals the token recurrence up to rounding; the chunk size only
+ * changes the rounding.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
+ *    to dense row-major arrays.  The caller owns every buffer, the workspace
+ *    included; the library allocates nothing and keeps no mutable global state.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
+ *    Argument errors are detected on the host before anything is enqueued and
+ *    nothing is written then.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  No C++ exception crosses this interface.
+ *  - Floating-point inputs are not checked for NaN/Inf; they propagate.
+ *  - Token-major layout: q, k [B][T][H][Dk], v and O [B][T][H][Dv]; per-token
+ *    scalars log_alpha, beta [B][T][H] (fp32); states [N][H][Dv][Dk] (fp32).
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,          /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,         /* inconsistent or out-of-range sizes */
+    GDN_ERR_UNSUPPORTED = 3,   /* (Dk, Dv, C, dtype) has no compiled kernel */
+    GDN_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than required */
+    GDN_ERR_HIP = 5,           /* a HIP launch or runtime call failed */
+    GDN_ERR_INTERNAL = 6
+} gdn_status;
+
+typedef enum {
+    GDN_F32 = 0,               /* q, k, v, O in fp32; all arithmetic in fp32 */
+    GDN_BF16 = 1               /* q, k, v, O in bf16; fp32 accumulation and state */
+} gdn_dtype;
+
+/* Compiled (Dk, Dv, C, dtype) instantiations:
+ *   (16, 16, 16, F32)  (64, 64, 16, F32)  (64, 64, 64, F32)
+ *   (128, 128, 64, BF16) (128, 256, 64, BF16) (128, 128, 64, F32) (128, 256, 64, F32)
+ * Returns 1 when the combination is compiled, 0 otherwise. */
+int gdn_chunk_fwd_supported(int Dk, int Dv, int C, gdn_dtype dt);
+
+/* Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 on bad
+ * sizes).  n_seqs is only read when cu_seqlens will be passed (B must then be
+ * 1); pass n_seqs = 0 for fixed-length batches. */
+size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
+                                     int n_seqs, gdn_dtype dt);
+
+/* Chunkwise forward over a batch.
+ *
+ *  q, k        [B][T][H][Dk] in dt.  Keys are used as given (no normalisation,
+ *              no 1/sqrt(Dk) scale: the read is o = S q).
+ *  v           [B][T][H][Dv] in dt.
+ *  log_alpha   [B][T][H] fp32, log of the per-token gate alpha in (0, 1];
+ *              NULL means alpha = 1 (DeltaNet).
+ *  beta        [B][T][H] fp32, per-token write strength (not clamped).
+ *  S0          [N][H][Dv][Dk] fp32 initial states; NULL means zero states.
+ *  cu_seqlens  NULL: the batch is N = B sequences of T tokens each.
+ *              Otherwise a DEVICE int32 array [n_seqs + 1] of prefix offsets of
+ *              n_seqs sequences packed along T (B must be 1, N = n_seqs):
+ *              sequence i is tokens cu_seqlens[i] .. cu_seqlens[i+1]-1.  It must
+ *              be non-decreasing with cu_seqlens[0] = 0 and cu_seqlens[n] = T;
+ *              the device clamps it to a monotone sequence inside [0, T] so that
+ *              no access leaves the buffers, and O rows of tokens outside every
+ *              sequence are then left unwritten.  A sequence of length 0 gets
+ *              S_T = S0.  Chunks never straddle two sequences.
+ *  O           [B][T][H][Dv] in dt: o_t for every token.
+ *  S_T         [N][H][Dv][Dk] fp32 final states; may be NULL (not written) and
+ *              may equal S0 (updated in place).
+ *  C           chunk size (16 or 64, see the instantiation list).
+ *  workspace   device buffer of at least gdn_chunk_fwd_workspace_bytes(...)
+ *              bytes, 256-byte aligned; its contents on entry are ignored and on
+ *              return hold intermediates (no stable layout).  Two calls that
+ *              overlap in time must not share a workspace.
+ *  stream      hipStream_t to enqueue on.
+ * With T = 0 nothing but S_T = S0 is computed and q, k, v, beta, O (and the
+ * workspace, whose required size may then be 0) may be NULL.
+ * Errors: GDN_ERR_NULL (q, k, v, beta, O or workspace NULL), GDN_ERR_SHAPE
+ * (B, H < 1, T < 0, n_seqs < 1 or B != 1 with cu_seqlens, more than 2^31-1
+ * elements in a tensor, q/k/v/O/workspace not 16-byte aligned),
+ * GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP. */
+gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *beta, const float *S0,
+                         const int32_t *cu_seqlens, int n_seqs,
+                         void *O, float *S_T,
+                         int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Measurement variant of gdn_chunk_fwd: same arguments and result, plus
+ * kernel_ms, a HOST array of 4 floats that receives the device time in
+ * milliseconds of each kernel of this call, taken with HIP events recorded
+ * on `stream` around every launch: [0] packed-batch chunk table (0 when
+ * cu_seqlens is NULL), [1] prep, [2] scan, [3] output (prep and output are 0
+ * when there are no tokens).  Unlike gdn_chunk_fwd it BLOCKS until the call's
+ * work on `stream` has finished.  Errors: as gdn_chunk_fwd, plus GDN_ERR_NULL
+ * when kernel_ms is NULL. */
+gdn_status gdn_chunk_fwd_profiled(const void *q, const void *k, const void *v,
+                                  const float *log_alpha, const float *beta, const float *S0,
+                                  const int32_t *cu_seqlens, int n_seqs,
+                                  void *O, float *S_T,
+                                  int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
+                                  void *workspace, size_t workspace_bytes, void *stream,
+                                  float *kernel_ms);
+
+/* One token per sequence (decoding).  Updates the state in place and reads it:
+ *     S <- alpha S (I - beta k k^T) + beta v k^T,   o = S q     (same section).
+ *  q, k [N][H][Dk] in dt; v [N][H][Dv] in dt; log_alpha (nullable: alpha = 1)
+ *  and beta [N][H] fp32; S [N][H][Dv][Dk] fp32, read and written in place;
+ *  o [N][H][Dv] in dt.
+ * Supported (Dk, Dv): any with Dk, Dv in {16, 64, 128, 256}, both dtypes.
+ * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP. */
+gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v,
+                              const float *log_alpha, const float *beta,
+                              float *S, void *o,
+                              int N, int H, int Dk, int Dv, gdn_dtype dt, void *stream);
+
+/* Static English text for a status code (never NULL). */
+const char *gdn_status_string(gdn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -60,6 +60,15 @@ def _load():
 
 
 
+def default_threads() -> int:
+    """Worker threads when none are asked for: GDN_ORACLE_THREADS if set, else
+    min(cores, 16) -- the CPU share of one GPU on the measurement machines."""
+    env = os.environ.get("GDN_ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
 def _f64(x) -> Optional[np.ndarray]:
     """Exact upcast of a CPU tensor / array (fp32 or bf16) to contiguous fp64."""
     if x is None:
@@ -113,6 +122,8 @@ def forward(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
         assert s0.shape == (N, H, Dv, Dk)
     O = np.zeros((B, T, H, Dv), dtype=np.float64)
     S_T = np.zeros((N, H, Dv, Dk), dtype=np.float64)
+    if n_threads <= 0:
+        n_threads = default_threads()
     rc = (lib or _load()).gdn_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
                                     _ptr(cu), N, B, T, H, Dk, Dv, _ptr(O), _ptr(S_T),
                                     int(n_threads), 1 if no_erase else 0)

@@ -1,0 +1,123 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before touching the GPU (no compute call
+is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gated_delta_rule_16_amd as gdn
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn.so is not built (run __graft_entry__.build())")
+    return gdn.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gdn_chunk_fwd", "gdn_recurrent_step", "gdn_chunk_fwd_workspace_bytes",
+              "gdn_status_string", "gdn_chunk_fwd_supported"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.gdn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.gdn_status_string(99).decode() == "unknown status"
+
+
+def test_supported_instantiations(lib):
+    yes = [(16, 16, 16, F32), (64, 64, 16, F32), (64, 64, 64, F32), (128, 128, 64, BF16),
+           (128, 256, 64, BF16), (128, 128, 64, F32), (128, 256, 64, F32)]
+    for a in yes:
+        assert lib.gdn_chunk_fwd_supported(*a) == 1, a
+    for a in [(128, 128, 32, BF16), (64, 64, 64, BF16), (96, 96, 64, F32), (128, 128, 64, 7)]:
+        assert lib.gdn_chunk_fwd_supported(*a) == 0, a
+
+
+def test_workspace_bytes(lib):
+    f = lib.gdn_chunk_fwd_workspace_bytes
+    a = f(4, 4096, 16, 128, 128, 64, 0, BF16)
+    b = f(4, 4096, 16, 128, 128, 64, 0, F32)
+    assert a > 0 and b > a
+    # at least the per-chunk intermediates: g (fp32), W, U, V', chunk-start state
+    slots, H, C, Dk, Dv = 4 * 64, 16, 64, 128, 128
+    assert a >= slots * H * (C * 4 + 2 * (C * Dk + 2 * C * Dv + Dv * Dk))
+    assert f(1, 1000, 16, 128, 256, 64, 5, BF16) > 0          # packed batch
+    assert f(1, 0, 4, 64, 64, 64, 0, F32) >= 0                # empty sequence
+    assert f(0, 128, 1, 16, 16, 16, 0, F32) == 0              # bad B
+    assert f(2, 128, 1, 16, 16, 16, 3, F32) == 0              # packed needs B = 1
+    assert f(1, 128, 1, 96, 96, 64, 0, F32) == 0              # unsupported size
+    assert f(1, 1 << 30, 16, 128, 128, 64, 0, BF16) == 0      # > 2^31 elements
+
+
+def _fwd(lib, **kw):
+    """gdn_chunk_fwd with fake, never dereferenced pointers (argument checks
+    return before any HIP call)."""
+    p = ctypes.c_void_p(1 << 20)       # 16-byte aligned dummy address
+    a = dict(q=p, k=p, v=p, la=None, beta=p, S0=None, cu=None, n=0, O=p, S_T=None,
+             B=1, T=128, H=1, Dk=16, Dv=16, C=16, dt=F32, ws=p, wsb=1 << 40, st=None)
+    a.update(kw)
+    return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["la"], a["beta"], a["S0"], a["cu"], a["n"],
+                             a["O"], a["S_T"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"], a["C"],
+                             a["dt"], a["ws"], a["wsb"], a["st"])
+
+
+def test_chunk_fwd_argument_errors(lib):
+    for name in ("q", "k", "v", "beta", "O", "ws"):
+        assert _fwd(lib, **{name: None}) == GDN_ERR_NULL, name
+    assert _fwd(lib, B=0) == GDN_ERR_SHAPE
+    assert _fwd(lib, H=0) == GDN_ERR_SHAPE
+    assert _fwd(lib, T=-1) == GDN_ERR_SHAPE
+    assert _fwd(lib, cu=ctypes.c_void_p(1 << 20), n=0) == GDN_ERR_SHAPE     # packed, no sequences
+    assert _fwd(lib, cu=ctypes.c_void_p(1 << 20), n=2, B=2) == GDN_ERR_SHAPE
+    assert _fwd(lib, Dk=32, Dv=32) == GDN_ERR_UNSUPPORTED
+    assert _fwd(lib, C=32) == GDN_ERR_UNSUPPORTED
+    assert _fwd(lib, dt=BF16) == GDN_ERR_UNSUPPORTED          # (16, 16, 16) exists in fp32 only
+    assert _fwd(lib, dt=5) == GDN_ERR_UNSUPPORTED
+    assert _fwd(lib, wsb=16) == GDN_ERR_WORKSPACE
+    assert _fwd(lib, q=ctypes.c_void_p((1 << 20) + 4)) == GDN_ERR_SHAPE      # misaligned
+    need = lib.gdn_chunk_fwd_workspace_bytes(1, 128, 1, 16, 16, 16, 0, F32)
+    assert _fwd(lib, wsb=need - 1) == GDN_ERR_WORKSPACE
+
+
+def test_recurrent_step_argument_errors(lib):
+    p = ctypes.c_void_p(1 << 20)
+    f = lib.gdn_recurrent_step
+    assert f(None, p, p, None, p, p, p, 1, 1, 16, 16, F32, None) == GDN_ERR_NULL
+    assert f(p, p, p, None, None, p, p, 1, 1, 16, 16, F32, None) == GDN_ERR_NULL
+    assert f(p, p, p, None, p, None, p, 1, 1, 16, 16, F32, None) == GDN_ERR_NULL
+    assert f(p, p, p, None, p, p, p, 0, 1, 16, 16, F32, None) == GDN_ERR_SHAPE
+    assert f(p, p, p, None, p, p, p, 1, 1, 48, 16, F32, None) == GDN_ERR_UNSUPPORTED
+    assert f(p, p, p, None, p, p, p, 1, 1, 16, 16, 9, None) == GDN_ERR_UNSUPPORTED
+
+
+def test_python_binding_fails_loudly_without_gpu_tensors(lib):
+    import torch
+    import gated_delta_rule_16_amd as gdn
+    x = torch.zeros(1, 16, 1, 16)
+    b = torch.zeros(1, 16, 1)
+    with pytest.raises(ValueError):
+        gdn.gdn_chunk_fwd(x, x, x, None, b, chunk_size=16, workspace=None,
+                          O=torch.zeros(1, 16, 1, 16), S_T=torch.zeros(1, 1, 16, 16))

@@ -1,0 +1,72 @@
+"""Per-chunk intermediates of the prep kernel, read back from the workspace.
+
+The workspace layout is internal (the header promises none); this test
+mirrors the library's current carving to inspect g, W and U of every chunk
+and compares them with a dense numpy fp64 evaluation of the chunk algebra
+(row form, one chunk of n <= C tokens, padded rows act as zero tokens):
+  g = cumsum(log alpha),  A = strict_lower(diag(beta) (K K^T o exp(g_i - g_j)))
+  T = (I + A)^-1 (dense inverse),  W = T diag(beta exp(g)) K,  U = T diag(beta) V
+and checks that T is unit lower triangular with det(I + A) = 1.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_16_amd as gdn
+from gated_delta_rule_16_amd.inputs import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+def chunk_algebra(K, V, beta, la):
+    n = K.shape[0]
+    g = np.cumsum(la)
+    Gam = np.exp(g[:, None] - g[None, :])
+    A = np.tril(beta[:, None] * (K @ K.T) * Gam, -1)
+    IA = np.eye(n) + A
+    T = np.linalg.inv(IA)
+    assert np.allclose(np.diag(T), 1.0) and np.allclose(np.triu(T, 1), 0.0)
+    assert abs(np.linalg.det(IA) - 1.0) < 1e-9
+    W = T @ np.diag(beta * np.exp(g)) @ K
+    U = T @ np.diag(beta) @ V
+    return g, W, U
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv,C,tol", [("f32", 64, 64, 64, 1e-5), ("bf16", 128, 128, 64, 2e-2)])
+def test_prep_intermediates(dtype, Dk, Dv, C, tol):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B, T, H = 1, 150, 2
+    inp = make_inputs(B=B, T=T, H=H, Dk=Dk, Dv=Dv, dtype=dtype, gated=True, s0=True, seed=91)
+    d = inp.to("cuda:0")
+    es = 4 if dtype == "f32" else 2
+    nbytes = gdn.gdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, C, 0, d.q.dtype)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
+    gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, chunk_size=C, workspace=ws)
+    torch.cuda.synchronize()
+    cps = (T + C - 1) // C
+    u = B * cps * H
+    off_g = 0
+    off_w = _align(off_g + u * C * 4)
+    off_u = _align(off_w + u * C * Dk * es)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    wsc = ws.cpu()
+    g_all = wsc[off_g:off_g + u * C * 4].view(torch.float32).view(cps, H, C).double().numpy()
+    W_all = wsc[off_w:off_w + u * C * Dk * es].view(tdt).view(cps, H, C, Dk).double().numpy()
+    U_all = wsc[off_u:off_u + u * C * Dv * es].view(tdt).view(cps, H, C, Dv).double().numpy()
+    for c in range(cps):
+        t0, n = c * C, min(C, T - c * C)
+        for h in range(H):
+            K = inp.k[0, t0:t0 + n, h].double().numpy()
+            V = inp.v[0, t0:t0 + n, h].double().numpy()
+            be = inp.beta[0, t0:t0 + n, h].double().numpy()
+            la = inp.log_alpha[0, t0:t0 + n, h].double().numpy()
+            g, W, U = chunk_algebra(K, V, be, la)
+            assert np.abs(g_all[c, h, :n] - g).max() < 1e-5
+            assert np.abs(W_all[c, h, :n] - W).max() / np.abs(W).max() < tol, (c, h, "W")
+            assert np.abs(U_all[c, h, :n] - U).max() / np.abs(U).max() < tol, (c, h, "U")
+            assert not np.any(W_all[c, h, n:]) and not np.any(U_all[c, h, n:]), "padded rows"

@@ -1,0 +1,255 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on the GPU.
+
+Tolerances (max relative error per tensor, ||x - r||_inf / ||r||_inf, O and
+S_T separately): 1e-4 for the fp32 path, 2e-2 for bf16 inputs with fp32
+accumulation and state.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import oracle  # noqa: E402
+import gated_delta_rule_16_amd as gdn  # noqa: E402
+from gated_delta_rule_16_amd.inputs import WORKLOADS, make_inputs, workload_inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+def rel(x, r):
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    assert x.shape == r.shape, (x.shape, r.shape)
+    if x.size == 0:
+        return 0.0
+    return float(np.abs(x - r).max() / max(np.abs(r).max(), 1e-30))
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_gpu(inp, C=None, **kw):
+    d = inp.to(DEV)
+    O, S = gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, d.cu_seqlens,
+                             chunk_size=C or inp.C, **kw)
+    torch.cuda.synchronize()
+    return O.double().cpu().numpy(), None if S is None else S.double().cpu().numpy()
+
+
+def run_oracle(inp, heads=None):
+    """Oracle outputs; ``heads`` restricts it to a sample of heads (units are independent)."""
+    sl = (lambda t: t) if heads is None else (lambda t: None if t is None else t[:, :, heads])
+    s0 = inp.S0 if (heads is None or inp.S0 is None) else inp.S0[:, heads]
+    return oracle.forward(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.log_alpha), sl(inp.beta), s0,
+                          inp.cu_seqlens)
+
+
+def check(inp, dtype, C=None, heads=None, tag=""):
+    say(f"[gpu] {tag} shape q={tuple(inp.q.shape)} v={tuple(inp.v.shape)} dtype={dtype} "
+        f"C={C or inp.C} seed={inp.meta.get('seed')}")
+    O, S = run_gpu(inp, C)
+    Or, Sr = run_oracle(inp, heads)
+    if heads is not None:
+        O, S = O[:, :, heads], S[:, heads]
+    eo, es = rel(O, Or), rel(S, Sr)
+    say(f"      max rel err O {eo:.3e}  S_T {es:.3e}  (tol {TOL[dtype]:.0e})")
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+    return eo, es
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load_library()
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+def test_workload_deltanet_f32_t128_d16():
+    check(workload_inputs("deltanet_f32_b1_h1_t128_d16"), "f32", tag="workload 1")
+
+
+def test_workload_gdn_f32_b2_h4_t1024_d64():
+    check(workload_inputs("gdn_f32_b2_h4_t1024_d64"), "f32", tag="workload 2")
+
+
+def test_workload_gdn_bf16_b4_h16_t4096_d128():
+    check(workload_inputs("gdn_bf16_b4_h16_t4096_d128"), "bf16", tag="workload 3")
+
+
+def test_workload_gdn_bf16_long_t32768_sampled_heads():
+    check(workload_inputs("gdn_bf16_long_b1_h32_t32768_d128"), "bf16", heads=[0, 7, 18, 31],
+          tag="workload 4")
+
+
+def test_workload_gdn_bf16_varlen_dv256_sampled_heads():
+    inp = workload_inputs("gdn_bf16_varlen_65536_h16_dk128_dv256")
+    check(inp, "bf16", heads=[0, 5, 15], tag="workload 5")
+
+
+def test_second_seed_headline():
+    check(workload_inputs("gdn_bf16_b4_h16_t4096_d128", seed=103), "bf16", heads=[1, 14],
+          tag="workload 3 seed 103")
+
+
+# ---------------------------------------------------------------------------
+# shapes: several tiles, ragged tails, short and empty sequences
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,Dk,Dv,C", [("f32", 16, 16, 16), ("f32", 64, 64, 16),
+                                           ("f32", 64, 64, 64), ("f32", 128, 128, 64),
+                                           ("f32", 128, 256, 64), ("bf16", 128, 128, 64),
+                                           ("bf16", 128, 256, 64)])
+@pytest.mark.parametrize("T", [1, 5, 64, 300])
+def test_ragged(dtype, Dk, Dv, C, T):
+    inp = make_inputs(B=2, T=T, H=3, Dk=Dk, Dv=Dv, dtype=dtype, gated=True, s0=True,
+                      seed=1000 + T + Dv)
+    check(inp, dtype, C=C, tag="ragged")
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_deltanet_alpha_one_with_state(dtype, D):
+    inp = make_inputs(B=1, T=257, H=2, Dk=D, Dv=D, dtype=dtype, gated=False, s0=True, seed=5)
+    check(inp, dtype, C=64, tag="alpha=1")
+
+
+def test_zero_length_sequence_returns_initial_state():
+    inp = make_inputs(B=2, T=0, H=2, Dk=64, Dv=64, dtype="f32", gated=True, s0=True, seed=3)
+    O, S = run_gpu(inp, 64)
+    assert O.shape == (2, 0, 2, 64)
+    assert np.array_equal(S, inp.S0.double().numpy())
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [("f32", 64, 64), ("bf16", 128, 256), ("bf16", 128, 128)])
+def test_varlen_packed(dtype, Dk, Dv):
+    lengths = [0, 1, 63, 64, 65, 200, 0, 7, 130]
+    inp = make_inputs(B=1, T=sum(lengths), H=2, Dk=Dk, Dv=Dv, dtype=dtype, gated=True, s0=True,
+                      seed=77, lengths=lengths)
+    check(inp, dtype, C=64, tag=f"varlen {lengths}")
+
+
+def test_varlen_equals_separate_calls():
+    lengths = [100, 37, 256]
+    inp = make_inputs(B=1, T=sum(lengths), H=4, Dk=128, Dv=128, dtype="bf16", gated=True,
+                      s0=True, seed=78, lengths=lengths)
+    O, S = run_gpu(inp)
+    off = 0
+    for i, n in enumerate(lengths):
+        sub = make_inputs(B=1, T=n, H=4, Dk=128, Dv=128, dtype="bf16", seed=0)
+        sub.q, sub.k, sub.v = (t[:, off:off + n].contiguous() for t in (inp.q, inp.k, inp.v))
+        sub.beta = inp.beta[:, off:off + n].contiguous()
+        sub.log_alpha = inp.log_alpha[:, off:off + n].contiguous()
+        sub.S0 = inp.S0[i:i + 1].contiguous()
+        Oi, Si = run_gpu(sub)
+        assert np.array_equal(Oi[0], O[0, off:off + n]), f"sequence {i} O"
+        assert np.array_equal(Si[0], S[i]), f"sequence {i} S_T"
+        off += n
+
+
+# ---------------------------------------------------------------------------
+# invariants: determinism, chunk-size invariance, resume, in-place state
+# ---------------------------------------------------------------------------
+def test_bitwise_deterministic():
+    inp = workload_inputs("gdn_bf16_b4_h16_t4096_d128")
+    O1, S1 = run_gpu(inp)
+    O2, S2 = run_gpu(inp)
+    assert np.array_equal(O1, O2) and np.array_equal(S1, S2)
+
+
+def test_chunk_size_invariance_f32():
+    inp = make_inputs(B=2, T=333, H=2, Dk=64, Dv=64, dtype="f32", gated=True, s0=True, seed=9)
+    O16, S16 = run_gpu(inp, 16)
+    O64, S64 = run_gpu(inp, 64)
+    assert rel(O16, O64) <= 1e-5 and rel(S16, S64) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_resume_from_state(dtype, D):
+    inp = make_inputs(B=2, T=500, H=2, Dk=D, Dv=D, dtype=dtype, gated=True, s0=True, seed=21)
+    Or, Sr = run_oracle(inp)
+    T1 = 211
+    a = make_inputs(B=2, T=T1, H=2, Dk=D, Dv=D, dtype=dtype, seed=0)
+    b = make_inputs(B=2, T=500 - T1, H=2, Dk=D, Dv=D, dtype=dtype, seed=0)
+    for part, sl in ((a, slice(0, T1)), (b, slice(T1, 500))):
+        part.q, part.k, part.v = (t[:, sl].contiguous() for t in (inp.q, inp.k, inp.v))
+        part.beta, part.log_alpha = (t[:, sl].contiguous() for t in (inp.beta, inp.log_alpha))
+    a.S0 = inp.S0
+    Oa, Sa = run_gpu(a, 64)
+    b.S0 = torch.from_numpy(Sa).float()
+    Ob, Sb = run_gpu(b, 64)
+    assert rel(np.concatenate([Oa, Ob], 1), Or) <= TOL[dtype]
+    assert rel(Sb, Sr) <= TOL[dtype]
+
+
+def test_state_in_place_and_optional_final_state():
+    inp = make_inputs(B=2, T=190, H=2, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True, seed=31)
+    d = inp.to(DEV)
+    O_ref, S_ref = gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0)
+    S = d.S0.clone()
+    O_ip, _ = gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, S, S_T=S)
+    O_no, S_no = gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0,
+                                   output_final_state=False)
+    torch.cuda.synchronize()
+    assert S_no is None
+    assert torch.equal(O_ip, O_ref) and torch.equal(S, S_ref) and torch.equal(O_no, O_ref)
+
+
+def test_side_stream():
+    inp = make_inputs(B=1, T=130, H=2, Dk=64, Dv=64, dtype="f32", gated=True, s0=True, seed=41)
+    d = inp.to(DEV)
+    ref = gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], ref[0]) and torch.equal(out[1], ref[1])
+
+
+# ---------------------------------------------------------------------------
+# single-token step and prefill -> decode
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,Dk,Dv", [("f32", 16, 16), ("f32", 64, 64), ("bf16", 128, 128),
+                                         ("bf16", 128, 256), ("f32", 128, 256)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_recurrent_step(dtype, Dk, Dv, gated):
+    inp = make_inputs(B=3, T=1, H=4, Dk=Dk, Dv=Dv, dtype=dtype, gated=gated, s0=True, seed=51)
+    Or, Sr = run_oracle(inp)
+    d = inp.to(DEV)
+    S = d.S0.clone()
+    o = gdn.gdn_recurrent_step(d.q[:, 0].contiguous(), d.k[:, 0].contiguous(), d.v[:, 0].contiguous(),
+                               None if d.log_alpha is None else d.log_alpha[:, 0].contiguous(),
+                               d.beta[:, 0].contiguous(), S)
+    torch.cuda.synchronize()
+    assert rel(o.double().cpu().numpy(), Or[:, 0]) <= TOL[dtype]
+    assert rel(S.double().cpu().numpy(), Sr) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_prefill_then_decode(dtype, D):
+    T = 150
+    inp = make_inputs(B=2, T=T + 3, H=2, Dk=D, Dv=D, dtype=dtype, gated=True, s0=True, seed=61)
+    Or, Sr = run_oracle(inp)
+    d = inp.to(DEV)
+    O, S = gdn.gdn_chunk_fwd(d.q[:, :T].contiguous(), d.k[:, :T].contiguous(),
+                             d.v[:, :T].contiguous(), d.log_alpha[:, :T].contiguous(),
+                             d.beta[:, :T].contiguous(), d.S0)
+    outs = [O.double().cpu().numpy()]
+    for t in range(T, T + 3):
+        o = gdn.gdn_recurrent_step(d.q[:, t].contiguous(), d.k[:, t].contiguous(),
+                                   d.v[:, t].contiguous(), d.log_alpha[:, t].contiguous(),
+                                   d.beta[:, t].contiguous(), S)
+        outs.append(o.double().cpu().numpy()[:, None])
+    torch.cuda.synchronize()
+    assert rel(np.concatenate(outs, 1), Or) <= TOL[dtype]
+    assert rel(S.double().cpu().numpy(), Sr) <= TOL[dtype]
