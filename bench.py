@@ -1,0 +1,206 @@
+"""Throughput of the chunkwise gated delta rule forward on one MI355X.
+
+One step = one gdn_chunk_fwd call (prep and scan kernels) over the
+whole batch of the headline workload: B=4, H=16, T=4096, Dk=Dv=128, chunk 64,
+bf16 q/k/v/O, fp32 gates and state, S0 = 0, seeded synthetic inputs already
+resident in HBM.  Prints ONE JSON line.
+
+  value         tokens/s = B*T / (mean device time of one step)
+  roofline      dominant kernel: its algorithmic bytes (or flops) per launch over
+                its mean HIP-event duration, against MI355X's published peak
+  roofline_path the same for the whole call (all kernels)
+  cpu_baseline  the fp64 oracle on the host cores over the same inputs
+
+Options: --gpus (only 1), --steps, --warmup, --workload, --no-flush,
+--profile-steps, --cpu-sample (heads per batch row the oracle runs on, 0 = skip).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}   # dense flop/s
+METRIC = "tokens/sec gated-DeltaNet chunk fwd (H=16,T=4096,D=128,bf16); % roofline"
+
+
+def per_kernel_work(B, T, H, Dk, Dv, C, s_in, n_seqs, has_s0, gated):
+    """Algorithmic bytes and flops of each kernel and of the whole call.
+
+    Bytes count only the operation's own inputs and outputs that a kernel
+    touches (q, k, v, gates, O, S0, S_T); per-chunk intermediates (g and
+    T diag(beta), written by prep and read by scan) are implementation traffic
+    and are not counted.  Flops count dense 16x16 tiles of every product.
+    The path's flops are the method's count per token-head,
+    6 Dk Dv + 2C (3 Dk + 2 Dv) + C^2 / 3 (K K^T, W, Q K^T; U, P V'; inverse)."""
+    th = B * T * H                      # token-heads
+    gate_b = 4 + (4 if gated else 0)    # beta (+ log alpha), fp32
+    state_b = n_seqs * H * Dv * Dk * 4 * (2 if has_s0 else 1)
+    prep_b = th * (Dk * s_in + gate_b)
+    scan_b = th * (2 * Dk + 2 * Dv) * s_in + state_b
+    path_b = th * ((2 * Dk + 2 * Dv) * s_in + gate_b) + state_b
+    prep_f = th * (2 * C * Dk + C * C / 3)
+    scan_f = th * (6 * Dk * Dv + 2 * C * (Dk + 2 * Dv))
+    path_f = th * (6 * Dk * Dv + 2 * C * (3 * Dk + 2 * Dv) + C * C / 3)
+    return {"prep": (prep_b, prep_f), "scan": (scan_b, scan_f), "path": (path_b, path_f)}
+
+
+def roofline(name, bytes_, flops, seconds, dtype):
+    t_hbm, t_mma = bytes_ / HBM_PEAK, flops / MFMA_PEAK[dtype]
+    if t_hbm >= t_mma:
+        ach = bytes_ / seconds / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": round(ach / (HBM_PEAK / 1e9), 4), "traffic": None,
+                "alg_bytes": int(bytes_), "alg_flops": int(flops), "ms": round(seconds * 1e3, 4)}
+    ach = flops / seconds / 1e12
+    return {"kernel": name, "bound": "mfma", "achieved": round(ach, 2),
+            "peak": MFMA_PEAK[dtype] / 1e12, "unit": "TFLOP/s",
+            "frac": round(ach / (MFMA_PEAK[dtype] / 1e12), 4), "traffic": None,
+            "alg_bytes": int(bytes_), "alg_flops": int(flops), "ms": round(seconds * 1e3, 4)}
+
+
+def cpu_baseline(inp, heads_per_row: int):
+    """The fp64 oracle timed on the host cores over a bounded sample: every
+    batch row, the first ``heads_per_row`` heads, all tokens."""
+    import oracle
+    hs = list(range(min(heads_per_row, inp.q.shape[2])))
+    sl = lambda t: None if t is None else t[:, :, hs].contiguous()
+    q, k, v, la, be = (sl(t) for t in (inp.q, inp.k, inp.v, inp.log_alpha, inp.beta))
+    s0 = None if inp.S0 is None else inp.S0[:, hs].contiguous()
+    import numpy as np
+    q, k, v = (np.ascontiguousarray(t.double().numpy()) for t in (q, k, v))
+    la = None if la is None else np.ascontiguousarray(la.double().numpy())
+    be = np.ascontiguousarray(be.double().numpy())
+    t0 = time.perf_counter()
+    _, _, nt = oracle.forward(q, k, v, la, be, s0, inp.cu_seqlens, return_threads=True)
+    dt = time.perf_counter() - t0
+    tokens = inp.q.shape[0] * inp.q.shape[1]
+    # scale to the full workload's tokens/s: the sample holds len(hs) of H heads
+    H = inp.q.shape[2]
+    return {"value": round(tokens * len(hs) / H / dt, 1), "unit": "tokens/s", "cores": nt,
+            "kind": "oracle",
+            "sample": f"fp64 token recurrence over all {inp.q.shape[0]}x{inp.q.shape[1]} tokens "
+                      f"of heads 0..{len(hs) - 1} of {H} ({tokens * len(hs)} token-heads, "
+                      f"{dt:.2f} s wall on {nt} threads); tokens/s scaled by {len(hs)}/{H}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gdn_bf16_b4_h16_t4096_d128")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not overwrite a 512 MB buffer (L2 + MALL) before each step")
+    ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--cpu-sample", type=int, default=16,
+                    help="heads per batch row for the oracle baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the (sequence, head) units shard across GPUs with no communication, see the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_16_amd as gdn
+    from gated_delta_rule_16_amd.inputs import WORKLOADS, workload_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    w = WORKLOADS[args.workload]
+    inp = workload_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    d = inp.to(dev)
+    B, T, H = inp.q.shape[:3]
+    N = inp.n_seqs
+    tdt = inp.q.dtype
+    O = torch.empty(B, T, H, w.Dv, device=dev, dtype=tdt)
+    S_T = torch.empty(N, H, w.Dv, w.Dk, device=dev, dtype=torch.float32)
+    n_ws = gdn.gdn_chunk_fwd_workspace_bytes(B, T, H, w.Dk, w.Dv, w.C,
+                                             0 if inp.cu_seqlens is None else N, tdt)
+    ws = torch.empty(n_ws, device=dev, dtype=torch.uint8)
+    flush = None if args.no_flush else torch.empty(512 << 20, device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, d.cu_seqlens, chunk_size=w.C,
+                          O=O, S_T=S_T, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.zero_()
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.zero_()       # evict L2 and MALL: every step reads its inputs from HBM
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms = statistics.mean(step_ms)
+    tokens = B * T
+    value = tokens / (ms / 1e3)
+
+    # per-kernel device time (HIP events on the launch stream, inside the library)
+    kms = {"table": [], "prep": [], "scan": [], "unused": []}
+    for _ in range(args.profile_steps):
+        if flush is not None:
+            flush.zero_()
+        _, _, t = gdn.gdn_chunk_fwd_profiled(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0,
+                                             d.cu_seqlens, chunk_size=w.C, O=O, S_T=S_T,
+                                             workspace=ws, stream=stream)
+        for key, x in zip(kms, t):
+            kms[key].append(x)
+    kms.pop("unused")
+    kmean = {k_: (statistics.mean(v_) if v_ else 0.0) for k_, v_ in kms.items()}
+
+    s_in = 2 if w.dtype == "bf16" else 4
+    work = per_kernel_work(B, T, H, w.Dk, w.Dv, w.C, s_in, N, inp.S0 is not None,
+                           inp.log_alpha is not None)
+    dom = max(("prep", "scan"), key=lambda k_: kmean[k_])
+    rl = roofline(dom, *work[dom], kmean[dom] / 1e3, w.dtype)
+    rl_path = roofline("path", *work["path"], ms / 1e3, w.dtype)
+    kernels = {k_: {"ms": round(kmean[k_], 4),
+                    **({"frac": roofline(k_, *work[k_], kmean[k_] / 1e3, w.dtype)["frac"]}
+                       if k_ in work and kmean[k_] > 0 else {})}
+               for k_ in kms}
+
+    cpu = None
+    if args.cpu_sample > 0:
+        cpu = cpu_baseline(inp, args.cpu_sample)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "Dk": w.Dk, "Dv": w.Dv,
+                   "chunk": w.C, "state": "fp32", "S0": inp.S0 is not None,
+                   "flush_l2_mall": flush is not None},
+        "roofline": rl, "roofline_path": rl_path, "kernels": kernels,
+        "step_ms": {"median": round(statistics.median(step_ms), 4), "min": round(min(step_ms), 4),
+                    "max": round(max(step_ms), 4)},
+        "wall_s_timed_loop": round(wall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

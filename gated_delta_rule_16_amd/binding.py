@@ -6,8 +6,8 @@ workspace) and the stream.  There is no fallback: if the library is not built,
 or a tensor is not on a ROCm device, the call raises.
 
 The Python functions carry the C names:
-  gdn_chunk_fwd, gdn_recurrent_step, gdn_chunk_fwd_workspace_bytes,
-  gdn_chunk_fwd_supported, gdn_status_string.
+  gdn_chunk_fwd, gdn_chunk_fwd_profiled, gdn_recurrent_step,
+  gdn_chunk_fwd_workspace_bytes, gdn_chunk_fwd_supported, gdn_status_string.
 """
 from __future__ import annotations
 
@@ -51,6 +51,8 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_chunk_fwd_workspace_bytes.restype = SZ
     lib.gdn_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P, SZ, P]
     lib.gdn_chunk_fwd.restype = I
+    lib.gdn_chunk_fwd_profiled.argtypes = lib.gdn_chunk_fwd.argtypes + [P]
+    lib.gdn_chunk_fwd_profiled.restype = I
     lib.gdn_recurrent_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.gdn_recurrent_step.restype = I
     lib.gdn_status_string.argtypes = [I]
@@ -92,21 +94,8 @@ def _stream(device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                  log_alpha: Optional[torch.Tensor], beta: torch.Tensor,
-                  S0: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
-                  *, chunk_size: int = 64, O: Optional[torch.Tensor] = None,
-                  S_T: Optional[torch.Tensor] = None, output_final_state: bool = True,
-                  workspace: Optional[torch.Tensor] = None,
-                  stream: Optional[torch.cuda.Stream] = None
-                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunkwise gated delta rule forward (see include/gdn.h, gdn_chunk_fwd).
-
-    q, k [B,T,H,Dk]; v [B,T,H,Dv] (fp32 or bf16, same dtype); log_alpha (or
-    None: alpha = 1) and beta [B,T,H] fp32; S0 [N,H,Dv,Dk] fp32 or None;
-    cu_seqlens int32 [N+1] on the device for a packed batch (B = 1).
-    Returns (O [B,T,H,Dv], S_T [N,H,Dv,Dk] or None).  Outputs and the
-    workspace are allocated here unless passed in."""
+def _chunk_fwd(profiled: bool, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
+               output_final_state, workspace, stream):
     lib = load_library()
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,T,H,Dk] and v [B,T,H,Dv]")
@@ -129,17 +118,52 @@ def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     need = lib.gdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk_size, n_seqs, _DT[dt])
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), device=dev, dtype=torch.uint8)
-    rc = lib.gdn_chunk_fwd(
+    args = [
         _ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt),
         _ptr(log_alpha, "log_alpha", dev, torch.float32), _ptr(beta, "beta", dev, torch.float32),
         _ptr(S0, "S0", dev, torch.float32), _ptr(cu_seqlens, "cu_seqlens", dev, torch.int32),
         n_seqs, _ptr(O, "O", dev, dt), _ptr(S_T, "S_T", dev, torch.float32),
         B, T, H, Dk, Dv, chunk_size, _DT[dt],
         _ptr(workspace, "workspace", dev), workspace.numel() * workspace.element_size(),
-        _stream(dev, stream))
+        _stream(dev, stream)]
+    if profiled:
+        ms = (ctypes.c_float * 4)()
+        rc = lib.gdn_chunk_fwd_profiled(*args, ms)
+        if rc != 0:
+            raise GdnError(rc, "gdn_chunk_fwd_profiled")
+        return O, S_T, [float(x) for x in ms]
+    rc = lib.gdn_chunk_fwd(*args)
     if rc != 0:
         raise GdnError(rc, "gdn_chunk_fwd")
     return O, S_T
+
+
+def gdn_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  log_alpha: Optional[torch.Tensor], beta: torch.Tensor,
+                  S0: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                  *, chunk_size: int = 64, O: Optional[torch.Tensor] = None,
+                  S_T: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  workspace: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise gated delta rule forward (see include/gdn.h, gdn_chunk_fwd).
+
+    q, k [B,T,H,Dk]; v [B,T,H,Dv] (fp32 or bf16, same dtype); log_alpha (or
+    None: alpha = 1) and beta [B,T,H] fp32; S0 [N,H,Dv,Dk] fp32 or None;
+    cu_seqlens int32 [N+1] on the device for a packed batch (B = 1).
+    Returns (O [B,T,H,Dv], S_T [N,H,Dv,Dk] or None).  Outputs and the
+    workspace are allocated here unless passed in."""
+    return _chunk_fwd(False, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
+                      output_final_state, workspace, stream)
+
+
+def gdn_chunk_fwd_profiled(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
+                           chunk_size: int = 64, O=None, S_T=None, output_final_state=True,
+                           workspace=None, stream=None):
+    """As gdn_chunk_fwd, and also returns the device milliseconds of each
+    kernel [table, prep, scan, output]; blocks until the call has finished."""
+    return _chunk_fwd(True, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
+                      output_final_state, workspace, stream)
 
 
 def gdn_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

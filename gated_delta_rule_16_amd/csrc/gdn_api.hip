@@ -3,9 +3,8 @@
 //
 // Data flow of gdn_chunk_fwd (all on the caller's stream):
 //   [packed batches only] chunk table  <- cu_seqlens
-//   prep   (chunk slot, head)            g, W, U          (independent chunks)
-//   scan   (Dv slice, head, sequence)    V', h, S_T       (serial over chunks)
-//   output (chunk slot, head, Dv slice)  O                (independent chunks)
+//   prep  (chunk slot, head)            g, Tb = T diag(beta)   (independent chunks)
+//   scan  (Dv slice, head, sequence)    O, S_T                 (serial over chunks)
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
@@ -13,7 +12,6 @@
 
 #include "../../include/gdn.h"
 #include "gdn_device.h"
-#include "gdn_output.h"
 #include "gdn_prep.h"
 #include "gdn_scan.h"
 #include "gdn_step.h"
@@ -57,7 +55,7 @@ struct FwdArgs {
 // Workspace regions, in order; every region starts on a 256-byte boundary.
 struct Layout {
     int64_t slots, N;
-    size_t g, W, U, Vp, hs, bounds, seq_slot, table, total;
+    size_t g, Tb, bounds, seq_slot, table, total;
 };
 
 Layout make_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C,
@@ -70,10 +68,7 @@ Layout make_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int6
     auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
     const size_t u = (size_t)(L.slots * H);
     L.g = take(u * C * sizeof(float));
-    L.W = take(u * C * Dk * es);
-    L.U = take(u * C * Dv * es);
-    L.Vp = take(u * Dv * C * es);
-    L.hs = take(u * Dv * Dk * es);
+    L.Tb = take(u * C * C * es);
     if (varlen) {
         L.bounds = take((size_t)(n_seqs + 1) * sizeof(int));
         L.seq_slot = take((size_t)(n_seqs + 1) * sizeof(int));
@@ -96,7 +91,7 @@ void allow_smem(size_t bytes) {
 }
 
 // Optional per-kernel timing: events recorded on the launch stream around each
-// kernel (table, prep, scan, output).
+// kernel (table, prep, scan).
 struct KernelTimer {
     hipEvent_t ev[8];
     int n = 0;
@@ -111,10 +106,7 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     const bool varlen = a.cu != nullptr;
     const Layout L = make_layout(a.B, a.T, a.H, DK, DV, C, varlen, a.n_seqs, sizeof(T));
     float* g_ws = reinterpret_cast<float*>(a.ws + L.g);
-    T* W_ws = reinterpret_cast<T*>(a.ws + L.W);
-    T* U_ws = reinterpret_cast<T*>(a.ws + L.U);
-    T* Vp_ws = reinterpret_cast<T*>(a.ws + L.Vp);
-    T* h_ws = reinterpret_cast<T*>(a.ws + L.hs);
+    T* Tb_ws = reinterpret_cast<T*>(a.ws + L.Tb);
 
     SeqGeom geom{};
     geom.C = C;
@@ -137,12 +129,12 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     const T* v = static_cast<const T*>(a.v);
 
     if (L.slots > 0) {
-        using P = PrepCfg<T, DK, DV, C>;
-        constexpr auto kp = gdn_prep_kernel<T, DK, DV, C>;
+        using P = PrepCfg<T, DK, C>;
+        constexpr auto kp = gdn_prep_kernel<T, DK, C>;
         allow_smem<kp>(P::SMEM);
         tm->mark(a.stream);
         hipLaunchKernelGGL(kp, dim3((unsigned)L.slots, a.H), dim3(kThreads), P::SMEM, a.stream,
-                           k, v, a.log_alpha, a.beta, geom, a.H, g_ws, W_ws, U_ws);
+                           k, a.log_alpha, a.beta, geom, a.H, g_ws, Tb_ws);
         if (gdn_status s = check_launch(a.stream)) return s;
         tm->mark(a.stream);
     }
@@ -152,19 +144,9 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         constexpr auto ks = gdn_scan_kernel<T, DK, DV, C, DVT>;
         allow_smem<ks>(S::SMEM);
         tm->mark(a.stream);
-        hipLaunchKernelGGL(ks, dim3(DV / DVT, a.H, (unsigned)L.N), dim3(kThreads), S::SMEM, a.stream,
-                           k, a.S0, geom, a.H, g_ws, W_ws, U_ws, Vp_ws, h_ws, a.S_T);
-        if (gdn_status s = check_launch(a.stream)) return s;
-        tm->mark(a.stream);
-    }
-    if (L.slots > 0) {
-        constexpr int DVO = DV >= 64 ? 64 : DV;
-        using O = OutCfg<T, DK, DV, C, DVO>;
-        constexpr auto ko = gdn_output_kernel<T, DK, DV, C, DVO>;
-        allow_smem<ko>(O::SMEM);
-        tm->mark(a.stream);
-        hipLaunchKernelGGL(ko, dim3((unsigned)L.slots, a.H, DV / DVO), dim3(kThreads), O::SMEM,
-                           a.stream, q, k, geom, a.H, g_ws, Vp_ws, h_ws, static_cast<T*>(a.O));
+        hipLaunchKernelGGL(ks, dim3(DV / DVT, a.H, (unsigned)L.N), dim3(S::NTHR), S::SMEM,
+                           a.stream, q, k, v, a.S0, geom, a.H, g_ws, Tb_ws,
+                           static_cast<T*>(a.O), a.S_T);
         if (gdn_status s = check_launch(a.stream)) return s;
         tm->mark(a.stream);
     }
@@ -293,15 +275,14 @@ extern "C" gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const
                                       &tm);
         if (s == GDN_OK && hipEventSynchronize(tm.ev[tm.n - 1]) != hipSuccess) s = GDN_ERR_HIP;
         if (s == GDN_OK) {
-            // pairs of marks: [table], prep, scan, output (prep/output absent when T = 0)
+            // pairs of marks: [table], [prep], scan (prep absent when there are no chunks)
             const bool varlen = cu_seqlens != nullptr;
-            const bool has_chunks = tm.n >= (varlen ? 8 : 6);
+            const bool has_chunks = tm.n >= (varlen ? 6 : 4);
             int slot[4] = {-1, -1, -1, -1};
             int m = 0;
             if (varlen) slot[0] = m++;
             if (has_chunks) slot[1] = m++;
             slot[2] = m++;
-            if (has_chunks) slot[3] = m++;
             for (int i = 0; i < 4; ++i) {
                 if (slot[i] < 0) continue;
                 float ms = 0.f;

@@ -21,7 +21,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;   // 4 waves per workgroup in every kernel
+constexpr int kThreads = 256;   // 4 waves per workgroup (prep, step)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
@@ -131,13 +131,13 @@ __device__ __forceinline__ void seq_slots(const SeqGeom& g, int seq, int& first,
 // Copies a [rows x D] tile of token-major input (row r = token t0 + r of head h)
 // into LDS with leading dimension ldl, zero-filling rows >= len.
 // src points at element (token 0, head 0, 0) and the token stride is H * D.
-template <typename T, int D>
+template <typename T, int D, int NTHR>
 __device__ __forceinline__ void stage_tokens(T* dst, int ldl, const T* src, int t0, int len,
                                              int rows, int H, int h) {
     constexpr int V = 16 / sizeof(T);           // elements per 16-byte vector
     constexpr int VPR = D / V;                  // vectors per row
     static_assert(D % V == 0, "row must be a whole number of 16-byte vectors");
-    for (int i = threadIdx.x; i < rows * VPR; i += kThreads) {
+    for (int i = threadIdx.x; i < rows * VPR; i += NTHR) {
         const int r = i / VPR, c = (i - r * VPR) * V;
         uint4 val = make_uint4(0u, 0u, 0u, 0u);
         if (r < len) {
@@ -149,12 +149,12 @@ __device__ __forceinline__ void stage_tokens(T* dst, int ldl, const T* src, int 
 }
 
 // Copies a dense [rows x D] tile (row stride ld_src elements) into LDS.
-template <typename T, int D>
+template <typename T, int D, int NTHR>
 __device__ __forceinline__ void stage_dense(T* dst, int ldl, const T* src, int64_t ld_src, int rows) {
     constexpr int V = 16 / sizeof(T);
     constexpr int VPR = D / V;
     static_assert(D % V == 0, "row must be a whole number of 16-byte vectors");
-    for (int i = threadIdx.x; i < rows * VPR; i += kThreads) {
+    for (int i = threadIdx.x; i < rows * VPR; i += NTHR) {
         const int r = i / VPR, c = (i - r * VPR) * V;
         *reinterpret_cast<uint4*>(dst + r * ldl + c) =
             *reinterpret_cast<const uint4*>(src + (int64_t)r * ld_src + c);

@@ -1,61 +1,54 @@
 // gdn_prep.h -- per-chunk preparation kernel (independent across chunks).
 //
-// For one chunk of n <= C tokens of one head (row form: K is n x Dk, V is n x Dv,
-// token i is row i):
-//   g_i   = sum_{t<=i} log alpha_t           in-chunk inclusive cumulative log-gate
-//   A     = strict_lower( diag(beta) (K K^T o Gamma) ),  Gamma_ij = exp(g_i - g_j)
-//   T     = (I + A)^-1                        unit lower triangular
-//   W     = T diag(beta o gamma) K,   U = T diag(beta) V,    gamma_i = exp(g_i)
+// For one chunk of n <= C tokens of one head (row form: K is n x Dk, token i is
+// row i):
+//   g_i  = sum_{t<=i} log alpha_t              in-chunk inclusive cumulative log-gate
+//   A    = strict_lower( diag(beta) (K K^T o Gamma) ),   Gamma_ij = exp(g_i - g_j)
+//   T    = (I + A)^-1                           unit lower triangular
+//   Tb   = T diag(beta)                         stored (input dtype), with g (fp32)
+// The scan kernel applies Tb to the chunk's prediction errors:
+//   V' = Tb (V - diag(gamma) K S^T) = U - W S^T,  U = T diag(beta) V,
+//   W = T diag(beta o gamma) K,  gamma_i = exp(g_i).
 // Sources: Qiita article on the Linear Attention lineage, section
 // "Gated-DeltaNet": the w and u recursions and their triangular systems
-// (I + (strictly triangular K^T K part) D_beta)^-1; the gate enters W only
-// through D_gamma in the S0 term of that section's parallel form, and the
-// decay ratios gamma_i / gamma_s enter U.  LinearAttention系列解读(六), sections
-// 4.2 and 4.5: the unit-lower-triangular inverse is cheap at chunk size, and
-// W, U, T do not depend on the state, so every chunk is prepared in parallel.
-// Here T diag(beta o gamma) K equals diag(gamma) times the ungated solve for W
-// (I + A = D_gamma (I + A_0) D_gamma^-1), which is the form the scan needs.
+// (I + (strictly triangular part of K^T K, gated by gamma_i/gamma_s) D_beta)^-1;
+// LinearAttention系列解读(六)：DeltaNet的Chunkwise Form推导, sections 4.2 and 4.5:
+// the inverse is a small unit-lower-triangular one, and T depends on the chunk's
+// keys and gates only, never on the state, so every chunk is prepared in parallel.
+// Gating: I + A = D_gamma (I + A_0) D_gamma^-1 with A_0 the ungated matrix, so
+// T diag(beta o gamma) K is diag(gamma) times the ungated W of that section.
 //
-// Padding: rows i >= n act as tokens with k = v = 0, beta = 0, log alpha = 0;
-// they leave every valid row unchanged and give W = U = 0 rows.
+// Padding: rows i >= n act as tokens with k = 0, beta = 0, log alpha = 0, which
+// makes their rows and columns of Tb zero.
 #pragma once
 
 #include "gdn_device.h"
 
 namespace gdn {
 
-template <typename T, int DK, int DV, int C>
+template <typename T, int DK, int C>
 struct PrepCfg {
     static constexpr int PAD = 16 / sizeof(T);           // keeps 16-byte row alignment
     static constexpr int LDK = DK + PAD;
-    static constexpr int LDV = DV + PAD;
     static constexpr int LDA = C + 4;                     // fp32 A
-    static constexpr int LDC = C + PAD;                   // T-typed C x C operands
     static constexpr size_t OFF_K = 0;
-    static constexpr size_t OFF_V = OFF_K + sizeof(T) * C * LDK;
-    static constexpr size_t OFF_A = OFF_V + sizeof(T) * C * LDV;
-    static constexpr size_t SZ_A = sizeof(float) * C * LDA;
-    static constexpr size_t SZ_TT = 2 * sizeof(T) * C * LDC;
-    static constexpr size_t OFF_G = OFF_A + (SZ_A > SZ_TT ? SZ_A : SZ_TT);
+    static constexpr size_t OFF_A = OFF_K + sizeof(T) * C * LDK;
+    static constexpr size_t OFF_G = OFF_A + sizeof(float) * C * LDA;
     static constexpr size_t OFF_B = OFF_G + sizeof(float) * C;
     static constexpr size_t SMEM = OFF_B + sizeof(float) * C;
-    static_assert(C <= 64, "one wave solves the chunk's triangular system");
-    static_assert(C % Mfma<T>::KS == 0 || Mfma<T>::KS <= 16, "chunk must cover whole MFMA steps");
+    static_assert(C <= 64 && C % 16 == 0, "one wave solves the chunk's triangular system");
 };
 
-template <typename T, int DK, int DV, int C>
+template <typename T, int DK, int C>
 __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
-    const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ log_alpha,
+    const T* __restrict__ k, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, SeqGeom geom, int H,
-    float* __restrict__ g_ws, T* __restrict__ W_ws, T* __restrict__ U_ws) {
-    using Cfg = PrepCfg<T, DK, DV, C>;
+    float* __restrict__ g_ws, T* __restrict__ Tb_ws) {
+    using Cfg = PrepCfg<T, DK, C>;
     using M = Mfma<T>;
     extern __shared__ __align__(16) unsigned char smem[];
     T* sK = reinterpret_cast<T*>(smem + Cfg::OFF_K);
-    T* sV = reinterpret_cast<T*>(smem + Cfg::OFF_V);
     float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
-    T* sTw = reinterpret_cast<T*>(smem + Cfg::OFF_A);            // aliases A after the solve
-    T* sTu = sTw + C * Cfg::LDC;
     float* sg = reinterpret_cast<float*>(smem + Cfg::OFF_G);
     float* sb = reinterpret_cast<float*>(smem + Cfg::OFF_B);
 
@@ -84,13 +77,12 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
             g_ws[unit * C + l] = la;
         }
     }
-    stage_tokens<T, DK>(sK, Cfg::LDK, k, ci.t0, ci.len, C, H, h);
-    stage_tokens<T, DV>(sV, Cfg::LDV, v, ci.t0, ci.len, C, H, h);
+    stage_tokens<T, DK, kThreads>(sK, Cfg::LDK, k, ci.t0, ci.len, C, H, h);
     __syncthreads();
 
     // A = strict_lower(diag(beta) (K K^T o Gamma)) on MFMA, lower tiles only
     constexpr int NT = C / 16;
-    for (int t = w; t < NT * NT; t += 4) {
+    for (int t = w; t < NT * NT; t += kThreads / 64) {
         const int ti = t / NT, tj = t - ti * NT;
         if (tj > ti) continue;
         f32x4 acc = zero4();
@@ -106,7 +98,8 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
     }
     __syncthreads();
 
-    // T = (I + A)^-1 by forward substitution; lane c owns column c of T.
+    // T = (I + A)^-1 by forward substitution; lane c owns column c of T and
+    // writes column c of Tb = T diag(beta) (each row store is contiguous).
     if (w == 0) {
         const int c = l;
         float x[C];
@@ -125,38 +118,10 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
         }
         if (c < C) {
             const float bc = sb[c];
-            const float wc = bc * __expf(sg[c]);
+            T* out = Tb_ws + unit * C * C + c;
 #pragma unroll
-            for (int i = 0; i < C; ++i) {
-                sTw[i * Cfg::LDC + c] = from_f32<T>(x[i] * wc);
-                sTu[i * Cfg::LDC + c] = from_f32<T>(x[i] * bc);
-            }
+            for (int i = 0; i < C; ++i) out[i * C] = from_f32<T>(x[i] * bc);
         }
-    }
-    __syncthreads();
-
-    // W = (T diag(beta gamma)) K and U = (T diag(beta)) V; T is lower triangular,
-    // so row tile ti only needs the first (ti + 1) * 16 contraction columns.
-    constexpr int NW = NT * (DK / 16), NU = NT * (DV / 16);
-    T* Wout = W_ws + unit * C * DK;
-    T* Uout = U_ws + unit * C * DV;
-    for (int t = w; t < NW + NU; t += 4) {
-        const bool isw = t < NW;
-        const int tt = isw ? t : t - NW;
-        const int ncol = isw ? DK / 16 : DV / 16;
-        const int ti = tt / ncol, tn = tt - ti * ncol;
-        const T* sTm = isw ? sTw : sTu;
-        const T* sX = isw ? sK : sV;
-        const int ldx = isw ? Cfg::LDK : Cfg::LDV;
-        const int kend = ((ti + 1) * 16 + M::KS - 1) / M::KS * M::KS;
-        f32x4 acc = zero4();
-        for (int kk = 0; kk < kend; kk += M::KS)
-            acc = M::mma(frag_kc(sTm, Cfg::LDC, ti * 16, kk), frag_ks(sX, ldx, kk, tn * 16), acc);
-        T* out = isw ? Wout : Uout;
-        const int ld = isw ? DK : DV;
-        const int col = tn * 16 + (l & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) out[(ti * 16 + 4 * (l >> 4) + r) * ld + col] = from_f32<T>(acc[r]);
     }
 }
 

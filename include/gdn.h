@@ -9,8 +9,10 @@
  * (gate, predict, delta, write, read) is spelled out in the kkkzoz blog post
  * "linear-attention", sections "Gated DeltaNet" and "Workflow".
  *
- * gdn_chunk_fwd evaluates it chunk by chunk in the WY form: inside a chunk of C
- * tokens the coupled writes are resolved by one unit-lower-triangular solve
+ * gdn_chunk_fwd evaluates it chunk by chunk in the WY form with two kernels, a
+ * parallel per-chunk prep and a serial per-sequence scan that also writes the
+ * outputs: inside a chunk of C tokens the coupled writes are resolved by one
+ * unit-lower-triangular solve
  * (LinearAttention系列解读(六)：DeltaNet的Chunkwise Form推导, sections 4.2-4.5; the
  * Qiita article, sections "Gated-DeltaNet" (triangular systems for W and U) and
  * "Chunk Computation"), and the state is carried serially from chunk to chunk.
@@ -110,8 +112,8 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
  * kernel_ms, a HOST array of 4 floats that receives the device time in
  * milliseconds of each kernel of this call, taken with HIP events recorded
  * on `stream` around every launch: [0] packed-batch chunk table (0 when
- * cu_seqlens is NULL), [1] prep, [2] scan, [3] output (prep and output are 0
- * when there are no tokens).  Unlike gdn_chunk_fwd it BLOCKS until the call's
+ * cu_seqlens is NULL), [1] prep (0 when there are no tokens), [2] scan (which
+ * also writes O), [3] reserved, always 0.  Unlike gdn_chunk_fwd it BLOCKS until the call's
  * work on `stream` has finished.  Errors: as gdn_chunk_fwd, plus GDN_ERR_NULL
  * when kernel_ms is NULL. */
 gdn_status gdn_chunk_fwd_profiled(const void *q, const void *k, const void *v,
