@@ -123,6 +123,7 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         tm->mark(a.stream);
         geom.table = table;
         geom.seq_slot = seq_slot;
+        geom.bounds = bounds;
     }
     const T* q = static_cast<const T*>(a.q);
     const T* k = static_cast<const T*>(a.k);

@@ -20,6 +20,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16 raw bytes
 
 constexpr int kThreads = 256;   // 4 waves per workgroup (prep, step)
 
@@ -98,6 +99,7 @@ struct ChunkInfo {
 struct SeqGeom {
     const int* table;        // varlen: [slots][4] = {seq, t0, len, pad}; NULL for fixed length
     const int* seq_slot;     // varlen: [N+1] first slot of each sequence
+    const int* bounds;       // varlen: [N+1] clamped token offsets of the sequences
     int T;                   // fixed: tokens per sequence
     int chunks_per_seq;      // fixed: ceil(T / C)
     int C;

@@ -30,13 +30,18 @@ template <typename T, int DK, int C>
 struct PrepCfg {
     static constexpr int PAD = 16 / sizeof(T);           // keeps 16-byte row alignment
     static constexpr int LDK = DK + PAD;
-    static constexpr int LDA = C + 4;                     // fp32 A
-    static constexpr size_t OFF_K = 0;
-    static constexpr size_t OFF_A = OFF_K + sizeof(T) * C * LDK;
-    static constexpr size_t OFF_G = OFF_A + sizeof(float) * C * LDA;
+    static constexpr int LDA = C + 4;                     // fp32 A and T
+    static constexpr int LDR = 16 + 4;                    // fp32 16x16 scratch per wave
+    static constexpr int NB = C / 16;                     // 16-row diagonal blocks
+    static constexpr size_t SZ_K = sizeof(T) * C * LDK;
+    static constexpr size_t SZ_T = sizeof(float) * C * LDA;
+    static constexpr size_t OFF_K = 0;                    // K, then T (K is dead by then)
+    static constexpr size_t OFF_A = OFF_K + (SZ_K > SZ_T ? SZ_K : SZ_T);
+    static constexpr size_t OFF_R = OFF_A + sizeof(float) * C * LDA;
+    static constexpr size_t OFF_G = OFF_R + sizeof(float) * 4 * 16 * LDR;
     static constexpr size_t OFF_B = OFF_G + sizeof(float) * C;
     static constexpr size_t SMEM = OFF_B + sizeof(float) * C;
-    static_assert(C <= 64 && C % 16 == 0, "one wave solves the chunk's triangular system");
+    static_assert(C <= 64 && C % 16 == 0, "at most four 16-row blocks");
 };
 
 template <typename T, int DK, int C>
@@ -98,30 +103,64 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
     }
     __syncthreads();
 
-    // T = (I + A)^-1 by forward substitution; lane c owns column c of T and
-    // writes column c of Tb = T diag(beta) (each row store is contiguous).
-    if (w == 0) {
-        const int c = l;
-        float x[C];
+    // T = (I + A)^-1, blocked by 16 rows.  Diagonal blocks by forward
+    // substitution (wave 0, lane = 16 b + column); then, one block diagonal
+    // at a time, T_ij = -T_ii (sum_{j<=m<i} A_im T_mj) on fp32 MFMA.
+    float* sT = reinterpret_cast<float*>(smem + Cfg::OFF_K);
+    float* sR = reinterpret_cast<float*>(smem + Cfg::OFF_R) + w * 16 * Cfg::LDR;
+    using MF = Mfma<float>;
+    if (w == 0 && l < C) {
+        const int b = l >> 4, c = l & 15;
+        float x[16];
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
+        for (int i = 0; i < 16; ++i) {
+            const float* arow = sA + (16 * b + i) * Cfg::LDA + 16 * b;
             float acc = (i == c) ? 1.f : 0.f;
-            const float* arow = sA + i * Cfg::LDA;
 #pragma unroll
-            for (int j = 0; j < (i & ~3); j += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(arow + j);
-                acc -= a4.x * x[j] + a4.y * x[j + 1] + a4.z * x[j + 2] + a4.w * x[j + 3];
-            }
-#pragma unroll
-            for (int j = (i & ~3); j < i; ++j) acc -= arow[j] * x[j];
+            for (int j = 0; j < i; ++j) acc -= arow[j] * x[j];
             x[i] = acc;
         }
-        if (c < C) {
-            const float bc = sb[c];
-            T* out = Tb_ws + unit * C * C + c;
 #pragma unroll
-            for (int i = 0; i < C; ++i) out[i * C] = from_f32<T>(x[i] * bc);
+        for (int i = 0; i < 16; ++i) sT[(16 * b + i) * Cfg::LDA + 16 * b + c] = x[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d < Cfg::NB; ++d) {
+        const int j = w, i = w + d;          // wave w builds block (j + d, j)
+        const bool mine = w < Cfg::NB - d;
+        if (mine) {
+            f32x4 acc = zero4();
+            for (int kk = 16 * j; kk < 16 * i; kk += MF::KS)
+                acc = MF::mma(frag_kc(sA, Cfg::LDA, 16 * i, kk), frag_ks(sT, Cfg::LDA, kk, 16 * j), acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sR[(4 * (l >> 4) + r) * Cfg::LDR + (l & 15)] = acc[r];
         }
+        __syncthreads();
+        if (mine) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 16; kk += MF::KS)
+                acc = MF::mma(frag_kc(sT, Cfg::LDA, 16 * i, 16 * i + kk), frag_ks(sR, Cfg::LDR, kk, 0), acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sT[(16 * i + 4 * (l >> 4) + r) * Cfg::LDA + 16 * j + (l & 15)] = -acc[r];
+        }
+        __syncthreads();
+    }
+
+    // Tb = T diag(beta), row-major, zero above the diagonal; 16-byte stores
+    constexpr int EV = 16 / sizeof(T), VPR = C / EV;
+    T* out = Tb_ws + unit * C * C;
+    for (int idx = threadIdx.x; idx < C * VPR; idx += kThreads) {
+        const int i = idx / VPR, c0 = (idx - i * VPR) * EV;
+        union { uint4 u; T e[EV]; } pk;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+            const int c = c0 + e;
+            const bool lower = (c >> 4) < (i >> 4) || ((c >> 4) == (i >> 4) && c <= i);
+            pk.e[e] = from_f32<T>(lower ? sT[i * Cfg::LDA + c] * sb[c] : 0.f);
+        }
+        *reinterpret_cast<uint4*>(out + i * C + c0) = pk.u;
     }
 }
 

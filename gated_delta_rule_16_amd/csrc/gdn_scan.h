@@ -23,9 +23,10 @@
 // each token's prediction error against the chunk-start state, corrected by the
 // triangular solve) and section 4.5 (T, W, U do not depend on S).
 //
-// The next chunk's inputs (K, Q, the V slice, Tb, g) do not depend on S: they
-// are fetched into registers one chunk ahead and written to LDS at the end of
-// phase C, so the global-memory latency overlaps the serial work.
+// The chunks' inputs (K, Q, the V slice, Tb, g) do not depend on S: they are
+// fetched into a ring of register sets NPF chunks ahead and written to LDS at
+// the end of the previous chunk's phase C, so global-memory latency overlaps
+// the serial work.
 #pragma once
 
 #include "gdn_device.h"
@@ -48,6 +49,7 @@ struct ScanCfg {
     static constexpr int VV = C * DVT / EV, PV = (VV + NTHR - 1) / NTHR;
     static constexpr int VT = C * C / EV, PT = (VT + NTHR - 1) / NTHR;
     static constexpr int VG = C / 4;
+    static constexpr int NPF = sizeof(T) == 2 ? 3 : 2;   // chunks fetched ahead, in registers
     static constexpr size_t SZ_K = sizeof(T) * C * LDK;
     static constexpr size_t SZ_REST = SZ_K                       // Q
                                     + sizeof(T) * C * LDV        // V slice
@@ -76,70 +78,67 @@ struct ScanCfg {
 // Register-staged copy of one chunk's state-independent inputs.
 template <typename Cfg, typename T, int DK, int DV, int C, int DVT>
 struct ChunkFetch {
-    uint4 k[Cfg::PK], q[Cfg::PK], v[Cfg::PV], tb[Cfg::PT], g;
+    u32x4 k[Cfg::PK], q[Cfg::PK], v[Cfg::PV], tb[Cfg::PT], g;
 
+    // Every lane issues every load, unmasked (rows past the chunk end read row
+    // 0 of the chunk): nothing consumes the registers until store(), so the
+    // compiler waits only for the oldest register set.  store() zeroes the
+    // rows past the end.
     __device__ __forceinline__ void load(const T* __restrict__ kg, const T* __restrict__ qg,
                                          const T* __restrict__ vg, const float* __restrict__ g_ws,
-                                         const T* __restrict__ Tb_ws, const ChunkInfo& ci,
+                                         const T* __restrict__ Tb_ws, int t0, int len,
                                          int64_t unit, int H, int h, int v0) {
         const int tid = threadIdx.x;
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
         constexpr int RK = DK / Cfg::EV, RV = DVT / Cfg::EV;
 #pragma unroll
         for (int m = 0; m < Cfg::PK; ++m) {
-            const int i = tid + Cfg::NTHR * m;
+            const int i = (tid + Cfg::NTHR * m) % Cfg::VK;
             const int r = i / RK, c = (i - r * RK) * Cfg::EV;
-            k[m] = z;
-            q[m] = z;
-            if (i < Cfg::VK && r < ci.len) {
-                const int64_t off = ((int64_t)(ci.t0 + r) * H + h) * DK + c;
-                k[m] = *reinterpret_cast<const uint4*>(kg + off);
-                q[m] = *reinterpret_cast<const uint4*>(qg + off);
-            }
+            const int64_t off = ((int64_t)(t0 + (r < len ? r : 0)) * H + h) * DK + c;
+            k[m] = *reinterpret_cast<const u32x4*>(kg + off);
+            q[m] = *reinterpret_cast<const u32x4*>(qg + off);
         }
 #pragma unroll
         for (int m = 0; m < Cfg::PV; ++m) {
-            const int i = tid + Cfg::NTHR * m;
+            const int i = (tid + Cfg::NTHR * m) % Cfg::VV;
             const int r = i / RV, c = (i - r * RV) * Cfg::EV;
-            v[m] = z;
-            if (i < Cfg::VV && r < ci.len)
-                v[m] = *reinterpret_cast<const uint4*>(vg + ((int64_t)(ci.t0 + r) * H + h) * DV + v0 + c);
+            v[m] = *reinterpret_cast<const u32x4*>(
+                vg + ((int64_t)(t0 + (r < len ? r : 0)) * H + h) * DV + v0 + c);
         }
 #pragma unroll
         for (int m = 0; m < Cfg::PT; ++m) {
-            const int i = tid + Cfg::NTHR * m;
-            tb[m] = z;
-            if (i < Cfg::VT) tb[m] = *reinterpret_cast<const uint4*>(Tb_ws + unit * C * C + (int64_t)i * Cfg::EV);
+            const int i = (tid + Cfg::NTHR * m) % Cfg::VT;
+            tb[m] = *reinterpret_cast<const u32x4*>(Tb_ws + unit * C * C + (int64_t)i * Cfg::EV);
         }
-        g = z;
-        if (tid < Cfg::VG) g = *reinterpret_cast<const uint4*>(g_ws + unit * C + 4 * tid);
+        g = *reinterpret_cast<const u32x4*>(g_ws + unit * C + 4 * (tid % Cfg::VG));
     }
 
-    __device__ __forceinline__ void store(T* sK, T* sQ, T* sV, T* sTb, float* sg) const {
+    __device__ __forceinline__ void store(T* sK, T* sQ, T* sV, T* sTb, float* sg, int len) const {
         const int tid = threadIdx.x;
+        const u32x4 z = {0u, 0u, 0u, 0u};
         constexpr int RK = DK / Cfg::EV, RV = DVT / Cfg::EV, RT = C / Cfg::EV;
 #pragma unroll
         for (int m = 0; m < Cfg::PK; ++m) {
             const int i = tid + Cfg::NTHR * m;
             const int r = i / RK, c = (i - r * RK) * Cfg::EV;
             if (i < Cfg::VK) {
-                *reinterpret_cast<uint4*>(sK + r * Cfg::LDK + c) = k[m];
-                *reinterpret_cast<uint4*>(sQ + r * Cfg::LDK + c) = q[m];
+                *reinterpret_cast<u32x4*>(sK + r * Cfg::LDK + c) = r < len ? k[m] : z;
+                *reinterpret_cast<u32x4*>(sQ + r * Cfg::LDK + c) = r < len ? q[m] : z;
             }
         }
 #pragma unroll
         for (int m = 0; m < Cfg::PV; ++m) {
             const int i = tid + Cfg::NTHR * m;
             const int r = i / RV, c = (i - r * RV) * Cfg::EV;
-            if (i < Cfg::VV) *reinterpret_cast<uint4*>(sV + r * Cfg::LDV + c) = v[m];
+            if (i < Cfg::VV) *reinterpret_cast<u32x4*>(sV + r * Cfg::LDV + c) = r < len ? v[m] : z;
         }
 #pragma unroll
         for (int m = 0; m < Cfg::PT; ++m) {
             const int i = tid + Cfg::NTHR * m;
             const int r = i / RT, c = (i - r * RT) * Cfg::EV;
-            if (i < Cfg::VT) *reinterpret_cast<uint4*>(sTb + r * Cfg::LDC + c) = tb[m];
+            if (i < Cfg::VT) *reinterpret_cast<u32x4*>(sTb + r * Cfg::LDC + c) = tb[m];
         }
-        if (tid < Cfg::VG) *reinterpret_cast<uint4*>(sg + 4 * tid) = g;
+        if (tid < Cfg::VG) *reinterpret_cast<u32x4*>(sg + 4 * tid) = g;
     }
 };
 
@@ -198,131 +197,171 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(
         }
     }
 
-    int first, count;
-    seq_slots(geom, seq, first, count);
-    ChunkFetch<Cfg, T, DK, DV, C, DVT> pf;
+    // this sequence's tokens [ts, te) and first chunk slot, read once; chunk cc
+    // covers tokens ts + cc C .. min(ts + (cc + 1) C, te) - 1 in slot first + cc
+    int ts, te, first;
+    if (geom.table) {
+        ts = geom.bounds[seq];
+        te = geom.bounds[seq + 1];
+        first = geom.seq_slot[seq];
+    } else {
+        ts = seq * geom.T;
+        te = ts + geom.T;
+        first = seq * geom.chunks_per_seq;
+    }
+    const int count = (te - ts + C - 1) / C;
+    auto fetch = [&](auto& dst, int cc) __attribute__((always_inline)) {
+        const int t0 = ts + cc * C;
+        const int len = min(C, te - t0);
+        dst.load(k, q, v, g_ws, Tb_ws, t0, len, (int64_t)(first + cc) * H + h, H, h, v0);
+    };
+    // register ring: chunk j of the sequence is fetched into set j % NPF,
+    // NPF chunks before it is needed, and written to LDS one chunk ahead
+    using Fetch = ChunkFetch<Cfg, T, DK, DV, C, DVT>;
+    static_assert(Cfg::NPF == 2 || Cfg::NPF == 3, "ring of two or three register sets");
+    Fetch pf0, pf1, pf2;   // pf2 unused when NPF == 2
     if (count > 0) {
-        const ChunkInfo c0 = chunk_info(geom, first);
-        pf.load(k, q, v, g_ws, Tb_ws, c0, (int64_t)first * H + h, H, h, v0);
-        pf.store(sK0, sQ, sV, sTb, sg);
-        if (count > 1) {
-            const ChunkInfo c1 = chunk_info(geom, first + 1);
-            pf.load(k, q, v, g_ws, Tb_ws, c1, (int64_t)(first + 1) * H + h, H, h, v0);
+        fetch(pf0, 0);
+        pf0.store(sK0, sQ, sV, sTb, sg, min(C, te - ts));
+        fetch(pf1, min(1, count - 1));
+        if constexpr (Cfg::NPF == 3) {
+            fetch(pf2, min(2, count - 1));
+            fetch(pf0, min(3, count - 1));
+        } else {
+            fetch(pf0, min(2, count - 1));
         }
     }
     __syncthreads();
 
-    for (int cc = 0; cc < count; ++cc) {
-        const ChunkInfo ci = chunk_info(geom, first + cc);
-        T* sK = sK0 + (Cfg::KBUF == 2 ? (cc & 1) : 0) * (Cfg::SZ_K / sizeof(T));
+    auto chunk_step = [&](const int cc, Fetch& nxt) __attribute__((always_inline)) {
+            ChunkInfo ci;
+            ci.t0 = ts + cc * C;
+            ci.len = min(C, te - ci.t0);
+            T* sK = sK0 + (Cfg::KBUF == 2 ? (cc & 1) : 0) * (Cfg::SZ_K / sizeof(T));
 
-        // ---- phase A: Y = K S^T and Z = Q S^T; X = V - diag(gamma) Y (to LDS, transposed)
-        const float gn = sg[C - 1];
-        f32x4 Zr[Cfg::TPO];
+            // ---- phase A: Y = K S^T and Z = Q S^T; X = V - diag(gamma) Y (to LDS, transposed)
+            const float gn = sg[C - 1];
+            f32x4 Zr[Cfg::TPO];
 #pragma unroll
-        for (int m = 0; m < Cfg::TPO; ++m) {
-            const int t = w + NW * m;
-            Zr[m] = zero4();
-            if (t < Cfg::NTO) {
-                const int cb = t / Cfg::NVB, vb = t - cb * Cfg::NVB;
-                f32x4 accY = zero4(), accZ = zero4();
+            for (int m = 0; m < Cfg::TPO; ++m) {
+                const int t = w + NW * m;
+                Zr[m] = zero4();
+                if (t < Cfg::NTO) {
+                    const int cb = t / Cfg::NVB, vb = t - cb * Cfg::NVB;
+                    f32x4 accY = zero4(), accZ = zero4();
 #pragma unroll
-                for (int kk = 0; kk < DK; kk += M::KS) {
-                    const auto bS = frag_kc(sSb, Cfg::LDK, vb * 16, kk);
-                    accY = M::mma(frag_kc(sK, Cfg::LDK, cb * 16, kk), bS, accY);
-                    accZ = M::mma(frag_kc(sQ, Cfg::LDK, cb * 16, kk), bS, accZ);
-                }
-                const int vv = vb * 16 + n;
+                    for (int kk = 0; kk < DK; kk += M::KS) {
+                        const auto bS = frag_kc(sSb, Cfg::LDK, vb * 16, kk);
+                        accY = M::mma(frag_kc(sK, Cfg::LDK, cb * 16, kk), bS, accY);
+                        accZ = M::mma(frag_kc(sQ, Cfg::LDK, cb * 16, kk), bS, accZ);
+                    }
+                    const int vv = vb * 16 + n;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int c = cb * 16 + g4 + r;
-                    const float gam = __expf(sg[c]);
-                    sXt[vv * Cfg::LDC + c] = from_f32<T>(to_f32(sV[c * Cfg::LDV + vv]) - gam * accY[r]);
-                    Zr[m][r] = gam * accZ[r];
+                    for (int r = 0; r < 4; ++r) {
+                        const int c = cb * 16 + g4 + r;
+                        const float gam = __expf(sg[c]);
+                        sXt[vv * Cfg::LDC + c] = from_f32<T>(to_f32(sV[c * Cfg::LDV + vv]) - gam * accY[r]);
+                        Zr[m][r] = gam * accZ[r];
+                    }
                 }
             }
-        }
-        __syncthreads();
+            __syncthreads();
 
-        // ---- phase B: V' = Tb X (plain and decayed copies, transposed); P
+            // ---- phase B: V' = Tb X (plain and decayed copies, transposed); P
 #pragma unroll
-        for (int m = 0; m < Cfg::TPO; ++m) {
-            const int t = w + NW * m;
-            if (t < Cfg::NTO) {
-                const int cb = t / Cfg::NVB, vb = t - cb * Cfg::NVB;
-                const int kend = ((cb + 1) * 16 + M::KS - 1) / M::KS * M::KS;
+            for (int m = 0; m < Cfg::TPO; ++m) {
+                const int t = w + NW * m;
+                if (t < Cfg::NTO) {
+                    const int cb = t / Cfg::NVB, vb = t - cb * Cfg::NVB;
+                    const int kend = ((cb + 1) * 16 + M::KS - 1) / M::KS * M::KS;
+                    f32x4 acc = zero4();
+                    for (int kk = 0; kk < kend; kk += M::KS)
+                        acc = M::mma(frag_kc(sTb, Cfg::LDC, cb * 16, kk), frag_kc(sXt, Cfg::LDC, vb * 16, kk), acc);
+                    const int vv = vb * 16 + n;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int c = cb * 16 + g4 + r;
+                        sVpt[vv * Cfg::LDC + c] = from_f32<T>(acc[r]);
+                        sVdt[vv * Cfg::LDC + c] = from_f32<T>(acc[r] * __expf(gn - sg[c]));
+                    }
+                }
+            }
+            for (int t = w; t < Cfg::NTP; t += NW) {
+                int cb, jb;
+                lower_tile(t, cb, jb);
                 f32x4 acc = zero4();
-                for (int kk = 0; kk < kend; kk += M::KS)
-                    acc = M::mma(frag_kc(sTb, Cfg::LDC, cb * 16, kk), frag_kc(sXt, Cfg::LDC, vb * 16, kk), acc);
-                const int vv = vb * 16 + n;
+#pragma unroll
+                for (int kk = 0; kk < DK; kk += M::KS)
+                    acc = M::mma(frag_kc(sQ, Cfg::LDK, cb * 16, kk), frag_kc(sK, Cfg::LDK, jb * 16, kk), acc);
+                const int j = jb * 16 + n;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int c = cb * 16 + g4 + r;
-                    sVpt[vv * Cfg::LDC + c] = from_f32<T>(acc[r]);
-                    sVdt[vv * Cfg::LDC + c] = from_f32<T>(acc[r] * __expf(gn - sg[c]));
+                    const int i = cb * 16 + g4 + r;
+                    sP[i * Cfg::LDC + j] = from_f32<T>(j <= i ? acc[r] * __expf(sg[i] - sg[j]) : 0.f);
                 }
             }
-        }
-        for (int t = w; t < Cfg::NTP; t += NW) {
-            int cb, jb;
-            lower_tile(t, cb, jb);
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < DK; kk += M::KS)
-                acc = M::mma(frag_kc(sQ, Cfg::LDK, cb * 16, kk), frag_kc(sK, Cfg::LDK, jb * 16, kk), acc);
-            const int j = jb * 16 + n;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = cb * 16 + g4 + r;
-                sP[i * Cfg::LDC + j] = from_f32<T>(j <= i ? acc[r] * __expf(sg[i] - sg[j]) : 0.f);
-            }
-        }
-        const float gamma_n = __expf(gn);
-        __syncthreads();
+            const float gamma_n = __expf(gn);
+            __syncthreads();
 
-        // ---- phase C: O = diag(gamma) Z + P V';  S <- gamma_n S + V'd^T K
+            // ---- phase C: O = diag(gamma) Z + P V';  S <- gamma_n S + V'd^T K
 #pragma unroll
-        for (int m = 0; m < Cfg::TPO; ++m) {
-            const int t = w + NW * m;
-            if (t < Cfg::NTO) {
-                const int cb = t / Cfg::NVB, vb = t - cb * Cfg::NVB;
-                const int kend = ((cb + 1) * 16 + M::KS - 1) / M::KS * M::KS;
-                f32x4 acc = Zr[m];
-                for (int kk = 0; kk < kend; kk += M::KS)
-                    acc = M::mma(frag_kc(sP, Cfg::LDC, cb * 16, kk), frag_kc(sVpt, Cfg::LDC, vb * 16, kk), acc);
-                const int vv = v0 + vb * 16 + n;
+            for (int m = 0; m < Cfg::TPO; ++m) {
+                const int t = w + NW * m;
+                if (t < Cfg::NTO) {
+                    const int cb = t / Cfg::NVB, vb = t - cb * Cfg::NVB;
+                    const int kend = ((cb + 1) * 16 + M::KS - 1) / M::KS * M::KS;
+                    f32x4 acc = Zr[m];
+                    for (int kk = 0; kk < kend; kk += M::KS)
+                        acc = M::mma(frag_kc(sP, Cfg::LDC, cb * 16, kk), frag_kc(sVpt, Cfg::LDC, vb * 16, kk), acc);
+                    const int vv = v0 + vb * 16 + n;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int c = cb * 16 + g4 + r;
-                    if (c < ci.len) O[((int64_t)(ci.t0 + c) * H + h) * DV + vv] = from_f32<T>(acc[r]);
+                    for (int r = 0; r < 4; ++r) {
+                        const int c = cb * 16 + g4 + r;
+                        if (c < ci.len) O[((int64_t)(ci.t0 + c) * H + h) * DV + vv] = from_f32<T>(acc[r]);
+                    }
                 }
             }
-        }
 #pragma unroll
-        for (int m = 0; m < Cfg::TPS; ++m) {
-            const int t = w + NW * m;
-            if (t < Cfg::NTS) {
-                const int vb = t / Cfg::NDB, db = t - vb * Cfg::NDB;
-                f32x4 acc = S[m] * gamma_n;
+            for (int m = 0; m < Cfg::TPS; ++m) {
+                const int t = w + NW * m;
+                if (t < Cfg::NTS) {
+                    const int vb = t / Cfg::NDB, db = t - vb * Cfg::NDB;
+                    f32x4 acc = S[m] * gamma_n;
 #pragma unroll
-                for (int kk = 0; kk < C; kk += M::KS)
-                    acc = M::mma(frag_kc(sVdt, Cfg::LDC, vb * 16, kk), frag_ks(sK, Cfg::LDK, kk, db * 16), acc);
-                S[m] = acc;
-                const int vr = vb * 16 + g4, dc = db * 16 + n;
+                    for (int kk = 0; kk < C; kk += M::KS)
+                        acc = M::mma(frag_kc(sVdt, Cfg::LDC, vb * 16, kk), frag_ks(sK, Cfg::LDK, kk, db * 16), acc);
+                    S[m] = acc;
+                    const int vr = vb * 16 + g4, dc = db * 16 + n;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sSb[(vr + r) * Cfg::LDK + dc] = from_f32<T>(acc[r]);
+                    for (int r = 0; r < 4; ++r) sSb[(vr + r) * Cfg::LDK + dc] = from_f32<T>(acc[r]);
+                }
             }
-        }
-        if (cc + 1 < count) {
-            if constexpr (Cfg::KBUF == 1) __syncthreads();   // the update above still reads sK
-            T* sKn = sK0 + (Cfg::KBUF == 2 ? ((cc + 1) & 1) : 0) * (Cfg::SZ_K / sizeof(T));
-            pf.store(sKn, sQ, sV, sTb, sg);
-            if (cc + 2 < count) {
-                const ChunkInfo cn = chunk_info(geom, first + cc + 2);
-                pf.load(k, q, v, g_ws, Tb_ws, cn, (int64_t)(first + cc + 2) * H + h, H, h, v0);
+            if (cc + 1 < count) {
+                if constexpr (Cfg::KBUF == 1) __syncthreads();   // the update above still reads sK
+                T* sKn = sK0 + (Cfg::KBUF == 2 ? ((cc + 1) & 1) : 0) * (Cfg::SZ_K / sizeof(T));
+                nxt.store(sKn, sQ, sV, sTb, sg, min(C, te - (ci.t0 + C)));
             }
+            // refill this register set (past the end: re-read the last chunk, unused)
+            fetch(nxt, min(cc + 1 + Cfg::NPF, count - 1));
+            __syncthreads();
+    };
+
+    // chunk c + 1 sits in set (c + 1) % NPF
+    int base = 0;
+    if constexpr (Cfg::NPF == 3) {
+        for (; base + 3 <= count; base += 3) {
+            chunk_step(base, pf1);
+            chunk_step(base + 1, pf2);
+            chunk_step(base + 2, pf0);
         }
-        __syncthreads();
+        if (base < count) chunk_step(base, pf1);
+        if (base + 1 < count) chunk_step(base + 1, pf2);
+    } else {
+        for (; base + 2 <= count; base += 2) {
+            chunk_step(base, pf1);
+            chunk_step(base + 1, pf0);
+        }
+        if (base < count) chunk_step(base, pf1);
     }
 
     if (S_T) {
