@@ -67,7 +67,7 @@ Layout make_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int6
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
     const size_t u = (size_t)(L.slots * H);
-    L.g = take(u * C * sizeof(float));
+    L.g = take(u * 3 * C * sizeof(float));   // g, exp(g), exp(g_n - g) per chunk
     L.Tb = take(u * C * C * es);
     if (varlen) {
         L.bounds = take((size_t)(n_seqs + 1) * sizeof(int));
@@ -142,6 +142,7 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     {
         constexpr int DVT = DV >= 32 ? 32 : 16;
         using S = ScanCfg<T, DK, DV, C, DVT>;
+        static_assert(S::NTHR <= 256, "scan launch bounds");
         constexpr auto ks = gdn_scan_kernel<T, DK, DV, C, DVT>;
         allow_smem<ks>(S::SMEM);
         tm->mark(a.stream);

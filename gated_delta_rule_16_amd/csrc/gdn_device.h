@@ -25,7 +25,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16 raw byte
 constexpr int kThreads = 256;   // 4 waves per workgroup (prep, step)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// wave index, known to the compiler to be uniform across the wave
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 template <typename T> struct Mfma;
 

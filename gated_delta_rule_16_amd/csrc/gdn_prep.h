@@ -5,7 +5,8 @@
 //   g_i  = sum_{t<=i} log alpha_t              in-chunk inclusive cumulative log-gate
 //   A    = strict_lower( diag(beta) (K K^T o Gamma) ),   Gamma_ij = exp(g_i - g_j)
 //   T    = (I + A)^-1                           unit lower triangular
-//   Tb   = T diag(beta)                         stored (input dtype), with g (fp32)
+//   Tb   = T diag(beta)                         stored (input dtype), with g, exp(g) and
+//                                               exp(g_n - g) (fp32, [3][C] per chunk)
 // The scan kernel applies Tb to the chunk's prediction errors:
 //   V' = Tb (V - diag(gamma) K S^T) = U - W S^T,  U = T diag(beta) V,
 //   W = T diag(beta o gamma) K,  gamma_i = exp(g_i).
@@ -76,10 +77,14 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
             const float y = __shfl_up(la, off, 64);
             if (l >= off) la += y;
         }
+        const float glast = __shfl(la, C - 1, 64);
         if (l < C) {
             sg[l] = la;
             sb[l] = b;
-            g_ws[unit * C + l] = la;
+            float* gout = g_ws + unit * 3 * C;
+            gout[l] = la;                            // g_i
+            gout[C + l] = __expf(la);                // gamma_i = exp(g_i)
+            gout[2 * C + l] = __expf(glast - la);    // gamma_n / gamma_i
         }
     }
     stage_tokens<T, DK, kThreads>(sK, Cfg::LDK, k, ci.t0, ci.len, C, H, h);

@@ -50,10 +50,11 @@ def test_prep_intermediates(dtype, Dk, Dv, C, tol):
     cps = (T + C - 1) // C
     u = B * cps * H
     off_g = 0
-    off_t = _align(off_g + u * C * 4)
+    off_t = _align(off_g + u * 3 * C * 4)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     wsc = ws.cpu()
-    g_all = wsc[off_g:off_g + u * C * 4].view(torch.float32).view(cps, H, C).double().numpy()
+    g3 = wsc[off_g:off_g + u * 3 * C * 4].view(torch.float32).view(cps, H, 3, C).double().numpy()
+    g_all = g3[:, :, 0]
     Tb_all = wsc[off_t:off_t + u * C * C * es].view(tdt).view(cps, H, C, C).double().numpy()
     for c in range(cps):
         t0, n = c * C, min(C, T - c * C)
@@ -64,6 +65,8 @@ def test_prep_intermediates(dtype, Dk, Dv, C, tol):
             la = inp.log_alpha[0, t0:t0 + n, h].double().numpy()
             g, Tb = chunk_algebra(K, V, be, la)
             assert np.abs(g_all[c, h, :n] - g).max() < 1e-5
+            assert np.abs(g3[c, h, 1, :n] - np.exp(g)).max() < 1e-5
+            assert np.abs(g3[c, h, 2, :n] - np.exp(g[-1] - g)).max() < 1e-5
             got = Tb_all[c, h, :n, :n]
             assert np.abs(got - Tb).max() / np.abs(Tb).max() < tol, (c, h, "Tb")
             assert not np.any(Tb_all[c, h, n:]) and not np.any(Tb_all[c, h, :, n:]), "padding"
