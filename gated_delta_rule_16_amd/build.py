@@ -17,6 +17,10 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # no packed fp32 (v_pk_*_f32) code generation
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the kernels fit in 256 of them, and
+    # accumulation registers would cost a copy for every tile that is reused
+    # as an operand or rescaled
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

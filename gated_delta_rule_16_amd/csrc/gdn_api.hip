@@ -102,6 +102,14 @@ struct KernelTimer {
 };
 
 template <typename T, int DK, int DV, int C>
+constexpr int scan_columns() {
+    if constexpr (DV >= 32) {
+        if constexpr (ScanCfg<T, DK, DV, C, 32>::FITS) return 32;
+    }
+    return 16;
+}
+
+template <typename T, int DK, int DV, int C>
 gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     const bool varlen = a.cu != nullptr;
     const Layout L = make_layout(a.B, a.T, a.H, DK, DV, C, varlen, a.n_seqs, sizeof(T));
@@ -140,9 +148,11 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         tm->mark(a.stream);
     }
     {
-        constexpr int DVT = DV >= 32 ? 32 : 16;
+        // state columns per workgroup: 32 (two column blocks, 8 waves) where the
+        // staged chunk leaves room in LDS, else 16
+        constexpr int DVT = scan_columns<T, DK, DV, C>();
         using S = ScanCfg<T, DK, DV, C, DVT>;
-        static_assert(S::NTHR <= 256, "scan launch bounds");
+        static_assert(S::NTHR <= 512, "scan launch bounds");
         constexpr auto ks = gdn_scan_kernel<T, DK, DV, C, DVT>;
         allow_smem<ks>(S::SMEM);
         tm->mark(a.stream);
@@ -196,6 +206,8 @@ gdn_status check_sizes(int B, int T, int H, int Dk, int Dv, int C, bool varlen, 
     if (tokens * H * dmax > kMaxElems) return GDN_ERR_SHAPE;
     const int64_t N = varlen ? n_seqs : B;
     if (N * H * (int64_t)Dv * Dk > kMaxElems) return GDN_ERR_SHAPE;
+    // the scan addresses one chunk of one token tensor with 31-bit byte offsets
+    if ((int64_t)C * H * dmax * elem_size(dt) > kMaxElems) return GDN_ERR_SHAPE;
     if (!find_variant(Dk, Dv, C, dt)) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }

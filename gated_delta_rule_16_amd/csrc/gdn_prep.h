@@ -5,8 +5,9 @@
 //   g_i  = sum_{t<=i} log alpha_t              in-chunk inclusive cumulative log-gate
 //   A    = strict_lower( diag(beta) (K K^T o Gamma) ),   Gamma_ij = exp(g_i - g_j)
 //   T    = (I + A)^-1                           unit lower triangular
-//   Tb   = T diag(beta)                         stored (input dtype), with g, exp(g) and
-//                                               exp(g_n - g) (fp32, [3][C] per chunk)
+//   Tb   = T diag(beta)                         stored (input dtype; bf16 rows with the
+//                                               column order described at the store), with
+//                                               g, exp(g), exp(g_n - g) (fp32, [3][C] per chunk)
 // The scan kernel applies Tb to the chunk's prediction errors:
 //   V' = Tb (V - diag(gamma) K S^T) = U - W S^T,  U = T diag(beta) V,
 //   W = T diag(beta o gamma) K,  gamma_i = exp(g_i).
@@ -153,15 +154,19 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
         __syncthreads();
     }
 
-    // Tb = T diag(beta), row-major, zero above the diagonal; 16-byte stores
+    // Tb = T diag(beta), zero above the diagonal; 16-byte stores.  fp32 rows are
+    // plain; a bf16 row stores each 32-column group as the 4-column runs
+    // (0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31), so that the 16 bytes at
+    // group offset 8g are the operand of a 16-deep block pair (4g .. 4g+3 of both)
     constexpr int EV = 16 / sizeof(T), VPR = C / EV;
+    static_assert(sizeof(T) == 4 || C % 32 == 0, "bf16 Tb groups of 32 columns");
     T* out = Tb_ws + unit * C * C;
     for (int idx = threadIdx.x; idx < C * VPR; idx += kThreads) {
         const int i = idx / VPR, c0 = (idx - i * VPR) * EV;
         union { uint4 u; T e[EV]; } pk;
 #pragma unroll
         for (int e = 0; e < EV; ++e) {
-            const int c = c0 + e;
+            const int c = sizeof(T) == 4 ? c0 + e : (c0 & ~31) + 16 * (e >> 2) + ((c0 & 31) >> 1) + (e & 3);
             const bool lower = (c >> 4) < (i >> 4) || ((c >> 4) == (i >> 4) && c <= i);
             pk.e[e] = from_f32<T>(lower ? sT[i * Cfg::LDA + c] * sb[c] : 0.f);
         }

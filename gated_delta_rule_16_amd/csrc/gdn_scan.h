@@ -9,11 +9,10 @@
 //
 // Per chunk (row form, S = state at the chunk start, Dv x Dk; gamma_i = exp(g_i);
 // Tb = T diag(beta) from the prep kernel):
-//   phase A   Y = K S^T,  Z^T = S Q^T,  P^T = K Q^T      (all read only S)
-//             X = V - diag(gamma) Y                       prediction errors vs. the gated start state
-//   phase B   V' = Tb X   (= U - W S^T)                   corrected for the chunk's earlier writes
-//   phase C   O^T = Z^T diag(gamma) + V'^T P^T            P = (Q K^T) o Gamma o M
-//             S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V'
+//   Y  = K S^T,   X = V - diag(gamma) Y            prediction errors vs. the gated start state
+//   V' = Tb X     (= U - W S^T)                    corrected for the chunk's earlier writes
+//   O^T = Z^T diag(gamma) + V'^T P^T,  Z^T = S Q^T, P = (Q K^T) o Gamma o M
+//   S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V'
 // Sources: the same Qiita section (product form of S_i with I - sum w k^T =
 // A_1..A_i and the G_i identity; parallel form H = S0 (Q - W (M^T o K^T Q)) D_gamma
 // + U (Gamma o K^T Q) restricted to one chunk) and its section "Chunk
@@ -22,19 +21,30 @@
 // each token's prediction error against the chunk-start state, corrected by the
 // triangular solve) and section 4.5 (T, W, U do not depend on S).
 //
-// Work split: wave w owns token block w (16 tokens) for Y, Z, P, V' and O, and
-// d-blocks w, w + NW, ... of the state.  Operands are reused from registers
-// where the MFMA layouts allow it:
-//  - the Q fragments of a wave come straight from global memory (no LDS);
-//  - P^T and Z^T stay in the registers of the wave that computes them and feed
-//    the output product directly (a 16x16 accumulator tile has the lane layout
-//    of a 16-deep B operand);
-//  - S^T, X, V' go through LDS once per chunk, with 8-byte stores.
-// K is staged in LDS with 16-byte blocks XOR-swizzled by row group, which keeps
-// both its row reads and its column gathers free of bank conflicts (32 banks).
-// The chunks' state-independent inputs are fetched into a ring of register
-// sets NPF chunks ahead, with unconditional loads so that the compiler waits
-// only for the oldest set.
+// Work split: one wave per (token block cb, 16-column block vb) tile, NW x NVB
+// waves (8 for a 64-token chunk and a 32-column slice, two per SIMD).  Per chunk:
+//  phase A  each wave computes its tile of Y and Z^T and the P^T tiles of its
+//           token block, and writes its tile of X (transposed) to LDS; barrier;
+//  phase B  each wave computes V' for all token blocks of its column block
+//           from X^T and Tb (that small redundancy keeps V' in registers for
+//           both O and the state update), its O tile, and its two tiles of the
+//           new state (d-blocks cb, cb + NW), whose copy goes to LDS; barrier.
+// Register tiles feed MFMAs directly: a 16x16 accumulator tile (lane (g, n):
+// rows 4g..4g+3 of column n) is, per lane, an operand of a 16-deep contraction
+// block -- B when its rows are the contraction index, A of its transpose when
+// its columns are -- and two such blocks form one 16x16x32 bf16 operand,
+// provided A and B pair the same blocks.
+//
+// Data movement:
+//  - K, Q, the V slice, Tb and the gates of chunk cc + 2 are loaded into
+//    registers at the start of step cc (range-checked buffer loads: rows past
+//    the chunk end read as zeros) and written to the free one of two LDS
+//    staging buffers at the end of step cc + 1.
+//  - O leaves through range-checked buffer stores, so the padded rows of a
+//    last chunk are dropped without a branch.
+//  - LDS pitches and XOR swizzles keep each access pattern free of bank
+//    conflicts on 32 banks; on bf16, columns of row-major K and V are read with
+//    the transposing LDS load, which hands each lane 4 rows of one column.
 #pragma once
 
 #include <type_traits>
@@ -44,32 +54,98 @@
 namespace gdn {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// acc += A[m0 + m][k0 + k] * B[k][n] over one 16-deep k block, where B is a 16x16
-// accumulator tile held in the MFMA D layout (lane (g, n): rows 4g..4g+3 of column n)
-// and A is read from LDS (row-major, leading dimension lda).
-template <typename T> struct RegB;
-template <> struct RegB<bf16> {
-    __device__ __forceinline__ static f32x4 mma(const bf16* A, int lda, int m0, int k0, f32x4 b,
-                                                f32x4 acc) {
-        const int l = lane_id();
-        const s16x4 a = *reinterpret_cast<const s16x4*>(A + (m0 + (l & 15)) * lda + k0 + 4 * (l >> 4));
-        const bf16x4 bb = {(bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, bb), acc, 0, 0, 0);
+// Word 3 of a raw buffer resource: 32-bit untyped data, range-checked against
+// the record count (out-of-range loads return 0, stores are dropped).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a byte offset past every record count
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// s_waitcnt with vmcnt <= vm and lgkmcnt = 0 (expcnt not waited on)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+}
+
+// One 16-byte step of a contraction along the rows of two row-major operands:
+// lane (g, n) holds elements [k0 + g*EV, k0 + (g+1)*EV) of row n (EV = 16 / sizeof(T)).
+// bf16: one 16x16x32 MFMA; fp32: four 16x16x4 MFMAs, step r contracting
+// k0 + 4g + r (the same assignment on both operands).
+template <typename T> struct Step;
+template <> struct Step<bf16> {
+    static constexpr int KS = 32;
+    typedef bf16x8 frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
-template <> struct RegB<float> {
-    __device__ __forceinline__ static f32x4 mma(const float* A, int lda, int m0, int k0, f32x4 b,
-                                                f32x4 acc) {
-        const int l = lane_id();
-        const float* a = A + (m0 + (l & 15)) * lda + k0 + 4 * (l >> 4);
+template <> struct Step<float> {
+    static constexpr int KS = 16;
+    typedef f32x4 frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
-        return acc;
+        for (int r = 0; r < 4; ++r) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], c, 0, 0, 0);
+        return c;
     }
 };
 
-// 4 consecutive values of one lane, rounded to T, as one 8- or 16-byte store
+// Operand of one 16-deep contraction block: lane (g, n) holds k = 4g .. 4g+3
+// for row / column n of the other dimension.  A 16x16 accumulator tile has
+// exactly this layout, with k = its row.
+template <typename T> struct K16;
+template <> struct K16<bf16> {
+    typedef s16x4 op;
+    __device__ __forceinline__ static op tile(f32x4 t) {
+        const bf16x4 v = {(bf16)t[0], (bf16)t[1], (bf16)t[2], (bf16)t[3]};
+        return __builtin_bit_cast(s16x4, v);
+    }
+    __device__ __forceinline__ static f32x4 mma1(op a, op b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+    // blocks (a0, b0) and (a1, b1) in one 16x16x32 instruction
+    __device__ __forceinline__ static f32x4 mma2(op a0, op a1, op b0, op b1, f32x4 c) {
+        const s16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return mma2p(__builtin_bit_cast(bf16x8, a), b0, b1, c);
+    }
+    // the A pair already packed (a0 in elements 0..3, a1 in 4..7)
+    __device__ __forceinline__ static f32x4 mma2p(bf16x8 a, op b0, op b1, f32x4 c) {
+        const s16x8 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+template <> struct K16<float> {
+    typedef f32x4 op;
+    __device__ __forceinline__ static op tile(f32x4 t) { return t; }
+    __device__ __forceinline__ static f32x4 mma1(op a, op b, f32x4 c) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], c, 0, 0, 0);
+        return c;
+    }
+    __device__ __forceinline__ static f32x4 mma2(op a0, op a1, op b0, op b1, f32x4 c) {
+        return mma1(a1, b1, mma1(a0, b0, c));
+    }
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(short x) {
+    return __builtin_bit_cast(float, (unsigned)(unsigned short)x << 16);
+}
+
+// Transposing 64-bit LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+// lane s supplies the address of 4 consecutive 16-bit values; lane j receives
+// value j % 4 of lane 4e + j / 4 as its element e.
+__device__ __forceinline__ s16x4 tr_read(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// 4 consecutive values of one lane, rounded to T, as one 8- or 16-byte LDS store
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
     if constexpr (sizeof(T) == 2) {
@@ -80,200 +156,239 @@ __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d)
     }
 }
 
+// One staged region of a chunk: `rows` rows of `blk` 16-byte blocks of data,
+// `pitch` blocks apart in LDS; data block b of row r sits at block b ^ swz(r).
+// Swizzle kinds: 0 none; 1 (K, bf16) 2 (r mod 4) + (r / 4 mod 2); 2 (V, bf16)
+// 2 (r / 2 mod 2); 3 (Tb, bf16) r mod 8.
+template <int KIND>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (KIND == 1) return 2 * (r & 3) + ((r >> 2) & 1);
+    else if constexpr (KIND == 2) return ((r >> 1) & 1) << 1;
+    else if constexpr (KIND == 3) return r & 7;
+    else return 0;
+}
+
 template <typename T, int DK, int DV, int C, int DVT>
 struct ScanCfg {
-    static constexpr int NW = C / 16, NTHR = NW * 64;      // one wave per 16-token block (<= 256 threads)
-    static constexpr int EV = 16 / sizeof(T);              // elements per 16 bytes
-    static constexpr int LDK = DK + EV, LDC = C + EV, LDV = DVT + EV;
-    static constexpr int NVB = DVT / 16, NDB = DK / 16, NDBW = NDB / NW;
-    static constexpr int KS = Mfma<T>::KS, NQ = DK / KS;   // Q fragments per lane
-    static constexpr int VK = C * DK / EV, PK = (VK + NTHR - 1) / NTHR;
-    static constexpr int VV = C * DVT / EV, PV = (VV + NTHR - 1) / NTHR;
-    static constexpr int VT = C * C / EV, PT = (VT + NTHR - 1) / NTHR;
-    static constexpr int VG = 3 * C / 4;                   // g, exp(g), exp(g_n - g)
-    static constexpr int PG = (VG + NTHR - 1) / NTHR;
-    static constexpr int NPF = 2;                          // chunks fetched ahead
-    static constexpr size_t SZ_K = sizeof(T) * C * LDK;
-    static constexpr size_t SZ_REST = sizeof(T) * C * LDV + sizeof(T) * C * LDC +
-                                      sizeof(T) * DVT * LDK + 3 * sizeof(T) * DVT * LDC +
-                                      sizeof(float) * 3 * C;
+    static constexpr bool BF = sizeof(T) == 2;
+    static constexpr int ES = sizeof(T);
+    static constexpr int NW = C / 16;                      // 16-token blocks of a chunk
+    static constexpr int NVB = DVT / 16;                   // 16-column blocks of the state slice
+    static constexpr int NWV = NW * NVB, NTHR = NWV * 64;  // one wave per (token block, column block)
+    static constexpr int EV = 16 / ES;                     // elements per 16 bytes
+    // Staged regions.  bf16: unpadded rows with XOR swizzles that make every
+    // access of the loop conflict-free on 32 banks -- 16-byte row reads of K and
+    // Tb (8 lanes, 8 consecutive rows, one column block) and the transposing
+    // reads of K and V (16 lanes, 4 consecutive rows, 2 adjacent blocks);
+    // fp32: rows padded by one block (pitch = 4 words mod 32).
+    static constexpr int KB = DK / EV, VB = DVT / EV, TB = C / EV;     // data blocks per row
+    static constexpr int KP = BF ? KB : KB + 1, VP = BF ? VB : VB + 1, TP = BF ? TB : TB + 1;
+    static constexpr int KSW = BF ? 1 : 0, VSW = BF ? 2 : 0, TSW = BF ? 3 : 0;
+    static constexpr int LDK = KP * EV, LDV = VP * EV, LDC = TP * EV;   // pitches (elements)
+    static constexpr int LDS = DK + EV;                    // state copy S[v][d]
+    // X^T exchange buffer: DVT rows of C tokens (bf16: the token order within
+    // each 32-token group pairs runs 4g.. and 16+4g.., see xcol; rows swizzled
+    // like Tb); fp32: plain rows padded by one block
+    static constexpr int XP = BF ? TB : TB + 1, XSW = BF ? 3 : 0;
+    static constexpr int NDB = DK / 16, NDBW = NDB / NW;   // d-blocks of the state per wave
+    static constexpr int NP = (NW + 1) / 2;                // pairs of token blocks
+    static constexpr int KS = Step<T>::KS, NQ = DK / KS;   // Q fragments per lane
+    static constexpr int NKK = DK / KS;                    // contraction steps over d
+    // staging buffer: regions K | V slice | Tb | gates | Q, each a whole number of
+    // 1 KB blocks; block i is filled by wave i % NWV (64 lanes x 16 bytes)
+    static constexpr int blocks(int bytes) { return (bytes + 1023) / 1024; }
+    static constexpr int NIK = blocks(C * LDK * ES), NIV = blocks(C * LDV * ES);
+    static constexpr int NIT = blocks(C * LDC * ES), NIG = blocks(3 * C * 4);
+    static constexpr size_t SZ_SB = ((size_t)DVT * LDS * ES + 15) / 16 * 16;
+    static constexpr size_t SZ_X = (size_t)DVT * XP * 16;
     static constexpr size_t LDS_MAX = 160 * 1024;
-    static constexpr int KBUF = (2 * SZ_K + SZ_REST <= LDS_MAX) ? 2 : 1;
-    static constexpr size_t OFF_K = 0;
-    static constexpr size_t OFF_V = OFF_K + KBUF * SZ_K;
-    static constexpr size_t OFF_TB = OFF_V + sizeof(T) * C * LDV;
-    static constexpr size_t OFF_SB = OFF_TB + sizeof(T) * C * LDC;
-    static constexpr size_t OFF_XT = OFF_SB + sizeof(T) * DVT * LDK;
-    static constexpr size_t OFF_VPT = OFF_XT + sizeof(T) * DVT * LDC;
-    static constexpr size_t OFF_VDT = OFF_VPT + sizeof(T) * DVT * LDC;
-    static constexpr size_t OFF_G = OFF_VDT + sizeof(T) * DVT * LDC;
-    static constexpr size_t SMEM = OFF_G + sizeof(float) * 3 * C;
-    static_assert(SMEM <= LDS_MAX, "scan workgroup exceeds the LDS of one CU");
-    static_assert(C % 16 == 0 && NW >= 1 && NW <= 4, "one to four 16-token blocks");
+    // Q is staged with the rest (laid out as K) when two staging buffers hold it;
+    // otherwise each wave loads its token block of Q into registers a chunk ahead
+    // Batches: batch j holds LDS blocks j*NWV .. j*NWV + NWV - 1, block j*NWV + w
+    // filled by wave w (one 16-byte load per lane).  Regions start on batch
+    // boundaries, so a batch belongs to one region -- K, Q, Tb -- except the
+    // last, which holds V then the gates when both fit in one batch.
+    static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+    static constexpr bool VG1 = NIV + NIG <= NWV;
+    static constexpr int NBK = cdiv(NIK, NWV), NBT = cdiv(NIT, NWV);
+    static constexpr int NBVG = VG1 ? 1 : cdiv(NIV, NWV) + cdiv(NIG, NWV);
+    static constexpr bool QLDS = 2 * (size_t)(2 * NBK + NBT + NBVG) * NWV * 1024 + SZ_SB + SZ_X <= LDS_MAX;
+    static constexpr int NBQ = QLDS ? NBK : 0;
+    static constexpr int NL = NBK + NBQ + NBT + NBVG;      // batches = staging loads per lane per chunk
+    static constexpr int JQ = NBK, JT = JQ + NBQ, JV = JT + NBT;   // first batch of each region
+    static constexpr int JG = VG1 ? JV : JV + cdiv(NIV, NWV);
+    static constexpr int BG0 = VG1 ? JV * NWV + NIV : JG * NWV;  // first block of the gates
+    static constexpr size_t SZ_STAGE = (size_t)NL * NWV * 1024;
+    static constexpr size_t OFF_Q = (size_t)JQ * NWV * 1024, OFF_T = (size_t)JT * NWV * 1024;
+    static constexpr size_t OFF_V = (size_t)JV * NWV * 1024, OFF_G = (size_t)BG0 * 1024;
+    static constexpr int NSTAGE = 2;                       // chunk cc in cc % 2; cc + 1 staged meanwhile
+    static constexpr size_t OFF_SB = NSTAGE * SZ_STAGE, OFF_X = OFF_SB + SZ_SB;
+    static constexpr size_t SMEM = OFF_X + SZ_X;
+    static constexpr bool FITS = SMEM <= LDS_MAX;
+    static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVB >= 1 && NVB <= 2, "tile counts");
+    static_assert(NTHR <= 512, "launch bounds");
     static_assert(DV % DVT == 0 && DVT % 16 == 0 && NDB % NW == 0, "tile shapes");
-    static_assert(C % KS == 0 && DK % KS == 0, "whole MFMA steps");
+    static_assert(DK % KS == 0 && DK % EV == 0 && DVT % EV == 0 && C % EV == 0, "whole 16-byte steps");
+    static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && VB % 4 == 0 && TB % 8 == 0),
+                  "bf16 swizzles: Tb and X^T in 32-column groups, K / V / Tb rows of 8 / 4 / 8 blocks");
 };
 
-// Element (r, c) of the staged K chunk: 16-byte block c / EV of row r is stored
-// at block (c / EV) ^ swz(r); swz(r) only flips block-index bits that stay below
-// DK / EV, so every row keeps its own blocks.
-template <typename Cfg>
-__device__ __forceinline__ int kswz(int r) {
-    constexpr int NBLK = Cfg::LDK / Cfg::EV - 1;      // blocks per row (DK / EV)
-    return NBLK >= 8 ? (((r >> 3) & 3) << 1) : 0;
+// element (r, c) of a staged region (pitch P blocks, swizzle kind W)
+template <typename Cfg, int P, int W>
+__device__ __forceinline__ int sidx(int r, int c) {
+    return (r * P + ((c / Cfg::EV) ^ swz<W>(r))) * Cfg::EV + (c % Cfg::EV);
 }
 template <typename Cfg>
-__device__ __forceinline__ int kidx(int r, int c) {
-    return r * Cfg::LDK + (((c / Cfg::EV) ^ kswz<Cfg>(r)) * Cfg::EV) + (c % Cfg::EV);
+__device__ __forceinline__ int kidx(int r, int c) { return sidx<Cfg, Cfg::KP, Cfg::KSW>(r, c); }
+template <typename Cfg>
+__device__ __forceinline__ int vidx(int r, int c) { return sidx<Cfg, Cfg::VP, Cfg::VSW>(r, c); }
+template <typename Cfg>
+__device__ __forceinline__ int tidx(int r, int c) { return sidx<Cfg, Cfg::TP, Cfg::TSW>(r, c); }
+// X^T: row v, physical column c
+template <typename Cfg>
+__device__ __forceinline__ int xidx(int v, int c) { return sidx<Cfg, Cfg::XP, Cfg::XSW>(v, c); }
+// physical column of token t in a bf16 row of Tb or X^T: within each 32-token
+// group, the 4-token runs are stored in the order 0, 16, 4, 20, 8, 24, 12, 28
+template <typename Cfg>
+__device__ __forceinline__ int xcol(int t) {
+    if constexpr (Cfg::BF) return (t & ~31) + (((t >> 2) & 3) << 3) + (((t >> 4) & 1) << 2) + (t & 3);
+    else return t;
 }
 
-// x32 (bf16) / x4 (fp32) fragment of swizzled K with the contraction along d
-// (rows = tokens): element (row0 + n, k0 + g*KPL + e)
-template <typename Cfg, typename T>
-__device__ __forceinline__ typename Mfma<T>::frag kfrag_rows(const T* sK, int row0, int k0) {
-    const int l = lane_id();
-    const int r = row0 + (l & 15);
-    const T* p = sK + kidx<Cfg>(r, k0 + (l >> 4) * Mfma<T>::KPL);
-    if constexpr (Mfma<T>::KPL == 8) return *reinterpret_cast<const bf16x8*>(p);
-    else return *p;
+// Byte offset, relative to the chunk's first row, of the 16 bytes that lane l
+// brings in for LDS block i (slot l of it), or kOutOfRange for padding.
+// rs_k / rs_v: bytes between consecutive tokens of K (and Q) / V.
+template <typename Cfg, int P, int B, int W>
+__device__ __forceinline__ int64_t region_offset(int s, int64_t row_bytes) {
+    const int r = s / P, p = s - r * P;
+    if (r >= Cfg::NW * 16 || p >= B) return -1;
+    return r * row_bytes + (int64_t)((p ^ swz<W>(r)) * 16);
 }
-// fragment of swizzled K with the contraction along tokens: element
-// (d = d0 + n, token k0 + g*KPL + e), i.e. K^T, gathered
+// region of staging batch j for wave w: 0 K, 1 Q, 2 Tb, 3 V, 4 gates, 5 padding
+template <typename Cfg>
+__device__ __forceinline__ int stage_region(int j, int w) {
+    if (j < Cfg::JQ) return 0;
+    if (j < Cfg::JT) return 1;
+    if (j < Cfg::JV) return 2;
+    const int i = j * Cfg::NWV + w;                      // LDS block
+    if (i < Cfg::JV * Cfg::NWV + Cfg::NIV) return 3;
+    if (i >= Cfg::BG0 && i < Cfg::BG0 + Cfg::NIG) return 4;
+    return 5;
+}
+template <typename Cfg>
+__device__ __forceinline__ uint32_t stage_offset(int j, int w, int l, int64_t rs_k, int64_t rs_v) {
+    constexpr int C = Cfg::NW * 16;
+    const int i = j * Cfg::NWV + w;
+    int64_t off = -1;
+    switch (stage_region<Cfg>(j, w)) {
+        case 0: off = region_offset<Cfg, Cfg::KP, Cfg::KB, Cfg::KSW>(i * 64 + l, rs_k); break;
+        case 1: off = region_offset<Cfg, Cfg::KP, Cfg::KB, Cfg::KSW>((i - Cfg::JQ * Cfg::NWV) * 64 + l, rs_k); break;
+        case 2: off = region_offset<Cfg, Cfg::TP, Cfg::TB, Cfg::TSW>((i - Cfg::JT * Cfg::NWV) * 64 + l,
+                                                                  (int64_t)C * Cfg::ES); break;
+        case 3: off = region_offset<Cfg, Cfg::VP, Cfg::VB, Cfg::VSW>((i - Cfg::JV * Cfg::NWV) * 64 + l, rs_v); break;
+        case 4: {
+            const int s = (i - Cfg::BG0) * 64 + l;
+            off = s < 3 * C / 4 ? (int64_t)s * 16 : -1;
+            break;
+        }
+        default: break;
+    }
+    return (off < 0 || off >= (int64_t)kOutOfRange) ? kOutOfRange : (uint32_t)off;
+}
+
+// Step fragment (16 bytes) of the swizzled K chunk: K[row0 + n][k0 + g*EV ...]
 template <typename Cfg, typename T>
-__device__ __forceinline__ typename Mfma<T>::frag kfrag_cols(const T* sK, int k0, int d0) {
+__device__ __forceinline__ typename Step<T>::frag kfrag_rows(const T* sK, int row0, int k0) {
     const int l = lane_id();
-    const int d = d0 + (l & 15), r0 = k0 + (l >> 4) * Mfma<T>::KPL;
-    if constexpr (Mfma<T>::KPL == 8) {
-        bf16x8 f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = sK[kidx<Cfg>(r0 + e, d)];
-        return f;
+    return *reinterpret_cast<const typename Step<T>::frag*>(
+        sK + kidx<Cfg>(row0 + (l & 15), k0 + (l >> 4) * Cfg::EV));
+}
+// Step fragment of a plain row-major LDS tile
+template <typename T>
+__device__ __forceinline__ typename Step<T>::frag frag16(const T* p, int ld, int row0, int k0) {
+    const int l = lane_id();
+    return *reinterpret_cast<const typename Step<T>::frag*>(p + (row0 + (l & 15)) * ld + k0 +
+                                                             (l >> 4) * (16 / sizeof(T)));
+}
+
+// K^T as the A operand of token block kb: lane (g, n) gets K[kb*16 + 4g + e][d0 + n]
+// (bf16: one transposing read -- lane s of group g supplies row kb*16 + 4g + s/4,
+// columns d0 + 4 (s%4) .. +3; fp32: a gather)
+template <typename Cfg, typename T>
+__device__ __forceinline__ typename K16<T>::op kT16(const T* sK, int kb, int d0) {
+    const int l = lane_id(), g = l >> 4, n = l & 15;
+    if constexpr (Cfg::BF) {
+        return tr_read(sK + kidx<Cfg>(kb * 16 + 4 * g + (n >> 2), d0 + 4 * (n & 3)));
     } else {
-        return sK[kidx<Cfg>(r0, d)];
+        const T* p = sK + kidx<Cfg>(kb * 16 + 4 * g, d0 + n);        // fp32 rows are not swizzled
+        return f32x4{p[0], p[Cfg::LDK], p[2 * Cfg::LDK], p[3 * Cfg::LDK]};
+    }
+}
+// V rows jb*16 + 4g + e, column vb*16 + n, as fp32
+template <typename Cfg, typename T>
+__device__ __forceinline__ f32x4 vcol4(const T* sV, int jb, int vb) {
+    const int l = lane_id(), g = l >> 4, n = l & 15;
+    if constexpr (Cfg::BF) {
+        const s16x4 x = tr_read(sV + vidx<Cfg>(jb * 16 + 4 * g + (n >> 2), vb * 16 + 4 * (n & 3)));
+        return f32x4{bf16_bits_to_f32(x[0]), bf16_bits_to_f32(x[1]), bf16_bits_to_f32(x[2]),
+                     bf16_bits_to_f32(x[3])};
+    } else {
+        const T* p = sV + vidx<Cfg>(jb * 16 + 4 * g, vb * 16 + n);   // fp32 rows are not swizzled
+        return f32x4{p[0], p[Cfg::LDV], p[2 * Cfg::LDV], p[3 * Cfg::LDV]};
     }
 }
 
-// Register-staged copy of one chunk's state-independent inputs: K, the V slice,
-// Tb and the gate rows for LDS, and this wave's Q fragments (token block w).
-template <typename Cfg, typename T, int DK, int DV, int C, int DVT>
-struct ChunkFetch {
-    u32x4 k[Cfg::PK], v[Cfg::PV], tb[Cfg::PT], g[Cfg::PG];
-    typename Mfma<T>::frag q[Cfg::NQ];
-
-    // Every lane issues every load, unmasked (rows past the chunk end read row 0
-    // of the chunk); store() and the Q consumer zero those rows.
-    __device__ __forceinline__ void load(const T* __restrict__ kg, const T* __restrict__ qg,
-                                         const T* __restrict__ vg, const float* __restrict__ g_ws,
-                                         const T* __restrict__ Tb_ws, int t0, int len,
-                                         int64_t unit, int H, int h, int v0) {
-        const int tid = threadIdx.x, l = lane_id(), w = wave_id();
-        constexpr int RK = DK / Cfg::EV, RV = DVT / Cfg::EV;
-#pragma unroll
-        for (int m = 0; m < Cfg::PK; ++m) {
-            const int i = (tid + Cfg::NTHR * m) % Cfg::VK;
-            const int r = i / RK, c = (i - r * RK) * Cfg::EV;
-            k[m] = *reinterpret_cast<const u32x4*>(kg + ((int64_t)(t0 + (r < len ? r : 0)) * H + h) * DK + c);
-        }
-#pragma unroll
-        for (int m = 0; m < Cfg::PV; ++m) {
-            const int i = (tid + Cfg::NTHR * m) % Cfg::VV;
-            const int r = i / RV, c = (i - r * RV) * Cfg::EV;
-            v[m] = *reinterpret_cast<const u32x4*>(
-                vg + ((int64_t)(t0 + (r < len ? r : 0)) * H + h) * DV + v0 + c);
-        }
-#pragma unroll
-        for (int m = 0; m < Cfg::PT; ++m) {
-            const int i = (tid + Cfg::NTHR * m) % Cfg::VT;
-            tb[m] = *reinterpret_cast<const u32x4*>(Tb_ws + unit * C * C + (int64_t)i * Cfg::EV);
-        }
-#pragma unroll
-        for (int m = 0; m < Cfg::PG; ++m) {
-            const int i = (tid + Cfg::NTHR * m) % Cfg::VG;
-            g[m] = *reinterpret_cast<const u32x4*>(g_ws + unit * 3 * C + 4 * i);
-        }
-        const int qr = w * 16 + (l & 15);
-        const T* qrow = qg + ((int64_t)(t0 + (qr < len ? qr : 0)) * H + h) * DK + (l >> 4) * Mfma<T>::KPL;
-#pragma unroll
-        for (int j = 0; j < Cfg::NQ; ++j) {
-            if constexpr (Mfma<T>::KPL == 8) q[j] = *reinterpret_cast<const bf16x8*>(qrow + j * Cfg::KS);
-            else q[j] = qrow[j * Cfg::KS];
-        }
-    }
-
-    __device__ __forceinline__ void store(T* sK, T* sV, T* sTb, float* sg, int len) const {
-        const int tid = threadIdx.x;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        constexpr int RK = DK / Cfg::EV, RV = DVT / Cfg::EV, RT = C / Cfg::EV;
-#pragma unroll
-        for (int m = 0; m < Cfg::PK; ++m) {
-            const int i = tid + Cfg::NTHR * m;
-            const int r = i / RK, c = (i - r * RK) * Cfg::EV;
-            if (i < Cfg::VK) *reinterpret_cast<u32x4*>(sK + kidx<Cfg>(r, c)) = r < len ? k[m] : z;
-        }
-#pragma unroll
-        for (int m = 0; m < Cfg::PV; ++m) {
-            const int i = tid + Cfg::NTHR * m;
-            const int r = i / RV, c = (i - r * RV) * Cfg::EV;
-            if (i < Cfg::VV) *reinterpret_cast<u32x4*>(sV + r * Cfg::LDV + c) = r < len ? v[m] : z;
-        }
-#pragma unroll
-        for (int m = 0; m < Cfg::PT; ++m) {
-            const int i = tid + Cfg::NTHR * m;
-            const int r = i / RT, c = (i - r * RT) * Cfg::EV;
-            if (i < Cfg::VT) *reinterpret_cast<u32x4*>(sTb + r * Cfg::LDC + c) = tb[m];
-        }
-#pragma unroll
-        for (int m = 0; m < Cfg::PG; ++m) {
-            const int i = tid + Cfg::NTHR * m;
-            if (i < Cfg::VG) *reinterpret_cast<u32x4*>(sg + 4 * i) = g[m];
-        }
-    }
-};
+// Wave w's tile: column block h = w / NW; token block cb = w mod NW on even h and
+// NW - 1 - (w mod NW) on odd h.  Waves w and w + 4 share a SIMD, so the two
+// column blocks of one SIMD pair token blocks cb and NW - 1 - cb, which evens
+// out the causal work of P and O (it grows with cb).
+template <typename Cfg>
+__device__ __forceinline__ int wave_cb(int w) {
+    const int h = w / Cfg::NW, r = w - h * Cfg::NW;
+    return (h & 1) ? Cfg::NW - 1 - r : r;
+}
 
 template <typename T, int DK, int DV, int C, int DVT>
-__global__ __launch_bounds__(256) void gdn_scan_kernel(
+__global__ __launch_bounds__(512) void gdn_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* S0, SeqGeom geom, int H,
     const float* __restrict__ g_ws, const T* __restrict__ Tb_ws,
     T* __restrict__ O, float* S_T) {   // S_T may alias S0
     using Cfg = ScanCfg<T, DK, DV, C, DVT>;
-    using M = Mfma<T>;
-    using Frag = typename M::frag;
-    constexpr int NW = Cfg::NW, NVB = Cfg::NVB, NDBW = Cfg::NDBW, KS = Cfg::KS;
+    static_assert(Cfg::FITS, "scan workgroup exceeds the LDS of one CU");
+    using St16 = Step<T>;
+    using Frag = typename St16::frag;
+    using KO = K16<T>;
+    using Op = typename KO::op;
+    constexpr int NW = Cfg::NW, NDBW = Cfg::NDBW, KS = Cfg::KS, NP = Cfg::NP;
+    constexpr int ES = Cfg::ES;
     extern __shared__ __align__(16) unsigned char smem[];
-    T* sK0 = reinterpret_cast<T*>(smem + Cfg::OFF_K);
-    T* sV = reinterpret_cast<T*>(smem + Cfg::OFF_V);
-    T* sTb = reinterpret_cast<T*>(smem + Cfg::OFF_TB);
-    T* sSb = reinterpret_cast<T*>(smem + Cfg::OFF_SB);
-    T* sXt = reinterpret_cast<T*>(smem + Cfg::OFF_XT);
-    T* sVpt = reinterpret_cast<T*>(smem + Cfg::OFF_VPT);
-    T* sVdt = reinterpret_cast<T*>(smem + Cfg::OFF_VDT);
-    float* sg = reinterpret_cast<float*>(smem + Cfg::OFF_G);     // [g | exp(g) | exp(g_n - g)]
 
-    const int v0 = blockIdx.x * DVT, h = blockIdx.y, seq = blockIdx.z;
+    // Workgroups are dealt to the 8 XCDs round-robin by linear id; renumber them
+    // so that the DV / DVT column slices of one (sequence, head) share an XCD and
+    // its L2 serves their common K, Q, Tb and gate reads.
+    int v0, h, seq;
+    {
+        constexpr int NS = DV / DVT;
+        const int U = H * (int)gridDim.z;                       // (sequence, head) units
+        const int L = (int)(blockIdx.x + NS * (blockIdx.y + gridDim.y * blockIdx.z));
+        const int lfull = (U / 8) * 8 * NS;
+        int u, vs;
+        if (L < lfull) {
+            const int r = L >> 3;
+            vs = r % NS;
+            u = (L & 7) + 8 * (r / NS);
+        } else {
+            u = (U / 8) * 8 + (L - lfull) / NS;
+            vs = (L - lfull) % NS;
+        }
+        v0 = vs * DVT;
+        h = u % H;
+        seq = u / H;
+    }
     const int l = lane_id(), w = wave_id();
     const int n = l & 15, g4 = 4 * (l >> 4);
-
-    // Each wave runs its own copy of the loop, specialised on its token block
-    // cb (a compile-time constant there), so that no branch on the wave index
-    // remains inside the chunk loop.
-    auto run = [&](auto cb_const) __attribute__((always_inline)) {
-    constexpr int cb = decltype(cb_const)::value;
-
-    // state slice S^T (Dk x DVT): wave w owns d-blocks db = w + NW i, all v-blocks;
-    // lane (g, n) of tile (i, vb) holds S^T[db*16 + 4g + r][vb*16 + n]
-    f32x4 St[NDBW][NVB];
-    const int64_t sbase = ((int64_t)seq * H + h) * DV * DK;
-#pragma unroll
-    for (int i = 0; i < NDBW; ++i) {
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-            const int db = w + NW * i, vv = vb * 16 + n, d = db * 16 + g4;
-            St[i][vb] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (int64_t)(v0 + vv) * DK + d)
-                           : zero4();
-            store4(sSb + vv * Cfg::LDK + d, St[i][vb][0], St[i][vb][1], St[i][vb][2], St[i][vb][3]);
-        }
-    }
+    const int vb = w / NW;                 // this wave's column block (uniform)
 
     // this sequence's tokens [ts, te) and first chunk slot, read once; chunk cc
     // covers tokens ts + cc C .. min(ts + (cc + 1) C, te) - 1 in slot first + cc
@@ -288,79 +403,144 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
         first = seq * geom.chunks_per_seq;
     }
     const int count = (te - ts + C - 1) / C;
-    auto fetch = [&](auto& dst, int cc) __attribute__((always_inline)) {
-        const int t0 = ts + cc * C;
-        dst.load(k, q, v, g_ws, Tb_ws, t0, min(C, te - t0), (int64_t)(first + cc) * H + h, H, h, v0);
-    };
-    using Fetch = ChunkFetch<Cfg, T, DK, DV, C, DVT>;
-    static_assert(Cfg::NPF == 2 || Cfg::NPF == 3, "ring of two or three register sets");
-    Fetch pf0, pf1, pf2;                   // pf2 unused when NPF == 2
-    Frag qcur[Cfg::NQ];                    // Q fragments of the current chunk
-    if (count > 0) {
-        fetch(pf0, 0);
-        pf0.store(sK0, sV, sTb, sg, min(C, te - ts));
-#pragma unroll
-        for (int j = 0; j < Cfg::NQ; ++j) qcur[j] = pf0.q[j];
-        fetch(pf1, min(1, count - 1));
-        if constexpr (Cfg::NPF == 3) {
-            fetch(pf2, min(2, count - 1));
-            fetch(pf0, min(3, count - 1));
-        } else {
-            fetch(pf0, min(2, count - 1));
-        }
-    }
-    __syncthreads();
+    const int64_t sbase = ((int64_t)seq * H + h) * DV * DK;
+    const int64_t rs_k = (int64_t)H * DK * ES, rs_v = (int64_t)H * DV * ES;   // token strides (bytes)
+    T* sS = reinterpret_cast<T*>(smem + Cfg::OFF_SB);     // state copy S[v][d] (input dtype)
+    T* sX = reinterpret_cast<T*>(smem + Cfg::OFF_X);      // X^T of the current chunk
 
-    auto chunk_step = [&](const int cc, Fetch& nxt) __attribute__((always_inline)) {
-        const int t0 = ts + cc * C;
-        const int len = min(C, te - t0);
-        const T* sK = sK0 + (Cfg::KBUF == 2 ? (cc & 1) : 0) * (Cfg::SZ_K / sizeof(T));
-        const float* sgam = sg + C;
-        const float* sdec = sg + 2 * C;
+    // Each wave runs its own copy of the loop, specialised on its token block
+    // cb (a compile-time constant there), so that no branch on it remains
+    // inside the chunk loop.
+    auto run = [&](auto cb_const) __attribute__((always_inline)) {
+        constexpr int cb = decltype(cb_const)::value;
+        // this lane's staging loads: LDS block i = w + NWV j, slot l
+        uint32_t soff[Cfg::NL];
+#pragma unroll
+        for (int j = 0; j < Cfg::NL; ++j) soff[j] = stage_offset<Cfg>(j, w, l, rs_k, rs_v);
+        const uint32_t ooff = (uint32_t)((cb * 16 + n) * rs_v) + (vb * 16 + g4) * ES;
+        const uint32_t qoff = (uint32_t)((cb * 16 + n) * rs_k) + (l >> 4) * 16;
 
-        // ---- phase A: Y = K S^T, Z^T = S Q^T, P^T = K Q^T for token block cb
-        const int cq = cb * 16 + n;        // this lane's token as a column of Z^T, P^T, O^T
-        const bool qok = cq < len;
-        f32x4 Y[NVB], Zt[NVB], Pt[NW];
+        // chunk cd's K, V slice, Tb, gates and Q into registers (rows past the
+        // chunk end fall outside the buffer ranges and read as zeros) ...
+        auto stage_load = [&](u32x4* R, int cd) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const int64_t unit = (int64_t)(first + cd) * H + h;
+            const T* kb = k + ((int64_t)t0 * H + h) * DK;
+            const T* qb = q + ((int64_t)t0 * H + h) * DK;
+            const T* vb_ = v + ((int64_t)t0 * H + h) * DV + v0;
+            const T* tb = Tb_ws + unit * C * C;
+            const float* gb = g_ws + unit * 3 * C;
+            const int nk = (int)((len - 1) * rs_k + DK * ES), nv = (int)((len - 1) * rs_v + DVT * ES);
 #pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) Y[vb] = Zt[vb] = zero4();
-#pragma unroll
-        for (int jb = 0; jb < NW; ++jb) Pt[jb] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < DK; kk += KS) {
-            const Frag aq = qok ? qcur[kk / KS] : Frag{};
-            const Frag ak = kfrag_rows<Cfg>(sK, cb * 16, kk);
-#pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) {
-                const Frag bs = frag_kc(sSb, Cfg::LDK, vb * 16, kk);
-                Y[vb] = M::mma(ak, bs, Y[vb]);
-                Zt[vb] = M::mma(bs, aq, Zt[vb]);
+            for (int j = 0; j < Cfg::NL; ++j) {
+                // the region of batch j is fixed except in the shared V / gates batch
+                const void* base;
+                int nrec;
+                if (j < Cfg::JQ) { base = kb; nrec = nk; }
+                else if (j < Cfg::JT) { base = qb; nrec = nk; }
+                else if (j < Cfg::JV) { base = tb; nrec = C * C * ES; }
+                else {
+                    const int r = stage_region<Cfg>(j, w);
+                    base = r == 3 ? (const void*)vb_ : (const void*)gb;
+                    nrec = r == 3 ? nv : r == 4 ? 3 * C * 4 : 0;
+                }
+                R[j] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, nrec), soff[j], 0, 0);
             }
+        };
+        // this wave's Q fragments of chunk cd, when Q is not staged
+        auto q_in = [&](Frag* dst, int cd) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const __amdgpu_buffer_rsrc_t rq =
+                make_rsrc(q + ((int64_t)t0 * H + h) * DK, (len - 1) * rs_k + DK * ES);
 #pragma unroll
-            for (int jb = 0; jb < NW; ++jb) {
-                if (jb < cb) Pt[jb] = M::mma(kfrag_rows<Cfg>(sK, jb * 16, kk), aq, Pt[jb]);
-                else if (jb == cb) Pt[jb] = M::mma(ak, aq, Pt[jb]);
+            for (int j = 0; j < Cfg::NQ; ++j)
+                dst[j] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + j * 64, 0, 0));
+        };
+        // ... and from there into staging buffer `stage`
+        auto stage_store = [&](const u32x4* R, int stage) __attribute__((always_inline)) {
+            unsigned char* base = smem + stage * Cfg::SZ_STAGE + (w * 64 + l) * 16;
+#pragma unroll
+            for (int j = 0; j < Cfg::NL; ++j) *reinterpret_cast<u32x4*>(base + j * Cfg::NWV * 1024) = R[j];
+        };
+
+        // state slice: this wave owns tiles (d-block db = cb + NW i, column block vb)
+        // of S^T; lane (g, n) of tile i holds S^T[db*16 + 4g + r][vb*16 + n].  Its
+        // copy S[v][d] (input dtype) in LDS feeds the next chunk's K S^T and S Q^T.
+        f32x4 St[NDBW];
+#pragma unroll
+        for (int i = 0; i < NDBW; ++i) {
+            const int db = cb + NW * i, vv = vb * 16 + n, d = db * 16 + g4;
+            St[i] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (int64_t)(v0 + vv) * DK + d) : zero4();
+            store4(sS + vv * Cfg::LDS + d, St[i][0], St[i][1], St[i][2], St[i][3]);
+        }
+
+        // two register sets: the one holding chunk cc + 1 goes to LDS at the end
+        // of step cc; the other receives chunk cc + 2 at its start
+        u32x4 ra[Cfg::NL], rb[Cfg::NL];
+        Frag qa[Cfg::QLDS ? 1 : Cfg::NQ], qb[Cfg::QLDS ? 1 : Cfg::NQ];
+        if (count > 0) {
+            stage_load(ra, 0);
+            stage_load(rb, min(1, count - 1));
+            if constexpr (!Cfg::QLDS) q_in(qa, 0);
+            stage_store(ra, 0);
+        }
+        __syncthreads();
+
+        auto barrier = [&]() __attribute__((always_inline)) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+
+        auto chunk_step = [&](const int cc, u32x4* rload, const u32x4* rnext, const Frag* qcur, Frag* qnxt)
+                              __attribute__((always_inline)) {
+            const int t0 = ts + cc * C;
+            const int len = min(C, te - t0);
+            const int stage = cc & 1;
+            if constexpr (!Cfg::QLDS) q_in(qnxt, min(cc + 1, count - 1));
+            stage_load(rload, min(cc + 2, count - 1));   // past the end: re-read, unused
+
+            const unsigned char* sb = smem + stage * Cfg::SZ_STAGE;
+            const T* sK = reinterpret_cast<const T*>(sb);
+            const T* sV = reinterpret_cast<const T*>(sb + Cfg::OFF_V);
+            const T* sTb = reinterpret_cast<const T*>(sb + Cfg::OFF_T);
+            const float* sg = reinterpret_cast<const float*>(sb + Cfg::OFF_G);
+            const float* sgam = sg + C;
+            const float* sdec = sg + 2 * C;
+            const T* sQ = reinterpret_cast<const T*>(sb + Cfg::OFF_Q);
+
+            // ---- phase A: this wave's tile of Y = K S^T and Z^T = S Q^T, and the
+            // P^T tiles of its token block; X = V - diag(gamma) Y goes to LDS
+            const int cq = cb * 16 + n;    // this lane's token as a column of Z^T, P^T, O^T
+            f32x4 Y = zero4(), Zt = zero4(), Pt[NW];
+#pragma unroll
+            for (int jb = 0; jb < NW; ++jb) Pt[jb] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < DK; kk += KS) {
+                Frag aq;
+                if constexpr (Cfg::QLDS) aq = kfrag_rows<Cfg>(sQ, cb * 16, kk);   // staged Q is laid out as K
+                else aq = qcur[kk / KS];
+                const Frag bs = frag16(sS, Cfg::LDS, vb * 16, kk);
+                Zt = St16::mma(bs, aq, Zt);
+#pragma unroll
+                for (int jb = 0; jb <= cb; ++jb) {
+                    const Frag ak = kfrag_rows<Cfg>(sK, jb * 16, kk);
+                    Pt[jb] = St16::mma(ak, aq, Pt[jb]);
+                    if (jb == cb) Y = St16::mma(ak, bs, Y);
+                }
             }
-        }
-        // X = V - diag(gamma) Y  ->  X^T in LDS (4 consecutive tokens per lane)
-        const float4 gam4 = *reinterpret_cast<const float4*>(sgam + cb * 16 + g4);
+            {
+                const float4 gam4 = *reinterpret_cast<const float4*>(sgam + cb * 16 + g4);
+                const f32x4 vv = vcol4<Cfg>(sV, cb, vb);
+                // lane (g, n): X[cb*16 + 4g + r][vb*16 + n], 4 consecutive tokens of X^T row vb*16 + n
+                store4(sX + xidx<Cfg>(vb * 16 + n, xcol<Cfg>(cb * 16 + g4)), vv[0] - gam4.x * Y[0],
+                       vv[1] - gam4.y * Y[1], vv[2] - gam4.z * Y[2], vv[3] - gam4.w * Y[3]);
+            }
+            // Z^T column scaled by gamma_c; P^T = ((Q K^T) o Gamma o M)^T for block cb
+            const float gq = sg[cq], gamq = sgam[cq];
+            Zt *= gamq;
 #pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-            const int vv = vb * 16 + n, c = cb * 16 + g4;
-            const float x0 = to_f32(sV[(c + 0) * Cfg::LDV + vv]) - gam4.x * Y[vb][0];
-            const float x1 = to_f32(sV[(c + 1) * Cfg::LDV + vv]) - gam4.y * Y[vb][1];
-            const float x2 = to_f32(sV[(c + 2) * Cfg::LDV + vv]) - gam4.z * Y[vb][2];
-            const float x3 = to_f32(sV[(c + 3) * Cfg::LDV + vv]) - gam4.w * Y[vb][3];
-            store4(sXt + vv * Cfg::LDC + c, x0, x1, x2, x3);
-        }
-        // Z^T columns scaled by gamma_c; P = (Q K^T) o Gamma o M, kept as P^T tiles
-        const float gq = sg[cq];
-        const float gamq = sgam[cq];
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) Zt[vb] *= gamq;
-#pragma unroll
-        for (int jb = 0; jb < NW; ++jb) {
-            if (jb <= cb) {
+            for (int jb = 0; jb <= cb; ++jb) {
                 const float4 gj = *reinterpret_cast<const float4*>(sg + jb * 16 + g4);
                 const int j0 = jb * 16 + g4;
                 Pt[jb][0] = j0 + 0 <= cq ? Pt[jb][0] * __expf(gq - gj.x) : 0.f;
@@ -368,105 +548,127 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(
                 Pt[jb][2] = j0 + 2 <= cq ? Pt[jb][2] * __expf(gq - gj.z) : 0.f;
                 Pt[jb][3] = j0 + 3 <= cq ? Pt[jb][3] * __expf(gq - gj.w) : 0.f;
             }
-        }
-        const float gamma_n = sgam[C - 1];
-        __syncthreads();
+            wait_vm_lgkm0<63>();   // the X^T stores are visible after the barrier
+            barrier();
 
-        // ---- phase B: V' = Tb X for token block cb (plain and decayed copies, transposed)
-        {
-            const int kend = ((cb + 1) * 16 + KS - 1) / KS * KS;
-            const float4 dec4 = *reinterpret_cast<const float4*>(sdec + cb * 16 + g4);
+            // ---- phase B: V' = Tb X for every token block of column block vb
+            // (A: Tb rows; B: X^T rows; bf16 keeps both as 16-byte block pairs)
+            f32x4 Vp[NW];
+            {
+                typename St16::frag xb[NP];
+                Op x0[NP], x1[NP];
 #pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) {
-                f32x4 acc = zero4();
-                for (int kk = 0; kk < kend; kk += KS)
-                    acc = M::mma(frag_kc(sTb, Cfg::LDC, cb * 16, kk), frag_kc(sXt, Cfg::LDC, vb * 16, kk), acc);
-                const int vv = vb * 16 + n, c = cb * 16 + g4;
-                store4(sVpt + vv * Cfg::LDC + c, acc[0], acc[1], acc[2], acc[3]);
-                store4(sVdt + vv * Cfg::LDC + c, acc[0] * dec4.x, acc[1] * dec4.y, acc[2] * dec4.z,
-                       acc[3] * dec4.w);
-            }
-        }
-        __syncthreads();
-
-        // ---- phase C: O^T = Z^T + V'^T P^T (token block cb);  S^T update (own d-blocks)
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-            f32x4 acc = Zt[vb];
-#pragma unroll
-            for (int jb = 0; jb < NW; ++jb)
-                if (jb <= cb) acc = RegB<T>::mma(sVpt, Cfg::LDC, vb * 16, jb * 16, Pt[jb], acc);
-            // lane (g, n): O[token cb*16 + n][v0 + vb*16 + 4g .. + 3]
-            if (qok)
-                store4(O + ((int64_t)(t0 + cq) * H + h) * DV + v0 + vb * 16 + g4, acc[0], acc[1], acc[2],
-                       acc[3]);
-        }
-        {
-            Frag bvd[NVB][C / KS];
-#pragma unroll
-            for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-                for (int kk = 0; kk < C; kk += KS) bvd[vb][kk / KS] = frag_kc(sVdt, Cfg::LDC, vb * 16, kk);
-#pragma unroll
-            for (int i = 0; i < NDBW; ++i) {
-                const int db = w + NW * i;
-#pragma unroll
-                for (int vb = 0; vb < NVB; ++vb) St[i][vb] *= gamma_n;
-#pragma unroll
-                for (int kk = 0; kk < C; kk += KS) {
-                    const Frag a = kfrag_cols<Cfg>(sK, kk, db * 16);
-#pragma unroll
-                    for (int vb = 0; vb < NVB; ++vb) St[i][vb] = M::mma(a, bvd[vb][kk / KS], St[i][vb]);
+                for (int p = 0; p < NP; ++p) {
+                    if constexpr (Cfg::BF) {
+                        xb[p] = *reinterpret_cast<const bf16x8*>(sX + xidx<Cfg>(vb * 16 + n, 32 * p + 2 * g4));
+                    } else {
+                        x0[p] = *reinterpret_cast<const f32x4*>(sX + xidx<Cfg>(vb * 16 + n, 32 * p + g4));
+                        if (2 * p + 1 < NW)
+                            x1[p] = *reinterpret_cast<const f32x4*>(sX + xidx<Cfg>(vb * 16 + n, 32 * p + 16 + g4));
+                    }
                 }
 #pragma unroll
-                for (int vb = 0; vb < NVB; ++vb)
-                    store4(sSb + (vb * 16 + n) * Cfg::LDK + db * 16 + g4, St[i][vb][0], St[i][vb][1],
-                           St[i][vb][2], St[i][vb][3]);
-            }
-        }
-        if (cc + 1 < count) {
-            if constexpr (Cfg::KBUF == 1) __syncthreads();   // the update above still reads sK
-            T* sKn = sK0 + (Cfg::KBUF == 2 ? ((cc + 1) & 1) : 0) * (Cfg::SZ_K / sizeof(T));
-            nxt.store(sKn, sV, sTb, sg, min(C, te - (t0 + C)));
+                for (int ib = 0; ib < NW; ++ib) {
+                    const int ar = ib * 16 + n;
+                    f32x4 acc = zero4();
 #pragma unroll
-            for (int j = 0; j < Cfg::NQ; ++j) qcur[j] = nxt.q[j];
-        }
-        // refill this register set (past the end: re-read the last chunk, unused)
-        fetch(nxt, min(cc + 1 + Cfg::NPF, count - 1));
-        __syncthreads();
-    };
+                    for (int p = 0; p < NP; ++p) {
+                        if (2 * p > ib) continue;
+                        if constexpr (Cfg::BF) {
+                            acc = St16::mma(*reinterpret_cast<const bf16x8*>(sTb + tidx<Cfg>(ar, 32 * p + 2 * g4)),
+                                            xb[p], acc);
+                        } else {
+                            const f32x4 a0 = *reinterpret_cast<const f32x4*>(sTb + tidx<Cfg>(ar, 32 * p + g4));
+                            if (2 * p + 1 < NW)
+                                acc = KO::mma2(a0, *reinterpret_cast<const f32x4*>(sTb + tidx<Cfg>(ar, 32 * p + 16 + g4)),
+                                               x0[p], x1[p], acc);
+                            else
+                                acc = KO::mma1(a0, x0[p], acc);
+                        }
+                    }
+                    Vp[ib] = acc;
+                }
+            }
 
-    // chunk c + 1 sits in set (c + 1) % NPF
-    int base = 0;
-    if constexpr (Cfg::NPF == 3) {
-        for (; base + 3 <= count; base += 3) {
-            chunk_step(base, pf1);
-            chunk_step(base + 1, pf2);
-            chunk_step(base + 2, pf0);
-        }
-        if (base < count) chunk_step(base, pf1);
-        if (base + 1 < count) chunk_step(base + 1, pf2);
-    } else {
+            // O^T = Z^T + V'^T P^T for tile (cb, vb) (A: the V' tiles as V'^T; B: the
+            // P^T tiles); lane (g, n) stores O[token cb*16 + n][v0 + vb*16 + 4g .. + 3].
+            // bf16 pairs a last odd block with the (zero) P^T tile of the next one:
+            // every bf16 accumulation chain then stays on one MFMA shape, since a
+            // 16x16x16 MFMA that accumulates onto a 16x16x32 result has been seen
+            // to read a stale accumulator when the compiler keeps it in VGPRs.
+            {
+                const __amdgpu_buffer_rsrc_t ro =
+                    make_rsrc(O + ((int64_t)t0 * H + h) * DV + v0, (len - 1) * rs_v + DVT * ES);
+                f32x4 acc = Zt;
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    if (2 * p > cb) continue;
+                    if (2 * p + 1 <= cb || (Cfg::BF && 2 * p + 1 < NW))
+                        acc = KO::mma2(KO::tile(Vp[2 * p]), KO::tile(Vp[2 * p + 1]), KO::tile(Pt[2 * p]),
+                                       KO::tile(Pt[2 * p + 1]), acc);
+                    else
+                        acc = KO::mma1(KO::tile(Vp[2 * p]), KO::tile(Pt[2 * p]), acc);
+                }
+                if constexpr (Cfg::BF) {
+                    const bf16x4 o4 = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro, ooff, 0, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, ooff, 0, 0);
+                }
+            }
+
+            // S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V' for the own tiles;
+            // the new state's copy replaces the old one (its readers are past the
+            // barrier above)
+            const float gamma_n = sgam[C - 1];
+#pragma unroll
+            for (int jb = 0; jb < NW; ++jb) {
+                const float4 dec4 = *reinterpret_cast<const float4*>(sdec + jb * 16 + g4);
+                Vp[jb][0] *= dec4.x;
+                Vp[jb][1] *= dec4.y;
+                Vp[jb][2] *= dec4.z;
+                Vp[jb][3] *= dec4.w;
+            }
+#pragma unroll
+            for (int i = 0; i < NDBW; ++i) {
+                const int db = cb + NW * i;
+                Op kt[NW];
+#pragma unroll
+                for (int kb = 0; kb < NW; ++kb) kt[kb] = kT16<Cfg>(sK, kb, db * 16);
+                St[i] *= gamma_n;
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    if (2 * p + 1 < NW)
+                        St[i] = KO::mma2(kt[2 * p], kt[2 * p + 1], KO::tile(Vp[2 * p]), KO::tile(Vp[2 * p + 1]), St[i]);
+                    else
+                        St[i] = KO::mma1(kt[2 * p], KO::tile(Vp[2 * p]), St[i]);
+                }
+                store4(sS + (vb * 16 + n) * Cfg::LDS + db * 16 + g4, St[i][0], St[i][1], St[i][2], St[i][3]);
+            }
+
+            // chunk cc + 1 into the other staging buffer (last read in step cc - 1);
+            // the barrier publishes it and the new state copy
+            stage_store(rnext, stage ^ 1);
+            wait_vm_lgkm0<63>();
+            barrier();
+        };
+
+        int base = 0;
         for (; base + 2 <= count; base += 2) {
-            chunk_step(base, pf1);
-            chunk_step(base + 1, pf0);
+            chunk_step(base, ra, rb, qa, qb);
+            chunk_step(base + 1, rb, ra, qb, qa);
         }
-        if (base < count) chunk_step(base, pf1);
-    }
+        if (base < count) chunk_step(base, ra, rb, qa, qb);
 
-
-    if (S_T) {
+        if (S_T) {
 #pragma unroll
-        for (int i = 0; i < NDBW; ++i)
-#pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) {
-                const int db = w + NW * i;
-                *reinterpret_cast<f32x4*>(S_T + sbase + (int64_t)(v0 + vb * 16 + n) * DK + db * 16 + g4) =
-                    St[i][vb];
+            for (int i = 0; i < NDBW; ++i) {
+                const int db = cb + NW * i;
+                *reinterpret_cast<f32x4*>(S_T + sbase + (int64_t)(v0 + vb * 16 + n) * DK + db * 16 + g4) = St[i];
             }
-    }
+        }
     };
-    switch (w) {
+    switch (wave_cb<Cfg>(w)) {
         case 0: run(std::integral_constant<int, 0>{}); break;
         case 1: if constexpr (NW > 1) run(std::integral_constant<int, (NW > 1 ? 1 : 0)>{}); break;
         case 2: if constexpr (NW > 2) run(std::integral_constant<int, (NW > 2 ? 2 : 0)>{}); break;

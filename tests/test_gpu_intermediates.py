@@ -56,6 +56,15 @@ def test_prep_intermediates(dtype, Dk, Dv, C, tol):
     g3 = wsc[off_g:off_g + u * 3 * C * 4].view(torch.float32).view(cps, H, 3, C).double().numpy()
     g_all = g3[:, :, 0]
     Tb_all = wsc[off_t:off_t + u * C * C * es].view(tdt).view(cps, H, C, C).double().numpy()
+    if dtype == "bf16":
+        # bf16 rows store each 32-column group as the 4-column runs of columns
+        # 4g.. and 16+4g.. next to each other (g = 0..3)
+        p = np.arange(C)
+        logical = 32 * (p // 32) + 16 * ((p % 8) // 4) + 4 * ((p % 32) // 8) + p % 4
+        assert sorted(logical) == list(range(C))
+        unperm = np.empty_like(Tb_all)
+        unperm[..., logical] = Tb_all
+        Tb_all = unperm
     for c in range(cps):
         t0, n = c * C, min(C, T - c * C)
         for h in range(H):
