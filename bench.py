@@ -53,6 +53,40 @@ def per_kernel_work(B, T, H, Dk, Dv, C, s_in, n_seqs, has_s0, gated):
     return {"prep": (prep_b, prep_f), "scan": (scan_b, scan_f), "path": (path_b, path_f)}
 
 
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    d = os.path.join(ROOT, "gated_delta_rule_16_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".h", ".hip")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of ``kernel`` from the committed FETCH_SIZE / WRITE_SIZE
+    counter record for ``workload``, each counter scaled by what it read for a
+    plain copy of known size; None when there is no record or the kernel sources
+    changed since it was taken."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{workload.replace('gdn_', '', 1)}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources_sha256") != kernel_sources_sha256() or kernel not in rec.get("kernels", {}):
+        return None
+    cal = rec["copy_calibration"]
+    f_fetch = cal["read_bytes"] / (cal["fetch_kib"] * 1024.0)
+    f_write = cal["write_bytes"] / (cal["write_kib"] * 1024.0)
+    k = rec["kernels"][kernel]
+    return int(k["fetch_kib"] * 1024.0 * f_fetch + k["write_kib"] * 1024.0 * f_write)
+
+
 def roofline(name, bytes_, flops, seconds, dtype):
     t_hbm, t_mma = bytes_ / HBM_PEAK, flops / MFMA_PEAK[dtype]
     if t_hbm >= t_mma:
@@ -103,6 +137,9 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--cpu-sample", type=int, default=16,
                     help="heads per batch row for the oracle baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="after timing, copy an MB-megabyte buffer a few times (a plain copy "
+                         "kernel of known traffic, the scale for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -175,11 +212,23 @@ def main():
                            inp.log_alpha is not None)
     dom = max(("prep", "scan"), key=lambda k_: kmean[k_])
     rl = roofline(dom, *work[dom], kmean[dom] / 1e3, w.dtype)
+    rl["traffic"] = measured_traffic(args.workload, dom)
     rl_path = roofline("path", *work["path"], ms / 1e3, w.dtype)
     kernels = {k_: {"ms": round(kmean[k_], 4),
                     **({"frac": roofline(k_, *work[k_], kmean[k_] / 1e3, w.dtype)["frac"]}
                        if k_ in work and kmean[k_] > 0 else {})}
                for k_ in kms}
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            if flush is not None:
+                flush.zero_()
+            torch.mul(src, 1.0, out=dst)      # an elementwise kernel: reads and writes nbytes
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_sample > 0:

@@ -99,7 +99,8 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
  * workspace, whose required size may then be 0) may be NULL.
  * Errors: GDN_ERR_NULL (q, k, v, beta, O or workspace NULL), GDN_ERR_SHAPE
  * (B, H < 1, T < 0, n_seqs < 1 or B != 1 with cu_seqlens, more than 2^31-1
- * elements in a tensor, q/k/v/O/workspace not 16-byte aligned),
+ * elements in a tensor, C * H * max(Dk, Dv) * element size above 2^31-1 bytes,
+ * q/k/v/O/workspace not 16-byte aligned),
  * GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP. */
 gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
                          const float *log_alpha, const float *beta, const float *S0,
