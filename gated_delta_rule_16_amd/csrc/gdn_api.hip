@@ -78,6 +78,21 @@ Layout make_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int6
     return L;
 }
 
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev >= 64) dev = 63;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // Raises the dynamic LDS limit of one kernel instantiation once (gfx950
 // allows up to 160 KB per workgroup).
 template <auto Kernel>
@@ -141,9 +156,15 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         using P = PrepCfg<T, DK, C>;
         constexpr auto kp = gdn_prep_kernel<T, DK, C>;
         allow_smem<kp>(P::SMEM);
+        // persistent: as many workgroups as fit on the device at once, each
+        // walking units (slot, head) with a stride of the grid
+        const int64_t units = L.slots * a.H;
+        constexpr int per_cu = (int)(160 * 1024 / P::SMEM) < 8 ? (int)(160 * 1024 / P::SMEM) : 8;
+        const int64_t resident = (int64_t)device_cu_count() * per_cu;
+        const unsigned grid = (unsigned)(units < resident ? units : resident);
         tm->mark(a.stream);
-        hipLaunchKernelGGL(kp, dim3((unsigned)L.slots, a.H), dim3(kThreads), P::SMEM, a.stream,
-                           k, a.log_alpha, a.beta, geom, a.H, g_ws, Tb_ws);
+        hipLaunchKernelGGL(kp, dim3(grid), dim3(kThreads), P::SMEM, a.stream,
+                           k, a.log_alpha, a.beta, geom, a.H, (int)units, g_ws, Tb_ws);
         if (gdn_status s = check_launch(a.stream)) return s;
         tm->mark(a.stream);
     }

@@ -86,6 +86,28 @@ __device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, in
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Word 3 of a raw buffer resource: 32-bit untyped data, range-checked against
+// the record count (out-of-range loads return 0, stores are dropped).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a byte offset past every record count
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// XOR swizzles of 16-byte blocks in LDS rows: data block b of row r sits at
+// block b ^ swz(r).  Kinds: 0 none; 1 (K / Q rows of 8+ blocks) 2 (r mod 4) +
+// (r / 4 mod 2); 2 (V rows of 4+ blocks) 2 (r / 2 mod 2); 3 (Tb / X^T rows of 8+
+// blocks) r mod 8.
+template <int KIND>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (KIND == 1) return 2 * (r & 3) + ((r >> 2) & 1);
+    else if constexpr (KIND == 2) return ((r >> 1) & 1) << 1;
+    else if constexpr (KIND == 3) return r & 7;
+    else return 0;
+}
+
+
 // ---------------------------------------------------------------------------
 // Chunk metadata.  A chunk slot is one chunk of one sequence (shared by all
 // heads).  Fixed-length batches compute it; packed batches read a table

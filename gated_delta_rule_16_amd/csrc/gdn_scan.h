@@ -59,15 +59,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Word 3 of a raw buffer resource: 32-bit untyped data, range-checked against
-// the record count (out-of-range loads return 0, stores are dropped).
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr uint32_t kOutOfRange = 0x80000000u;   // a byte offset past every record count
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
 // s_waitcnt with vmcnt <= vm and lgkmcnt = 0 (expcnt not waited on)
 template <int VM>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -154,18 +145,6 @@ __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d)
     } else {
         *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
     }
-}
-
-// One staged region of a chunk: `rows` rows of `blk` 16-byte blocks of data,
-// `pitch` blocks apart in LDS; data block b of row r sits at block b ^ swz(r).
-// Swizzle kinds: 0 none; 1 (K, bf16) 2 (r mod 4) + (r / 4 mod 2); 2 (V, bf16)
-// 2 (r / 2 mod 2); 3 (Tb, bf16) r mod 8.
-template <int KIND>
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (KIND == 1) return 2 * (r & 3) + ((r >> 2) & 1);
-    else if constexpr (KIND == 2) return ((r >> 1) & 1) << 1;
-    else if constexpr (KIND == 3) return r & 7;
-    else return 0;
 }
 
 template <typename T, int DK, int DV, int C, int DVT>
