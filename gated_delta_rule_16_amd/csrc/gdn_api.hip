@@ -14,6 +14,7 @@
 #include "gdn_device.h"
 #include "gdn_prep.h"
 #include "gdn_scan.h"
+#include "gdn_scan_cols.h"
 #include "gdn_step.h"
 
 namespace gdn {
@@ -169,19 +170,48 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         tm->mark(a.stream);
     }
     {
-        // state columns per workgroup: 32 (two column blocks, 8 waves) where the
-        // staged chunk leaves room in LDS, else 16
-        constexpr int DVT = scan_columns<T, DK, DV, C>();
-        using S = ScanCfg<T, DK, DV, C, DVT>;
-        static_assert(S::NTHR <= 512, "scan launch bounds");
-        constexpr auto ks = gdn_scan_kernel<T, DK, DV, C, DVT>;
-        allow_smem<ks>(S::SMEM);
-        tm->mark(a.stream);
-        hipLaunchKernelGGL(ks, dim3(DV / DVT, a.H, (unsigned)L.N), dim3(S::NTHR), S::SMEM,
-                           a.stream, q, k, v, a.S0, geom, a.H, g_ws, Tb_ws,
-                           static_cast<T*>(a.O), a.S_T);
-        if (gdn_status s = check_launch(a.stream)) return s;
-        tm->mark(a.stream);
+        // the column-wave scan where its double-buffered staging fits in LDS,
+        // with 32 state columns per workgroup when that still gives every CU a
+        // workgroup, else 16; the row-block scan otherwise
+        using C32 = ColCfg<T, DK, DV, C, (DV >= 32 ? 32 : 16)>;
+        using C16 = ColCfg<T, DK, DV, C, 16>;
+        constexpr bool fit32 = DV >= 32 && C32::FITS, fit16 = C16::FITS;
+        const int64_t units = (int64_t)a.H * L.N;
+        auto launch_cols = [&](auto cfg_tag) -> gdn_status {
+            using CC = decltype(cfg_tag);
+            if constexpr (CC::FITS) {
+                constexpr int DVT = CC::NVW * 16;
+                constexpr auto ks = gdn_scan_cols_kernel<T, DK, DV, C, DVT>;
+                allow_smem<ks>(CC::SMEM);
+                tm->mark(a.stream);
+                hipLaunchKernelGGL(ks, dim3(DV / DVT, a.H, (unsigned)L.N), dim3(CC::NTHR), CC::SMEM,
+                                   a.stream, q, k, v, a.S0, geom, a.H, g_ws, Tb_ws,
+                                   static_cast<T*>(a.O), a.S_T);
+                if (gdn_status s = check_launch(a.stream)) return s;
+                tm->mark(a.stream);
+                return GDN_OK;
+            } else {
+                return GDN_ERR_INTERNAL;
+            }
+        };
+        if constexpr (fit32 || fit16) {
+            if (fit32 && (!fit16 || units * (DV / 32) >= device_cu_count())) return launch_cols(C32{});
+            return launch_cols(C16{});
+        } else {
+            // state columns per workgroup: 32 (two column blocks, 8 waves) where the
+            // staged chunk leaves room in LDS, else 16
+            constexpr int DVT = scan_columns<T, DK, DV, C>();
+            using S = ScanCfg<T, DK, DV, C, DVT>;
+            static_assert(S::NTHR <= 512, "scan launch bounds");
+            constexpr auto ks = gdn_scan_kernel<T, DK, DV, C, DVT>;
+            allow_smem<ks>(S::SMEM);
+            tm->mark(a.stream);
+            hipLaunchKernelGGL(ks, dim3(DV / DVT, a.H, (unsigned)L.N), dim3(S::NTHR), S::SMEM,
+                               a.stream, q, k, v, a.S0, geom, a.H, g_ws, Tb_ws,
+                               static_cast<T*>(a.O), a.S_T);
+            if (gdn_status s = check_launch(a.stream)) return s;
+            tm->mark(a.stream);
+        }
     }
     return GDN_OK;
 }

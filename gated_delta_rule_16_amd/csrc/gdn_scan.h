@@ -151,9 +151,9 @@ template <typename T, int DK, int DV, int C, int DVT>
 struct ScanCfg {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr int ES = sizeof(T);
-    static constexpr int NW = C / 16;                      // 16-token blocks of a chunk
-    static constexpr int NVB = DVT / 16;                   // 16-column blocks of the state slice
-    static constexpr int NWV = NW * NVB, NTHR = NWV * 64;  // one wave per (token block, column block)
+    static constexpr int NW = C / 16;                      // 16-token blocks = waves of each role
+    static constexpr int NVB = DVT / 16;                   // 16-column blocks of the slice (each wave: all)
+    static constexpr int NTHR = 2 * NW * 64;               // state waves, then output waves
     static constexpr int EV = 16 / ES;                     // elements per 16 bytes
     // Staged regions.  bf16: unpadded rows with XOR swizzles that make every
     // access of the loop conflict-free on 32 banks -- 16-byte row reads of K and
@@ -162,7 +162,7 @@ struct ScanCfg {
     // fp32: rows padded by one block (pitch = 4 words mod 32).
     static constexpr int KB = DK / EV, VB = DVT / EV, TB = C / EV;     // data blocks per row
     static constexpr int KP = BF ? KB : KB + 1, VP = BF ? VB : VB + 1, TP = BF ? TB : TB + 1;
-    static constexpr int KSW = BF ? 1 : 0, VSW = BF ? 2 : 0, TSW = BF ? 3 : 0;
+    static constexpr int KSW = BF ? 1 : 0, VSW = BF && VB >= 4 ? 2 : 0, TSW = BF ? 3 : 0;
     static constexpr int LDK = KP * EV, LDV = VP * EV, LDC = TP * EV;   // pitches (elements)
     static constexpr int LDS = DK + EV;                    // state copy S[v][d]
     // X^T exchange buffer: DVT rows of C tokens (bf16: the token order within
@@ -172,44 +172,42 @@ struct ScanCfg {
     static constexpr int NDB = DK / 16, NDBW = NDB / NW;   // d-blocks of the state per wave
     static constexpr int NP = (NW + 1) / 2;                // pairs of token blocks
     static constexpr int KS = Step<T>::KS, NQ = DK / KS;   // Q fragments per lane
-    static constexpr int NKK = DK / KS;                    // contraction steps over d
-    // staging buffer: regions K | V slice | Tb | gates | Q, each a whole number of
-    // 1 KB blocks; block i is filled by wave i % NWV (64 lanes x 16 bytes)
+    // staging buffer: regions K | Tb | V slice | gates, each a whole number of
+    // 1 KB blocks; block i is filled by output wave i % NW (64 lanes x 16 bytes)
     static constexpr int blocks(int bytes) { return (bytes + 1023) / 1024; }
     static constexpr int NIK = blocks(C * LDK * ES), NIV = blocks(C * LDV * ES);
     static constexpr int NIT = blocks(C * LDC * ES), NIG = blocks(3 * C * 4);
     static constexpr size_t SZ_SB = ((size_t)DVT * LDS * ES + 15) / 16 * 16;
     static constexpr size_t SZ_X = (size_t)DVT * XP * 16;
+    // V' of the chunk in MFMA operand order, handed from the state waves to the
+    // output waves: per (pair of token blocks p, column block vb) and lane, the
+    // lane's 4 values of token block 2p then those of 2p + 1
+    static constexpr size_t SZ_VP = (size_t)NP * NVB * 64 * 8 * ES;
     static constexpr size_t LDS_MAX = 160 * 1024;
-    // Q is staged with the rest (laid out as K) when two staging buffers hold it;
-    // otherwise each wave loads its token block of Q into registers a chunk ahead
-    // Batches: batch j holds LDS blocks j*NWV .. j*NWV + NWV - 1, block j*NWV + w
+    // Batches: batch j holds LDS blocks j*NW .. j*NW + NW - 1, block j*NW + w
     // filled by wave w (one 16-byte load per lane).  Regions start on batch
-    // boundaries, so a batch belongs to one region -- K, Q, Tb -- except the
-    // last, which holds V then the gates when both fit in one batch.
+    // boundaries, so a batch belongs to one region -- K, Tb -- except the last,
+    // which holds V then the gates when both fit in one batch.
     static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
-    static constexpr bool VG1 = NIV + NIG <= NWV;
-    static constexpr int NBK = cdiv(NIK, NWV), NBT = cdiv(NIT, NWV);
-    static constexpr int NBVG = VG1 ? 1 : cdiv(NIV, NWV) + cdiv(NIG, NWV);
-    static constexpr bool QLDS = 2 * (size_t)(2 * NBK + NBT + NBVG) * NWV * 1024 + SZ_SB + SZ_X <= LDS_MAX;
-    static constexpr int NBQ = QLDS ? NBK : 0;
-    static constexpr int NL = NBK + NBQ + NBT + NBVG;      // batches = staging loads per lane per chunk
-    static constexpr int JQ = NBK, JT = JQ + NBQ, JV = JT + NBT;   // first batch of each region
-    static constexpr int JG = VG1 ? JV : JV + cdiv(NIV, NWV);
-    static constexpr int BG0 = VG1 ? JV * NWV + NIV : JG * NWV;  // first block of the gates
-    static constexpr size_t SZ_STAGE = (size_t)NL * NWV * 1024;
-    static constexpr size_t OFF_Q = (size_t)JQ * NWV * 1024, OFF_T = (size_t)JT * NWV * 1024;
-    static constexpr size_t OFF_V = (size_t)JV * NWV * 1024, OFF_G = (size_t)BG0 * 1024;
+    static constexpr bool VG1 = NIV + NIG <= NW;
+    static constexpr int NBK = cdiv(NIK, NW), NBT = cdiv(NIT, NW);
+    static constexpr int NBVG = VG1 ? 1 : cdiv(NIV, NW) + cdiv(NIG, NW);
+    static constexpr int NL = NBK + NBT + NBVG;            // batches = staging loads per lane per chunk
+    static constexpr int JT = NBK, JV = JT + NBT;          // first batch of each region
+    static constexpr int JG = VG1 ? JV : JV + cdiv(NIV, NW);
+    static constexpr int BG0 = VG1 ? JV * NW + NIV : JG * NW;   // first block of the gates
+    static constexpr size_t SZ_STAGE = (size_t)NL * NW * 1024;
+    static constexpr size_t OFF_T = (size_t)JT * NW * 1024;
+    static constexpr size_t OFF_V = (size_t)JV * NW * 1024, OFF_G = (size_t)BG0 * 1024;
     static constexpr int NSTAGE = 2;                       // chunk cc in cc % 2; cc + 1 staged meanwhile
-    static constexpr size_t OFF_SB = NSTAGE * SZ_STAGE, OFF_X = OFF_SB + SZ_SB;
-    static constexpr size_t SMEM = OFF_X + SZ_X;
+    static constexpr size_t OFF_SB = NSTAGE * SZ_STAGE, OFF_X = OFF_SB + SZ_SB, OFF_VP = OFF_X + SZ_X;
+    static constexpr size_t SMEM = OFF_VP + SZ_VP;
     static constexpr bool FITS = SMEM <= LDS_MAX;
     static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVB >= 1 && NVB <= 2, "tile counts");
-    static_assert(NTHR <= 512, "launch bounds");
     static_assert(DV % DVT == 0 && DVT % 16 == 0 && NDB % NW == 0, "tile shapes");
     static_assert(DK % KS == 0 && DK % EV == 0 && DVT % EV == 0 && C % EV == 0, "whole 16-byte steps");
-    static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && VB % 4 == 0 && TB % 8 == 0),
-                  "bf16 swizzles: Tb and X^T in 32-column groups, K / V / Tb rows of 8 / 4 / 8 blocks");
+    static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && (VB % 4 == 0 || VB == 2) && TB % 8 == 0),
+                  "bf16 swizzles: Tb and X^T in 32-column groups, K / V / Tb rows of 8 / 2 or 4k / 8 blocks");
 };
 
 // element (r, c) of a staged region (pitch P blocks, swizzle kind W)
@@ -236,35 +234,33 @@ __device__ __forceinline__ int xcol(int t) {
 
 // Byte offset, relative to the chunk's first row, of the 16 bytes that lane l
 // brings in for LDS block i (slot l of it), or kOutOfRange for padding.
-// rs_k / rs_v: bytes between consecutive tokens of K (and Q) / V.
+// rs_k / rs_v: bytes between consecutive tokens of K / V.
 template <typename Cfg, int P, int B, int W>
 __device__ __forceinline__ int64_t region_offset(int s, int64_t row_bytes) {
     const int r = s / P, p = s - r * P;
     if (r >= Cfg::NW * 16 || p >= B) return -1;
     return r * row_bytes + (int64_t)((p ^ swz<W>(r)) * 16);
 }
-// region of staging batch j for wave w: 0 K, 1 Q, 2 Tb, 3 V, 4 gates, 5 padding
+// region of staging batch j for wave w: 0 K, 2 Tb, 3 V, 4 gates, 5 padding
 template <typename Cfg>
 __device__ __forceinline__ int stage_region(int j, int w) {
-    if (j < Cfg::JQ) return 0;
-    if (j < Cfg::JT) return 1;
+    if (j < Cfg::JT) return 0;
     if (j < Cfg::JV) return 2;
-    const int i = j * Cfg::NWV + w;                      // LDS block
-    if (i < Cfg::JV * Cfg::NWV + Cfg::NIV) return 3;
+    const int i = j * Cfg::NW + w;                       // LDS block
+    if (i < Cfg::JV * Cfg::NW + Cfg::NIV) return 3;
     if (i >= Cfg::BG0 && i < Cfg::BG0 + Cfg::NIG) return 4;
     return 5;
 }
 template <typename Cfg>
 __device__ __forceinline__ uint32_t stage_offset(int j, int w, int l, int64_t rs_k, int64_t rs_v) {
     constexpr int C = Cfg::NW * 16;
-    const int i = j * Cfg::NWV + w;
+    const int i = j * Cfg::NW + w;
     int64_t off = -1;
     switch (stage_region<Cfg>(j, w)) {
         case 0: off = region_offset<Cfg, Cfg::KP, Cfg::KB, Cfg::KSW>(i * 64 + l, rs_k); break;
-        case 1: off = region_offset<Cfg, Cfg::KP, Cfg::KB, Cfg::KSW>((i - Cfg::JQ * Cfg::NWV) * 64 + l, rs_k); break;
-        case 2: off = region_offset<Cfg, Cfg::TP, Cfg::TB, Cfg::TSW>((i - Cfg::JT * Cfg::NWV) * 64 + l,
+        case 2: off = region_offset<Cfg, Cfg::TP, Cfg::TB, Cfg::TSW>((i - Cfg::JT * Cfg::NW) * 64 + l,
                                                                   (int64_t)C * Cfg::ES); break;
-        case 3: off = region_offset<Cfg, Cfg::VP, Cfg::VB, Cfg::VSW>((i - Cfg::JV * Cfg::NWV) * 64 + l, rs_v); break;
+        case 3: off = region_offset<Cfg, Cfg::VP, Cfg::VB, Cfg::VSW>((i - Cfg::JV * Cfg::NW) * 64 + l, rs_v); break;
         case 4: {
             const int s = (i - Cfg::BG0) * 64 + l;
             off = s < 3 * C / 4 ? (int64_t)s * 16 : -1;
@@ -317,16 +313,6 @@ __device__ __forceinline__ f32x4 vcol4(const T* sV, int jb, int vb) {
     }
 }
 
-// Wave w's tile: column block h = w / NW; token block cb = w mod NW on even h and
-// NW - 1 - (w mod NW) on odd h.  Waves w and w + 4 share a SIMD, so the two
-// column blocks of one SIMD pair token blocks cb and NW - 1 - cb, which evens
-// out the causal work of P and O (it grows with cb).
-template <typename Cfg>
-__device__ __forceinline__ int wave_cb(int w) {
-    const int h = w / Cfg::NW, r = w - h * Cfg::NW;
-    return (h & 1) ? Cfg::NW - 1 - r : r;
-}
-
 template <typename T, int DK, int DV, int C, int DVT>
 __global__ __launch_bounds__(512) void gdn_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -339,7 +325,7 @@ __global__ __launch_bounds__(512) void gdn_scan_kernel(
     using Frag = typename St16::frag;
     using KO = K16<T>;
     using Op = typename KO::op;
-    constexpr int NW = Cfg::NW, NDBW = Cfg::NDBW, KS = Cfg::KS, NP = Cfg::NP;
+    constexpr int NW = Cfg::NW, NVB = Cfg::NVB, NDBW = Cfg::NDBW, KS = Cfg::KS, NP = Cfg::NP;
     constexpr int ES = Cfg::ES;
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -367,7 +353,6 @@ __global__ __launch_bounds__(512) void gdn_scan_kernel(
     }
     const int l = lane_id(), w = wave_id();
     const int n = l & 15, g4 = 4 * (l >> 4);
-    const int vb = w / NW;                 // this wave's column block (uniform)
 
     // this sequence's tokens [ts, te) and first chunk slot, read once; chunk cc
     // covers tokens ts + cc C .. min(ts + (cc + 1) C, te) - 1 in slot first + cc
@@ -386,26 +371,204 @@ __global__ __launch_bounds__(512) void gdn_scan_kernel(
     const int64_t rs_k = (int64_t)H * DK * ES, rs_v = (int64_t)H * DV * ES;   // token strides (bytes)
     T* sS = reinterpret_cast<T*>(smem + Cfg::OFF_SB);     // state copy S[v][d] (input dtype)
     T* sX = reinterpret_cast<T*>(smem + Cfg::OFF_X);      // X^T of the current chunk
+    T* sVp = reinterpret_cast<T*>(smem + Cfg::OFF_VP);    // V' of the current chunk
 
-    // Each wave runs its own copy of the loop, specialised on its token block
-    // cb (a compile-time constant there), so that no branch on it remains
-    // inside the chunk loop.
-    auto run = [&](auto cb_const) __attribute__((always_inline)) {
+    auto barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // staged chunk cc: K, Tb, V slice, gates (g, gamma = e^g, gamma_n / gamma)
+    struct Staged {
+        const T *K, *V, *Tb;
+        const float *g, *gam, *dec;
+    };
+    auto staged = [&](int cc) __attribute__((always_inline)) {
+        const unsigned char* sb = smem + (cc & 1) * Cfg::SZ_STAGE;
+        Staged st;
+        st.K = reinterpret_cast<const T*>(sb);
+        st.V = reinterpret_cast<const T*>(sb + Cfg::OFF_V);
+        st.Tb = reinterpret_cast<const T*>(sb + Cfg::OFF_T);
+        st.g = reinterpret_cast<const float*>(sb + Cfg::OFF_G);
+        st.gam = st.g + C;
+        st.dec = st.g + 2 * C;
+        return st;
+    };
+
+    // ---- state waves: the recurrence.  Wave cb owns the tiles (d-block
+    // db = cb + NW i, column block vb) of S^T; lane (g, n) of tile (i, vb) holds
+    // S^T[db*16 + 4g + r][vb*16 + n].  Per chunk: Y = K S^T and X = V - diag(gamma) Y
+    // for token block cb (X^T to LDS); barrier; V' = Tb X for every token block,
+    // V' of block cb to LDS for the output waves, and the state update with the
+    // new state's copy S[v][d] (input dtype) to LDS; barrier.
+    auto run_state = [&](auto cb_const) __attribute__((always_inline)) {
         constexpr int cb = decltype(cb_const)::value;
-        // this lane's staging loads: LDS block i = w + NWV j, slot l
+        f32x4 St[NDBW][NVB];
+#pragma unroll
+        for (int i = 0; i < NDBW; ++i)
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) {
+                const int db = cb + NW * i, vv = vb * 16 + n, d = db * 16 + g4;
+                St[i][vb] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (int64_t)(v0 + vv) * DK + d) : zero4();
+                store4(sS + vv * Cfg::LDS + d, St[i][vb][0], St[i][vb][1], St[i][vb][2], St[i][vb][3]);
+            }
+        __syncthreads();
+
+        auto step = [&](const int cc) __attribute__((always_inline)) {
+            const Staged st = staged(cc);
+            // phase A: Y and X for token block cb
+            f32x4 Y[NVB];
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) Y[vb] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < DK; kk += KS) {
+                const Frag ak = kfrag_rows<Cfg>(st.K, cb * 16, kk);
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) Y[vb] = St16::mma(ak, frag16(sS, Cfg::LDS, vb * 16, kk), Y[vb]);
+            }
+            {
+                const float4 gam4 = *reinterpret_cast<const float4*>(st.gam + cb * 16 + g4);
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    const f32x4 vv = vcol4<Cfg>(st.V, cb, vb);
+                    // lane (g, n): X[cb*16 + 4g + r][vb*16 + n], 4 consecutive tokens of X^T row vb*16 + n
+                    store4(sX + xidx<Cfg>(vb * 16 + n, xcol<Cfg>(cb * 16 + g4)), vv[0] - gam4.x * Y[vb][0],
+                           vv[1] - gam4.y * Y[vb][1], vv[2] - gam4.z * Y[vb][2], vv[3] - gam4.w * Y[vb][3]);
+                }
+            }
+            wait_vm_lgkm0<63>();   // the X^T stores are visible after the barrier
+            barrier();
+
+            // phase B: V' = Tb X for every token block (A: Tb rows, shared by the
+            // column blocks; B: X^T rows; bf16 keeps both as 16-byte block pairs)
+            f32x4 Vp[NVB][NW];
+            {
+                typename St16::frag xb[NVB][NP];
+                Op x0[NVB][NP], x1[NVB][NP];
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        if constexpr (Cfg::BF) {
+                            xb[vb][p] = *reinterpret_cast<const bf16x8*>(sX + xidx<Cfg>(vb * 16 + n, 32 * p + 2 * g4));
+                        } else {
+                            x0[vb][p] = *reinterpret_cast<const f32x4*>(sX + xidx<Cfg>(vb * 16 + n, 32 * p + g4));
+                            if (2 * p + 1 < NW)
+                                x1[vb][p] = *reinterpret_cast<const f32x4*>(sX + xidx<Cfg>(vb * 16 + n, 32 * p + 16 + g4));
+                        }
+                    }
+#pragma unroll
+                for (int ib = 0; ib < NW; ++ib) {
+                    const int ar = ib * 16 + n;
+                    f32x4 acc[NVB];
+#pragma unroll
+                    for (int vb = 0; vb < NVB; ++vb) acc[vb] = zero4();
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        if (2 * p > ib) continue;
+                        if constexpr (Cfg::BF) {
+                            const bf16x8 ta = *reinterpret_cast<const bf16x8*>(st.Tb + tidx<Cfg>(ar, 32 * p + 2 * g4));
+#pragma unroll
+                            for (int vb = 0; vb < NVB; ++vb) acc[vb] = St16::mma(ta, xb[vb][p], acc[vb]);
+                        } else {
+                            const f32x4 a0 = *reinterpret_cast<const f32x4*>(st.Tb + tidx<Cfg>(ar, 32 * p + g4));
+                            if (2 * p + 1 < NW) {
+                                const f32x4 a1 = *reinterpret_cast<const f32x4*>(st.Tb + tidx<Cfg>(ar, 32 * p + 16 + g4));
+#pragma unroll
+                                for (int vb = 0; vb < NVB; ++vb) acc[vb] = KO::mma2(a0, a1, x0[vb][p], x1[vb][p], acc[vb]);
+                            } else {
+#pragma unroll
+                                for (int vb = 0; vb < NVB; ++vb) acc[vb] = KO::mma1(a0, x0[vb][p], acc[vb]);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int vb = 0; vb < NVB; ++vb) Vp[vb][ib] = acc[vb];
+                }
+            }
+            // V' of token block cb, in the operand order of the output waves
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb)
+                store4(sVp + (((cb / 2) * NVB + vb) * 64 + l) * 8 + (cb & 1) * 4, Vp[vb][cb][0], Vp[vb][cb][1],
+                       Vp[vb][cb][2], Vp[vb][cb][3]);
+
+            // S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V' for the own tiles;
+            // the new state's copy replaces the old one (its readers are past the
+            // barrier above)
+            const float gamma_n = st.gam[C - 1];
+#pragma unroll
+            for (int jb = 0; jb < NW; ++jb) {
+                const float4 dec4 = *reinterpret_cast<const float4*>(st.dec + jb * 16 + g4);
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    Vp[vb][jb][0] *= dec4.x;
+                    Vp[vb][jb][1] *= dec4.y;
+                    Vp[vb][jb][2] *= dec4.z;
+                    Vp[vb][jb][3] *= dec4.w;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NDBW; ++i) {
+                const int db = cb + NW * i;
+                Op kt[NW];
+#pragma unroll
+                for (int kb = 0; kb < NW; ++kb) kt[kb] = kT16<Cfg>(st.K, kb, db * 16);
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    f32x4 s = St[i][vb] * gamma_n;
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        if (2 * p + 1 < NW)
+                            s = KO::mma2(kt[2 * p], kt[2 * p + 1], KO::tile(Vp[vb][2 * p]), KO::tile(Vp[vb][2 * p + 1]), s);
+                        else
+                            s = KO::mma1(kt[2 * p], KO::tile(Vp[vb][2 * p]), s);
+                    }
+                    St[i][vb] = s;
+                    store4(sS + (vb * 16 + n) * Cfg::LDS + db * 16 + g4, s[0], s[1], s[2], s[3]);
+                }
+            }
+            wait_vm_lgkm0<63>();   // the state copy and V' are visible after the barrier
+            barrier();
+        };
+        int cc = 0;
+        for (; cc + 2 <= count; cc += 2) {
+            step(cc);
+            step(cc + 1);
+        }
+        if (cc < count) step(cc);
+
+        if (S_T) {
+#pragma unroll
+            for (int i = 0; i < NDBW; ++i)
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    const int db = cb + NW * i;
+                    *reinterpret_cast<f32x4*>(S_T + sbase + (int64_t)(v0 + vb * 16 + n) * DK + db * 16 + g4) = St[i][vb];
+                }
+        }
+    };
+
+    // ---- output waves: staging and the outputs, one chunk behind the state
+    // waves.  Wave cb stages its share of each chunk, computes Z^T = S Q^T
+    // (scaled by gamma) and P^T = ((Q K^T) o Gamma o M)^T for query block cb of
+    // chunk cc, and, in the next step, O^T = Z^T + V'^T P^T from the V' the
+    // state waves left in LDS.
+    auto run_out = [&](auto cb_const) __attribute__((always_inline)) {
+        constexpr int cb = decltype(cb_const)::value;
+        const int wf = cb;   // filler index of this wave
+        // this lane's staging loads: LDS block i = wf + NW j, slot l
         uint32_t soff[Cfg::NL];
 #pragma unroll
-        for (int j = 0; j < Cfg::NL; ++j) soff[j] = stage_offset<Cfg>(j, w, l, rs_k, rs_v);
-        const uint32_t ooff = (uint32_t)((cb * 16 + n) * rs_v) + (vb * 16 + g4) * ES;
+        for (int j = 0; j < Cfg::NL; ++j) soff[j] = stage_offset<Cfg>(j, wf, l, rs_k, rs_v);
+        const uint32_t ooff = (uint32_t)((cb * 16 + n) * rs_v) + g4 * ES;
         const uint32_t qoff = (uint32_t)((cb * 16 + n) * rs_k) + (l >> 4) * 16;
 
-        // chunk cd's K, V slice, Tb, gates and Q into registers (rows past the
+        // chunk cd's K, Tb, V slice and gates into registers (rows past the
         // chunk end fall outside the buffer ranges and read as zeros) ...
         auto stage_load = [&](u32x4* R, int cd) __attribute__((always_inline)) {
             const int t0 = ts + cd * C, len = min(C, te - t0);
             const int64_t unit = (int64_t)(first + cd) * H + h;
             const T* kb = k + ((int64_t)t0 * H + h) * DK;
-            const T* qb = q + ((int64_t)t0 * H + h) * DK;
             const T* vb_ = v + ((int64_t)t0 * H + h) * DV + v0;
             const T* tb = Tb_ws + unit * C * C;
             const float* gb = g_ws + unit * 3 * C;
@@ -415,18 +578,23 @@ __global__ __launch_bounds__(512) void gdn_scan_kernel(
                 // the region of batch j is fixed except in the shared V / gates batch
                 const void* base;
                 int nrec;
-                if (j < Cfg::JQ) { base = kb; nrec = nk; }
-                else if (j < Cfg::JT) { base = qb; nrec = nk; }
+                if (j < Cfg::JT) { base = kb; nrec = nk; }
                 else if (j < Cfg::JV) { base = tb; nrec = C * C * ES; }
                 else {
-                    const int r = stage_region<Cfg>(j, w);
+                    const int r = stage_region<Cfg>(j, wf);
                     base = r == 3 ? (const void*)vb_ : (const void*)gb;
                     nrec = r == 3 ? nv : r == 4 ? 3 * C * 4 : 0;
                 }
                 R[j] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, nrec), soff[j], 0, 0);
             }
         };
-        // this wave's Q fragments of chunk cd, when Q is not staged
+        // ... and from there into the staging buffer of chunk cd
+        auto stage_store = [&](const u32x4* R, int cd) __attribute__((always_inline)) {
+            unsigned char* base = smem + (cd & 1) * Cfg::SZ_STAGE + (wf * 64 + l) * 16;
+#pragma unroll
+            for (int j = 0; j < Cfg::NL; ++j) *reinterpret_cast<u32x4*>(base + j * Cfg::NW * 1024) = R[j];
+        };
+        // this wave's Q fragments of chunk cd (token block cb)
         auto q_in = [&](Frag* dst, int cd) __attribute__((always_inline)) {
             const int t0 = ts + cd * C, len = min(C, te - t0);
             const __amdgpu_buffer_rsrc_t rq =
@@ -435,223 +603,130 @@ __global__ __launch_bounds__(512) void gdn_scan_kernel(
             for (int j = 0; j < Cfg::NQ; ++j)
                 dst[j] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + j * 64, 0, 0));
         };
-        // ... and from there into staging buffer `stage`
-        auto stage_store = [&](const u32x4* R, int stage) __attribute__((always_inline)) {
-            unsigned char* base = smem + stage * Cfg::SZ_STAGE + (w * 64 + l) * 16;
-#pragma unroll
-            for (int j = 0; j < Cfg::NL; ++j) *reinterpret_cast<u32x4*>(base + j * Cfg::NWV * 1024) = R[j];
-        };
 
-        // state slice: this wave owns tiles (d-block db = cb + NW i, column block vb)
-        // of S^T; lane (g, n) of tile i holds S^T[db*16 + 4g + r][vb*16 + n].  Its
-        // copy S[v][d] (input dtype) in LDS feeds the next chunk's K S^T and S Q^T.
-        f32x4 St[NDBW];
-#pragma unroll
-        for (int i = 0; i < NDBW; ++i) {
-            const int db = cb + NW * i, vv = vb * 16 + n, d = db * 16 + g4;
-            St[i] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (int64_t)(v0 + vv) * DK + d) : zero4();
-            store4(sS + vv * Cfg::LDS + d, St[i][0], St[i][1], St[i][2], St[i][3]);
-        }
-
-        // two register sets: the one holding chunk cc + 1 goes to LDS at the end
-        // of step cc; the other receives chunk cc + 2 at its start
+        // two register sets take turns: step cc writes the one holding chunk
+        // cc + 1 to LDS as it starts and refills it with chunk cc + 3; Q is read
+        // straight into registers, two chunks ahead
         u32x4 ra[Cfg::NL], rb[Cfg::NL];
-        Frag qa[Cfg::QLDS ? 1 : Cfg::NQ], qb[Cfg::QLDS ? 1 : Cfg::NQ];
+        Frag qa[Cfg::NQ], qb[Cfg::NQ];
         if (count > 0) {
             stage_load(ra, 0);
             stage_load(rb, min(1, count - 1));
-            if constexpr (!Cfg::QLDS) q_in(qa, 0);
+            q_in(qa, 0);
+            q_in(qb, min(1, count - 1));
             stage_store(ra, 0);
+            stage_load(ra, min(2, count - 1));
         }
         __syncthreads();
 
-        auto barrier = [&]() __attribute__((always_inline)) {
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
+        // Z^T (scaled) and P^T of the previous chunk, consumed by its output
+        f32x4 Zt[NVB], Pt[NW];
+        // O^T = Z^T + V'^T P^T for tiles (cb, vb) of chunk cd (A: the V' tiles as
+        // V'^T, from LDS; B: the P^T tiles); lane (g, n) stores
+        // O[token cb*16 + n][v0 + vb*16 + 4g .. + 3].  bf16 pairs a last odd block
+        // with the (zero) P^T tile of the next one: every bf16 accumulation chain
+        // then stays on one MFMA shape, since a 16x16x16 MFMA that accumulates
+        // onto a 16x16x32 result has been seen to read a stale accumulator when
+        // the compiler keeps it in VGPRs.
+        auto output = [&](int cd) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(O + ((int64_t)t0 * H + h) * DV + v0, (len - 1) * rs_v + DVT * ES);
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) {
+                f32x4 acc = Zt[vb];
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    if (2 * p > cb) continue;
+                    const T* src = sVp + ((p * NVB + vb) * 64 + l) * 8;
+                    if constexpr (Cfg::BF) {
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(src);
+                        acc = KO::mma2p(a, KO::tile(Pt[2 * p]), KO::tile(Pt[2 * p + 1]), acc);
+                    } else {
+                        const f32x4 a0 = *reinterpret_cast<const f32x4*>(src);
+                        if (2 * p + 1 <= cb)
+                            acc = KO::mma2(a0, *reinterpret_cast<const f32x4*>(src + 4), Pt[2 * p], Pt[2 * p + 1], acc);
+                        else
+                            acc = KO::mma1(a0, Pt[2 * p], acc);
+                    }
+                }
+                if constexpr (Cfg::BF) {
+                    const bf16x4 o4 = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro, ooff + vb * 16 * ES, 0, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, ooff + vb * 16 * ES, 0, 0);
+                }
+            }
         };
 
-        auto chunk_step = [&](const int cc, u32x4* rload, const u32x4* rnext, const Frag* qcur, Frag* qnxt)
-                              __attribute__((always_inline)) {
-            const int t0 = ts + cc * C;
-            const int len = min(C, te - t0);
-            const int stage = cc & 1;
-            if constexpr (!Cfg::QLDS) q_in(qnxt, min(cc + 1, count - 1));
-            stage_load(rload, min(cc + 2, count - 1));   // past the end: re-read, unused
+        auto step = [&](const int cc, u32x4* rnext, Frag* qcur) __attribute__((always_inline)) {
+            // chunk cc + 1 into the other staging buffer (its last readers are
+            // past the previous barrier); the next barrier publishes it
+            stage_store(rnext, cc + 1);
+            stage_load(rnext, min(cc + 3, count - 1));   // past the end: re-read, unused
+            const Staged st = staged(cc);
 
-            const unsigned char* sb = smem + stage * Cfg::SZ_STAGE;
-            const T* sK = reinterpret_cast<const T*>(sb);
-            const T* sV = reinterpret_cast<const T*>(sb + Cfg::OFF_V);
-            const T* sTb = reinterpret_cast<const T*>(sb + Cfg::OFF_T);
-            const float* sg = reinterpret_cast<const float*>(sb + Cfg::OFF_G);
-            const float* sgam = sg + C;
-            const float* sdec = sg + 2 * C;
-            const T* sQ = reinterpret_cast<const T*>(sb + Cfg::OFF_Q);
+            // phase A: the previous chunk's output (its V' was published by the
+            // last barrier), then Z^T = S Q^T of this chunk while S is in LDS
+            if (cc > 0) output(cc - 1);
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) Zt[vb] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < DK; kk += KS)
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb)
+                    Zt[vb] = St16::mma(frag16(sS, Cfg::LDS, vb * 16, kk), qcur[kk / KS], Zt[vb]);
+            wait_vm_lgkm0<63>();   // the staged chunk is visible after the barrier
+            barrier();
 
-            // ---- phase A: this wave's tile of Y = K S^T and Z^T = S Q^T, and the
-            // P^T tiles of its token block; X = V - diag(gamma) Y goes to LDS
-            const int cq = cb * 16 + n;    // this lane's token as a column of Z^T, P^T, O^T
-            f32x4 Y = zero4(), Zt = zero4(), Pt[NW];
+            // phase B: P^T tiles of query block cb (rows: key tokens), decayed
+            // and masked; Z^T columns scaled by gamma
 #pragma unroll
             for (int jb = 0; jb < NW; ++jb) Pt[jb] = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DK; kk += KS) {
-                Frag aq;
-                if constexpr (Cfg::QLDS) aq = kfrag_rows<Cfg>(sQ, cb * 16, kk);   // staged Q is laid out as K
-                else aq = qcur[kk / KS];
-                const Frag bs = frag16(sS, Cfg::LDS, vb * 16, kk);
-                Zt = St16::mma(bs, aq, Zt);
+            for (int kk = 0; kk < DK; kk += KS)
 #pragma unroll
-                for (int jb = 0; jb <= cb; ++jb) {
-                    const Frag ak = kfrag_rows<Cfg>(sK, jb * 16, kk);
-                    Pt[jb] = St16::mma(ak, aq, Pt[jb]);
-                    if (jb == cb) Y = St16::mma(ak, bs, Y);
-                }
-            }
-            {
-                const float4 gam4 = *reinterpret_cast<const float4*>(sgam + cb * 16 + g4);
-                const f32x4 vv = vcol4<Cfg>(sV, cb, vb);
-                // lane (g, n): X[cb*16 + 4g + r][vb*16 + n], 4 consecutive tokens of X^T row vb*16 + n
-                store4(sX + xidx<Cfg>(vb * 16 + n, xcol<Cfg>(cb * 16 + g4)), vv[0] - gam4.x * Y[0],
-                       vv[1] - gam4.y * Y[1], vv[2] - gam4.z * Y[2], vv[3] - gam4.w * Y[3]);
-            }
-            // Z^T column scaled by gamma_c; P^T = ((Q K^T) o Gamma o M)^T for block cb
-            const float gq = sg[cq], gamq = sgam[cq];
-            Zt *= gamq;
+                for (int jb = 0; jb <= cb; ++jb)
+                    Pt[jb] = St16::mma(kfrag_rows<Cfg>(st.K, jb * 16, kk), qcur[kk / KS], Pt[jb]);
+            q_in(qcur, min(cc + 2, count - 1));   // this chunk's Q is consumed
+            const int cq = cb * 16 + n;
+            const float gq = st.g[cq], gamq = st.gam[cq];
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb) Zt[vb] *= gamq;
 #pragma unroll
             for (int jb = 0; jb <= cb; ++jb) {
-                const float4 gj = *reinterpret_cast<const float4*>(sg + jb * 16 + g4);
+                const float4 gj = *reinterpret_cast<const float4*>(st.g + jb * 16 + g4);
                 const int j0 = jb * 16 + g4;
                 Pt[jb][0] = j0 + 0 <= cq ? Pt[jb][0] * __expf(gq - gj.x) : 0.f;
                 Pt[jb][1] = j0 + 1 <= cq ? Pt[jb][1] * __expf(gq - gj.y) : 0.f;
                 Pt[jb][2] = j0 + 2 <= cq ? Pt[jb][2] * __expf(gq - gj.z) : 0.f;
                 Pt[jb][3] = j0 + 3 <= cq ? Pt[jb][3] * __expf(gq - gj.w) : 0.f;
             }
-            wait_vm_lgkm0<63>();   // the X^T stores are visible after the barrier
-            barrier();
-
-            // ---- phase B: V' = Tb X for every token block of column block vb
-            // (A: Tb rows; B: X^T rows; bf16 keeps both as 16-byte block pairs)
-            f32x4 Vp[NW];
-            {
-                typename St16::frag xb[NP];
-                Op x0[NP], x1[NP];
-#pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    if constexpr (Cfg::BF) {
-                        xb[p] = *reinterpret_cast<const bf16x8*>(sX + xidx<Cfg>(vb * 16 + n, 32 * p + 2 * g4));
-                    } else {
-                        x0[p] = *reinterpret_cast<const f32x4*>(sX + xidx<Cfg>(vb * 16 + n, 32 * p + g4));
-                        if (2 * p + 1 < NW)
-                            x1[p] = *reinterpret_cast<const f32x4*>(sX + xidx<Cfg>(vb * 16 + n, 32 * p + 16 + g4));
-                    }
-                }
-#pragma unroll
-                for (int ib = 0; ib < NW; ++ib) {
-                    const int ar = ib * 16 + n;
-                    f32x4 acc = zero4();
-#pragma unroll
-                    for (int p = 0; p < NP; ++p) {
-                        if (2 * p > ib) continue;
-                        if constexpr (Cfg::BF) {
-                            acc = St16::mma(*reinterpret_cast<const bf16x8*>(sTb + tidx<Cfg>(ar, 32 * p + 2 * g4)),
-                                            xb[p], acc);
-                        } else {
-                            const f32x4 a0 = *reinterpret_cast<const f32x4*>(sTb + tidx<Cfg>(ar, 32 * p + g4));
-                            if (2 * p + 1 < NW)
-                                acc = KO::mma2(a0, *reinterpret_cast<const f32x4*>(sTb + tidx<Cfg>(ar, 32 * p + 16 + g4)),
-                                               x0[p], x1[p], acc);
-                            else
-                                acc = KO::mma1(a0, x0[p], acc);
-                        }
-                    }
-                    Vp[ib] = acc;
-                }
-            }
-
-            // O^T = Z^T + V'^T P^T for tile (cb, vb) (A: the V' tiles as V'^T; B: the
-            // P^T tiles); lane (g, n) stores O[token cb*16 + n][v0 + vb*16 + 4g .. + 3].
-            // bf16 pairs a last odd block with the (zero) P^T tile of the next one:
-            // every bf16 accumulation chain then stays on one MFMA shape, since a
-            // 16x16x16 MFMA that accumulates onto a 16x16x32 result has been seen
-            // to read a stale accumulator when the compiler keeps it in VGPRs.
-            {
-                const __amdgpu_buffer_rsrc_t ro =
-                    make_rsrc(O + ((int64_t)t0 * H + h) * DV + v0, (len - 1) * rs_v + DVT * ES);
-                f32x4 acc = Zt;
-#pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    if (2 * p > cb) continue;
-                    if (2 * p + 1 <= cb || (Cfg::BF && 2 * p + 1 < NW))
-                        acc = KO::mma2(KO::tile(Vp[2 * p]), KO::tile(Vp[2 * p + 1]), KO::tile(Pt[2 * p]),
-                                       KO::tile(Pt[2 * p + 1]), acc);
-                    else
-                        acc = KO::mma1(KO::tile(Vp[2 * p]), KO::tile(Pt[2 * p]), acc);
-                }
-                if constexpr (Cfg::BF) {
-                    const bf16x4 o4 = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro, ooff, 0, 0);
-                } else {
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, ooff, 0, 0);
-                }
-            }
-
-            // S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V' for the own tiles;
-            // the new state's copy replaces the old one (its readers are past the
-            // barrier above)
-            const float gamma_n = sgam[C - 1];
-#pragma unroll
-            for (int jb = 0; jb < NW; ++jb) {
-                const float4 dec4 = *reinterpret_cast<const float4*>(sdec + jb * 16 + g4);
-                Vp[jb][0] *= dec4.x;
-                Vp[jb][1] *= dec4.y;
-                Vp[jb][2] *= dec4.z;
-                Vp[jb][3] *= dec4.w;
-            }
-#pragma unroll
-            for (int i = 0; i < NDBW; ++i) {
-                const int db = cb + NW * i;
-                Op kt[NW];
-#pragma unroll
-                for (int kb = 0; kb < NW; ++kb) kt[kb] = kT16<Cfg>(sK, kb, db * 16);
-                St[i] *= gamma_n;
-#pragma unroll
-                for (int p = 0; p < NP; ++p) {
-                    if (2 * p + 1 < NW)
-                        St[i] = KO::mma2(kt[2 * p], kt[2 * p + 1], KO::tile(Vp[2 * p]), KO::tile(Vp[2 * p + 1]), St[i]);
-                    else
-                        St[i] = KO::mma1(kt[2 * p], KO::tile(Vp[2 * p]), St[i]);
-                }
-                store4(sS + (vb * 16 + n) * Cfg::LDS + db * 16 + g4, St[i][0], St[i][1], St[i][2], St[i][3]);
-            }
-
-            // chunk cc + 1 into the other staging buffer (last read in step cc - 1);
-            // the barrier publishes it and the new state copy
-            stage_store(rnext, stage ^ 1);
-            wait_vm_lgkm0<63>();
+            wait_vm_lgkm0<63>();   // all reads of this chunk's staging buffer are done
             barrier();
         };
-
-        int base = 0;
-        for (; base + 2 <= count; base += 2) {
-            chunk_step(base, ra, rb, qa, qb);
-            chunk_step(base + 1, rb, ra, qb, qa);
+        int cc = 0;
+        for (; cc + 2 <= count; cc += 2) {
+            step(cc, rb, qa);
+            step(cc + 1, ra, qb);
         }
-        if (base < count) chunk_step(base, ra, rb, qa, qb);
-
-        if (S_T) {
-#pragma unroll
-            for (int i = 0; i < NDBW; ++i) {
-                const int db = cb + NW * i;
-                *reinterpret_cast<f32x4*>(S_T + sbase + (int64_t)(v0 + vb * 16 + n) * DK + db * 16 + g4) = St[i];
-            }
-        }
+        if (cc < count) step(cc, rb, qa);
+        if (count > 0) output(count - 1);   // its V' was published by the last barrier
     };
-    switch (wave_cb<Cfg>(w)) {
-        case 0: run(std::integral_constant<int, 0>{}); break;
-        case 1: if constexpr (NW > 1) run(std::integral_constant<int, (NW > 1 ? 1 : 0)>{}); break;
-        case 2: if constexpr (NW > 2) run(std::integral_constant<int, (NW > 2 ? 2 : 0)>{}); break;
-        default: if constexpr (NW > 3) run(std::integral_constant<int, (NW > 3 ? 3 : 0)>{}); break;
+
+    switch (w) {
+        case 0: run_state(std::integral_constant<int, 0>{}); break;
+        case 1: if constexpr (NW > 1) run_state(std::integral_constant<int, (NW > 1 ? 1 : 0)>{}); break;
+        case 2: if constexpr (NW > 2) run_state(std::integral_constant<int, (NW > 2 ? 2 : 0)>{}); break;
+        case 3: if constexpr (NW > 3) run_state(std::integral_constant<int, (NW > 3 ? 3 : 0)>{}); break;
+        default: break;
+    }
+    switch (w - NW) {
+        case 0: run_out(std::integral_constant<int, 0>{}); break;
+        case 1: if constexpr (NW > 1) run_out(std::integral_constant<int, (NW > 1 ? 1 : 0)>{}); break;
+        case 2: if constexpr (NW > 2) run_out(std::integral_constant<int, (NW > 2 ? 2 : 0)>{}); break;
+        case 3: if constexpr (NW > 3) run_out(std::integral_constant<int, (NW > 3 ? 3 : 0)>{}); break;
+        default: break;
     }
 }
 

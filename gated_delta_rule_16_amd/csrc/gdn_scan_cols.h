@@ -1,0 +1,585 @@
+// gdn_scan_cols.h -- serial inter-chunk state scan with the chunk outputs fused
+// in, one wave per 16 state columns.
+//
+// Same arithmetic as gdn_scan.h (row form, per chunk, S = state at the chunk
+// start, Dv x Dk; gamma_i = exp(g_i); Tb = T diag(beta) from the prep kernel):
+//   Y  = K S^T,   X = V - diag(gamma) Y,   V' = Tb X
+//   O^T = Z^T diag(gamma) + V'^T P^T,  Z^T = S Q^T, P = (Q K^T) o Gamma o M
+//   S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V'
+// (Qiita, the Linear Attention lineage, section "Gated-DeltaNet" and "Chunk
+// Computation"; LinearAttention系列解读(六), sections 4.4 and 4.5).
+//
+// Work split.  A workgroup owns a DVT-column slice of one (sequence, head):
+//  - column waves (DVT / 16): wave vb holds all Dk rows of columns vb*16 ..
+//    vb*16 + 15 of S^T in MFMA accumulators, so that Y, X, V', the state update
+//    and the output of its columns never leave the wave -- the recurrence has no
+//    synchronisation inside a chunk;
+//  - four helper waves stage the next chunks (K, Q, Tb, the V slice, gates)
+//    through registers into a double-buffered LDS area, and the first two of
+//    them compute P for the chunk (query blocks split between them) and leave
+//    its decayed, masked tiles in LDS.
+// With waves dealt to the four SIMDs in turn, the column waves and the P
+// helpers get a SIMD each and the staging-only helpers share the column
+// waves' SIMDs.
+// One barrier per chunk.  A column wave forms the output of chunk cc - 1 during
+// step cc, when the helpers' P^T tiles of that chunk are published.
+//
+// State tile layout.  Column wave vb keeps Dk / 16 tiles; lane (g, n) of tile i
+// holds S^T[drow(i, 4g + r)][vb*16 + n], r = 0..3.  bf16: tile 2m + h covers
+// d = 32m + 8a + 4h + r for its rows 4a + r, so that the lane values of tiles
+// 2m and 2m + 1 concatenate to d = 32m + 8g .. 32m + 8g + 7, the order of a
+// 16-byte row fragment of K or Q; one 16x16x32 MFMA then contracts 32 d.
+// fp32: tile i covers d = 16 i + rho (four 16x16x4 MFMAs per tile).
+#pragma once
+
+#include "gdn_scan.h"
+
+namespace gdn {
+
+template <typename T, int DK, int DV, int C, int DVT>
+struct ColCfg {
+    static constexpr bool BF = sizeof(T) == 2;
+    static constexpr int ES = sizeof(T);
+    static constexpr int NW = C / 16;                      // 16-token blocks of a chunk
+    static constexpr int NVW = DVT / 16;                   // column waves
+    static constexpr int NPW = 4;                          // helper waves: all stage,
+    static constexpr int NPP = 2;                          // the first NPP also form P
+    static constexpr int NWG = NVW + NPW, NTHR = NWG * 64;
+    static constexpr int NF = NPW;                         // staging waves: the helpers
+    static constexpr int EV = 16 / ES;                     // elements per 16 bytes
+    // staged rows: bf16 unpadded with XOR swizzles (K and Q: kind 1; V: kind 2
+    // for rows of 4+ blocks; Tb: kind 3), fp32 padded by one block
+    static constexpr int KB = DK / EV, VB = DVT / EV, TB = C / EV;
+    static constexpr int KP = BF ? KB : KB + 1, VP = BF ? VB : VB + 1, TP = BF ? TB : TB + 1;
+    static constexpr int KSW = BF ? 1 : 0, VSW = BF && VB >= 4 ? 2 : 0, TSW = BF ? 3 : 0;
+    static constexpr int LDK = KP * EV, LDV = VP * EV, LDC = TP * EV;
+    static constexpr int NDB = DK / 16;                    // state tiles per column wave
+    static constexpr int NP = (NW + 1) / 2;                // pairs of token blocks
+    static constexpr int KS = Step<T>::KS, NKK = DK / KS;  // contraction steps over d
+    // staging buffer: regions K | Q | Tb | V slice | gates, whole 1 KB blocks;
+    // batch j holds blocks j*NF .. j*NF + NF - 1, block j*NF + f filled by
+    // helper wave f (one 16-byte load per lane); regions start on batch
+    // boundaries except the gates, which follow V in its last batch when they fit
+    static constexpr int blocks(int bytes) { return (bytes + 1023) / 1024; }
+    static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+    static constexpr int NIK = blocks(C * LDK * ES), NIV = blocks(C * LDV * ES);
+    static constexpr int NIT = blocks(C * LDC * ES), NIG = blocks(3 * C * 4);
+    static constexpr bool VG1 = NIV + NIG <= NF;
+    static constexpr int NBK = cdiv(NIK, NF), NBT = cdiv(NIT, NF);
+    static constexpr int NBVG = VG1 ? 1 : cdiv(NIV, NF) + cdiv(NIG, NF);
+    static constexpr int NL = 2 * NBK + NBT + NBVG;        // staging loads per lane per chunk
+    static constexpr int JQ = NBK, JT = 2 * NBK, JV = JT + NBT;
+    static constexpr int JG = VG1 ? JV : JV + cdiv(NIV, NF);
+    static constexpr int BG0 = VG1 ? JV * NF + NIV : JG * NF;
+    static constexpr size_t SZ_STAGE = (size_t)NL * NF * 1024;
+    static constexpr size_t OFF_Q = (size_t)JQ * NF * 1024, OFF_T = (size_t)JT * NF * 1024;
+    static constexpr size_t OFF_V = (size_t)JV * NF * 1024, OFF_G = (size_t)BG0 * 1024;
+    // P^T tiles of a chunk in MFMA operand order: 1 KB slots of 16 bytes per
+    // lane; bf16 one slot per pair of key blocks (the lane's 4 values of block
+    // 2p, then those of 2p + 1), fp32 one per key block; query block qb starts
+    // at slot prow(qb); two buffers (chunk parity)
+    static constexpr int prow(int qb) {
+        int s = 0;
+        for (int c = 0; c < qb; ++c) s += BF ? c / 2 + 1 : c + 1;
+        return s;
+    }
+    static constexpr size_t SZ_P = (size_t)prow(NW) * 1024;
+    static constexpr size_t OFF_P = 2 * SZ_STAGE;
+    static constexpr size_t SMEM = OFF_P + 2 * SZ_P;
+    static constexpr bool FITS = SMEM <= 160 * 1024;
+    // P helper of query block qb: 0 takes blocks 0 and NW - 1, 1 the middle ones
+    static constexpr int pwave(int qb) { return (qb < NW - 1 - qb ? qb : NW - 1 - qb) % NPP; }
+    static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && NVW <= 2, "tile counts");
+    static_assert(DV % DVT == 0 && DVT % 16 == 0 && DK % KS == 0 && DK % 16 == 0, "tile shapes");
+    static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && (VB % 4 == 0 || VB == 2) && TB % 8 == 0 && DK % 32 == 0),
+                  "bf16 swizzles and tile pairs");
+};
+
+// logical d of row rho of state tile i
+template <typename Cfg>
+__device__ __forceinline__ constexpr int drow(int i, int rho) {
+    if constexpr (Cfg::BF) return 32 * (i / 2) + 8 * (rho / 4) + 4 * (i % 2) + rho % 4;
+    else return 16 * i + rho;
+}
+
+// region of staging batch j for helper wave f: 0 K, 1 Q, 2 Tb, 3 V, 4 gates, 5 padding
+template <typename Cfg>
+__device__ __forceinline__ int col_region(int j, int f) {
+    if (j < Cfg::JQ) return 0;
+    if (j < Cfg::JT) return 1;
+    if (j < Cfg::JV) return 2;
+    const int i = j * Cfg::NF + f;
+    if (i < Cfg::JV * Cfg::NF + Cfg::NIV) return 3;
+    if (i >= Cfg::BG0 && i < Cfg::BG0 + Cfg::NIG) return 4;
+    return 5;
+}
+// byte offset, relative to the chunk's first row, of lane l's 16 bytes of
+// staging batch j for helper wave f (kOutOfRange for padding)
+template <typename Cfg>
+__device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_t rs_k, int64_t rs_v) {
+    constexpr int C = Cfg::NW * 16;
+    const int i = j * Cfg::NF + f;
+    int64_t off = -1;
+    auto region = [&](int s, int P, int B, int W, int64_t row_bytes) {
+        const int r = s / P, p = s - r * P;
+        if (r >= C || p >= B) return (int64_t)-1;
+        int x = p;
+        if (W == 1) x ^= swz<1>(r);
+        else if (W == 2) x ^= swz<2>(r);
+        else if (W == 3) x ^= swz<3>(r);
+        return r * row_bytes + (int64_t)(x * 16);
+    };
+    switch (col_region<Cfg>(j, f)) {
+        case 0: off = region(i * 64 + l, Cfg::KP, Cfg::KB, Cfg::KSW, rs_k); break;
+        case 1: off = region((i - Cfg::JQ * Cfg::NF) * 64 + l, Cfg::KP, Cfg::KB, Cfg::KSW, rs_k); break;
+        case 2: off = region((i - Cfg::JT * Cfg::NF) * 64 + l, Cfg::TP, Cfg::TB, Cfg::TSW, (int64_t)C * Cfg::ES); break;
+        case 3: off = region((i - Cfg::JV * Cfg::NF) * 64 + l, Cfg::VP, Cfg::VB, Cfg::VSW, rs_v); break;
+        case 4: {
+            const int s = (i - Cfg::BG0) * 64 + l;
+            off = s < 3 * C / 4 ? (int64_t)s * 16 : -1;
+            break;
+        }
+        default: break;
+    }
+    return (off < 0 || off >= (int64_t)kOutOfRange) ? kOutOfRange : (uint32_t)off;
+}
+
+// element (r, c) of the staged K / Q (swizzled 16-byte blocks)
+template <typename Cfg>
+__device__ __forceinline__ int ckidx(int r, int c) { return sidx<Cfg, Cfg::KP, Cfg::KSW>(r, c); }
+
+// K^T as the A operand of token block kb for state tile i: lane (g, n) gets
+// K[kb*16 + 4g + e][drow(i, n)] (bf16: one transposing read -- lane s of group g
+// supplies row kb*16 + 4g + s/4 at the 4-run of d holding drow(i, 4 (s%4));
+// fp32: a gather)
+template <typename Cfg, typename T>
+__device__ __forceinline__ typename K16<T>::op kT_tile(const T* sK, int kb, int i) {
+    const int l = lane_id(), g = l >> 4, n = l & 15;
+    if constexpr (Cfg::BF) {
+        return tr_read(sK + ckidx<Cfg>(kb * 16 + 4 * g + (n >> 2), drow<Cfg>(i, 4 * (n & 3))));
+    } else {
+        const T* p = sK + ckidx<Cfg>(kb * 16 + 4 * g, drow<Cfg>(i, n));
+        return f32x4{p[0], p[Cfg::LDK], p[2 * Cfg::LDK], p[3 * Cfg::LDK]};
+    }
+}
+
+template <typename T, int DK, int DV, int C, int DVT>
+__global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* S0, SeqGeom geom, int H,
+    const float* __restrict__ g_ws, const T* __restrict__ Tb_ws,
+    T* __restrict__ O, float* S_T) {   // S_T may alias S0
+    using Cfg = ColCfg<T, DK, DV, C, DVT>;
+    static_assert(Cfg::FITS, "scan workgroup exceeds the LDS of one CU");
+    using St16 = Step<T>;
+    using Frag = typename St16::frag;
+    using KO = K16<T>;
+    using Op = typename KO::op;
+    constexpr int NW = Cfg::NW, NDB = Cfg::NDB, KS = Cfg::KS, NP = Cfg::NP, NKK = Cfg::NKK;
+    constexpr int NVW = Cfg::NVW, ES = Cfg::ES;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    // Workgroups are dealt to the 8 XCDs round-robin by linear id; renumber them
+    // so that the DV / DVT column slices of one (sequence, head) share an XCD and
+    // its L2 serves their common K, Q, Tb and gate reads.
+    int v0, h, seq;
+    {
+        constexpr int NS = DV / DVT;
+        const int U = H * (int)gridDim.z;
+        const int L = (int)(blockIdx.x + NS * (blockIdx.y + gridDim.y * blockIdx.z));
+        const int lfull = (U / 8) * 8 * NS;
+        int u, vs;
+        if (L < lfull) {
+            const int r = L >> 3;
+            vs = r % NS;
+            u = (L & 7) + 8 * (r / NS);
+        } else {
+            u = (U / 8) * 8 + (L - lfull) / NS;
+            vs = (L - lfull) % NS;
+        }
+        v0 = vs * DVT;
+        h = u % H;
+        seq = u / H;
+    }
+    const int l = lane_id(), w = wave_id();
+    const int n = l & 15, g4 = 4 * (l >> 4);
+
+    int ts, te, first;
+    if (geom.table) {
+        ts = geom.bounds[seq];
+        te = geom.bounds[seq + 1];
+        first = geom.seq_slot[seq];
+    } else {
+        ts = seq * geom.T;
+        te = ts + geom.T;
+        first = seq * geom.chunks_per_seq;
+    }
+    const int count = (te - ts + C - 1) / C;
+    const int64_t sbase = ((int64_t)seq * H + h) * DV * DK;
+    const int64_t rs_k = (int64_t)H * DK * ES, rs_v = (int64_t)H * DV * ES;   // token strides (bytes)
+
+    auto barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    struct Staged {
+        const T *K, *Q, *V, *Tb;
+        const float *g, *gam, *dec;
+    };
+    auto staged = [&](int cc) __attribute__((always_inline)) {
+        const unsigned char* sb = smem + (cc & 1) * Cfg::SZ_STAGE;
+        Staged st;
+        st.K = reinterpret_cast<const T*>(sb);
+        st.Q = reinterpret_cast<const T*>(sb + Cfg::OFF_Q);
+        st.V = reinterpret_cast<const T*>(sb + Cfg::OFF_V);
+        st.Tb = reinterpret_cast<const T*>(sb + Cfg::OFF_T);
+        st.g = reinterpret_cast<const float*>(sb + Cfg::OFF_G);
+        st.gam = st.g + C;
+        st.dec = st.g + 2 * C;
+        return st;
+    };
+    // P^T slots of chunk cd
+    auto pbuf = [&](int cd) __attribute__((always_inline)) {
+        return reinterpret_cast<T*>(smem + Cfg::OFF_P + (cd & 1) * Cfg::SZ_P);
+    };
+
+    // ---- column wave vb
+    auto run_col = [&](auto vb_const) __attribute__((always_inline)) {
+        constexpr int vb = decltype(vb_const)::value;
+        const int vcol = v0 + vb * 16 + n;                 // this lane's state column
+        f32x4 St[NDB];
+#pragma unroll
+        for (int i = 0; i < NDB; ++i)
+            St[i] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (int64_t)vcol * DK + drow<Cfg>(i, g4)) : zero4();
+        __syncthreads();
+
+        // Z^T (scaled) and V' (operand form) of the chunk whose output is pending
+        f32x4 Zp[NW];
+        Op Vo[NW];
+        const uint32_t ooff = (uint32_t)(n * rs_v) + (vb * 16 + g4) * ES;
+        // P^T operands of one query block: bf16 pairs of key blocks, fp32 blocks
+        constexpr int NPQ = Cfg::BF ? NP : NW;
+        typedef typename std::conditional<Cfg::BF, s16x8, f32x4>::type PFrag;
+        auto load_p = [&](PFrag (*pf)[NPQ], int cd) __attribute__((always_inline)) {
+            const T* pb = pbuf(cd) + l * (16 / ES);
+#pragma unroll
+            for (int qb = 0; qb < NW; ++qb)
+#pragma unroll
+                for (int p = 0; p < NPQ; ++p)
+                    if ((Cfg::BF ? 2 * p : p) <= qb)
+                        pf[qb][p] = *reinterpret_cast<const PFrag*>(pb + (Cfg::prow(qb) + p) * 64 * (16 / ES));
+        };
+        // O^T = Z^T + V'^T P^T of chunk cd for every query block qb (A: the V'
+        // tiles as V'^T; B: the P^T tiles); lane (g, n) stores
+        // O[token qb*16 + n][v0 + vb*16 + 4g .. + 3]
+        auto output = [&](const PFrag (*pf)[NPQ], int cd) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(O + ((int64_t)t0 * H + h) * DV + v0, (len - 1) * rs_v + DVT * ES);
+#pragma unroll
+            for (int qb = 0; qb < NW; ++qb) {
+                f32x4 acc = Zp[qb];
+                if constexpr (Cfg::BF) {
+#pragma unroll
+                    for (int p = 0; p <= qb / 2; ++p)
+                        acc = KO::mma2(Vo[2 * p], Vo[2 * p + 1], __builtin_shufflevector(pf[qb][p], pf[qb][p], 0, 1, 2, 3),
+                                       __builtin_shufflevector(pf[qb][p], pf[qb][p], 4, 5, 6, 7), acc);
+                    const bf16x4 o4 = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro,
+                                                          ooff + (uint32_t)(qb * 16 * rs_v), 0, 0);
+                } else {
+#pragma unroll
+                    for (int jb = 0; jb <= qb; ++jb) acc = KO::mma1(Vo[jb], pf[qb][jb], acc);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro,
+                                                           ooff + (uint32_t)(qb * 16 * rs_v), 0, 0);
+                }
+            }
+        };
+
+        // One chunk.  The LDS operands of each group of MFMAs are requested one
+        // group ahead (scheduling fences keep the compiler from pulling the
+        // requests next to their uses).
+        auto step = [&](const int cc) __attribute__((always_inline)) {
+            const Staged st = staged(cc);
+            PFrag pf[NW][NPQ];
+            if (cc > 0) load_p(pf, cc - 1);   // published by the last barrier
+
+            // the state slice as MFMA operands (input dtype)
+            Op Sb[NDB];
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) Sb[i] = KO::tile(St[i]);
+            // Y = K S^T (A: K rows; B: the state tiles) and Z^T = S Q^T (A: the
+            // state tiles as S; B: Q rows) for every token block
+            f32x4 Y[NW], Z[NW];
+#pragma unroll
+            for (int tb = 0; tb < NW; ++tb) Y[tb] = Z[tb] = zero4();
+            Frag fk[2][NW], fq[2][NW];
+#pragma unroll
+            for (int tb = 0; tb < NW; ++tb) {
+                fk[0][tb] = kfrag_rows<Cfg>(st.K, tb * 16, 0);
+                fq[0][tb] = kfrag_rows<Cfg>(st.Q, tb * 16, 0);
+            }
+            float4 gam4[NW];
+            f32x4 vv[NW];
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int cur = kk & 1;
+                if (kk + 1 < NKK) {
+#pragma unroll
+                    for (int tb = 0; tb < NW; ++tb) {
+                        fk[cur ^ 1][tb] = kfrag_rows<Cfg>(st.K, tb * 16, (kk + 1) * KS);
+                        fq[cur ^ 1][tb] = kfrag_rows<Cfg>(st.Q, tb * 16, (kk + 1) * KS);
+                    }
+                } else {
+#pragma unroll
+                    for (int tb = 0; tb < NW; ++tb) {
+                        gam4[tb] = *reinterpret_cast<const float4*>(st.gam + tb * 16 + g4);
+                        vv[tb] = vcol4<Cfg>(st.V, tb, vb);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int tb = 0; tb < NW; ++tb) {
+                    if constexpr (Cfg::BF) {
+                        const s16x8 qs = __builtin_bit_cast(s16x8, fq[cur][tb]);
+                        Y[tb] = KO::mma2p(fk[cur][tb], Sb[2 * kk], Sb[2 * kk + 1], Y[tb]);
+                        Z[tb] = KO::mma2(Sb[2 * kk], Sb[2 * kk + 1], __builtin_shufflevector(qs, qs, 0, 1, 2, 3),
+                                         __builtin_shufflevector(qs, qs, 4, 5, 6, 7), Z[tb]);
+                    } else {
+                        Y[tb] = St16::mma(fk[cur][tb], Sb[kk], Y[tb]);
+                        Z[tb] = St16::mma(Sb[kk], fq[cur][tb], Z[tb]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+
+            // Tb rows for V' = Tb X, requested now
+            typedef typename std::conditional<Cfg::BF, bf16x8, f32x4>::type TFrag;
+            TFrag ta[NW][Cfg::BF ? NP : NW];
+#pragma unroll
+            for (int ib = 0; ib < NW; ++ib) {
+                const int ar = ib * 16 + n;
+#pragma unroll
+                for (int p = 0; p < (Cfg::BF ? NP : NW); ++p) {
+                    if constexpr (Cfg::BF) {
+                        if (2 * p <= ib) ta[ib][p] = *reinterpret_cast<const bf16x8*>(st.Tb + tidx<Cfg>(ar, 32 * p + 2 * g4));
+                    } else {
+                        if (p <= ib) ta[ib][p] = *reinterpret_cast<const f32x4*>(st.Tb + tidx<Cfg>(ar, 16 * p + g4));
+                    }
+                }
+            }
+            // the previous chunk's output while they arrive
+            if (cc > 0) output(pf, cc - 1);
+            // X = V - diag(gamma) Y, as the B operand of V' = Tb X
+            Op Xo[NW];
+#pragma unroll
+            for (int tb = 0; tb < NW; ++tb)
+                Xo[tb] = KO::tile(f32x4{vv[tb][0] - gam4[tb].x * Y[tb][0], vv[tb][1] - gam4[tb].y * Y[tb][1],
+                                        vv[tb][2] - gam4[tb].z * Y[tb][2], vv[tb][3] - gam4[tb].w * Y[tb][3]});
+            // K^T operands and the decays of the state update, requested now
+            Op kt[NDB][NW];
+#pragma unroll
+            for (int i = 0; i < NDB; ++i)
+#pragma unroll
+                for (int kb = 0; kb < NW; ++kb) kt[i][kb] = kT_tile<Cfg>(st.K, kb, i);
+            float4 dec4[NW];
+#pragma unroll
+            for (int jb = 0; jb < NW; ++jb) dec4[jb] = *reinterpret_cast<const float4*>(st.dec + jb * 16 + g4);
+            const float gamma_n = st.gam[C - 1];
+            __builtin_amdgcn_sched_barrier(0);
+
+            // V' = Tb X (A: Tb rows, token pairs as X)
+            f32x4 Vp[NW];
+#pragma unroll
+            for (int ib = 0; ib < NW; ++ib) {
+                f32x4 acc = zero4();
+                if constexpr (Cfg::BF) {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+                        if (2 * p <= ib) acc = KO::mma2p(ta[ib][p], Xo[2 * p], Xo[2 * p + 1], acc);
+                } else {
+#pragma unroll
+                    for (int jb = 0; jb <= ib; ++jb) acc = KO::mma1(ta[ib][jb], Xo[jb], acc);
+                }
+                Vp[ib] = acc;
+            }
+            // this chunk's Z^T (scaled by gamma) and V' for the next step's output
+#pragma unroll
+            for (int qb = 0; qb < NW; ++qb) {
+                Zp[qb] = Z[qb] * st.gam[qb * 16 + n];
+                Vo[qb] = KO::tile(Vp[qb]);
+            }
+            // S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V'
+            Op Vd[NW];
+#pragma unroll
+            for (int jb = 0; jb < NW; ++jb)
+                Vd[jb] = KO::tile(f32x4{Vp[jb][0] * dec4[jb].x, Vp[jb][1] * dec4[jb].y, Vp[jb][2] * dec4[jb].z,
+                                        Vp[jb][3] * dec4[jb].w});
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) St[i] *= gamma_n;
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int i = 0; i < NDB; ++i) {
+                    if (2 * p + 1 < NW)
+                        St[i] = KO::mma2(kt[i][2 * p], kt[i][2 * p + 1], Vd[2 * p], Vd[2 * p + 1], St[i]);
+                    else
+                        St[i] = KO::mma1(kt[i][2 * p], Vd[2 * p], St[i]);
+                }
+            wait_vm_lgkm0<63>();
+            barrier();
+        };
+        int cc = 0;
+        for (; cc + 2 <= count; cc += 2) {
+            step(cc);
+            step(cc + 1);
+        }
+        if (cc < count) step(cc);
+        if (count > 0) {   // the last chunk's P^T tiles were published by the last barrier
+            PFrag pf[NW][NPQ];
+            load_p(pf, count - 1);
+            output(pf, count - 1);
+        }
+
+        if (S_T) {
+#pragma unroll
+            for (int i = 0; i < NDB; ++i)
+                *reinterpret_cast<f32x4*>(S_T + sbase + (int64_t)vcol * DK + drow<Cfg>(i, g4)) = St[i];
+        }
+    };
+
+    // ---- helper wave hw: stages its share of each chunk; helpers hw < NPP also
+    // form P^T = ((Q K^T) o Gamma o M)^T (rows: key tokens) for their query
+    // blocks, decayed and masked, into the P^T slots of the chunk
+    auto run_help = [&](auto hw_const) __attribute__((always_inline)) {
+        constexpr int hw = decltype(hw_const)::value;
+        // staging: chunk cd's K, Q, Tb, V slice and gates into registers (rows
+        // past the chunk end fall outside the buffer ranges and read as zeros),
+        // then into the staging buffer of its parity
+        uint32_t soff[Cfg::NL];
+#pragma unroll
+        for (int j = 0; j < Cfg::NL; ++j) soff[j] = col_stage_offset<Cfg>(j, hw, l, rs_k, rs_v);
+        auto stage_load = [&](u32x4* R, int cd) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const int64_t unit = (int64_t)(first + cd) * H + h;
+            const T* kb = k + ((int64_t)t0 * H + h) * DK;
+            const T* qb = q + ((int64_t)t0 * H + h) * DK;
+            const T* vb_ = v + ((int64_t)t0 * H + h) * DV + v0;
+            const T* tb = Tb_ws + unit * C * C;
+            const float* gb = g_ws + unit * 3 * C;
+            const int nk = (int)((len - 1) * rs_k + DK * ES), nv = (int)((len - 1) * rs_v + DVT * ES);
+#pragma unroll
+            for (int j = 0; j < Cfg::NL; ++j) {
+                const void* base;
+                int nrec;
+                if (j < Cfg::JQ) { base = kb; nrec = nk; }
+                else if (j < Cfg::JT) { base = qb; nrec = nk; }
+                else if (j < Cfg::JV) { base = tb; nrec = C * C * ES; }
+                else {
+                    const int r = col_region<Cfg>(j, hw);
+                    base = r == 3 ? (const void*)vb_ : (const void*)gb;
+                    nrec = r == 3 ? nv : r == 4 ? 3 * C * 4 : 0;
+                }
+                R[j] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, nrec), soff[j], 0, 0);
+            }
+        };
+        auto stage_store = [&](const u32x4* R, int cd) __attribute__((always_inline)) {
+            unsigned char* base = smem + (cd & 1) * Cfg::SZ_STAGE + (hw * 64 + l) * 16;
+#pragma unroll
+            for (int j = 0; j < Cfg::NL; ++j)
+                if (col_region<Cfg>(j, hw) != 5) *reinterpret_cast<u32x4*>(base + j * Cfg::NF * 1024) = R[j];
+        };
+        // Two register sets take turns: step cc writes the one holding chunk
+        // cc + 1 to LDS as it starts (that buffer's readers are past the previous
+        // barrier) and refills it with chunk cc + 3.
+        u32x4 ra[Cfg::NL], rb[Cfg::NL];
+        if (count > 0) {
+            stage_load(ra, 0);
+            stage_load(rb, min(1, count - 1));
+            stage_store(ra, 0);
+            stage_load(ra, min(2, count - 1));
+        }
+        __syncthreads();
+
+        auto step = [&](const int cc, u32x4* rnext) __attribute__((always_inline)) {
+            stage_store(rnext, cc + 1);
+            stage_load(rnext, min(cc + 3, count - 1));   // past the end: re-read, unused
+            if constexpr (hw < Cfg::NPP) {
+                const Staged st = staged(cc);
+                T* pb = pbuf(cc) + l * (16 / ES);
+                f32x4 Pt[NW][NW];
+#pragma unroll
+                for (int qb = 0; qb < NW; ++qb)
+#pragma unroll
+                    for (int jb = 0; jb < NW; ++jb) Pt[qb][jb] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    Frag kf[NW];
+#pragma unroll
+                    for (int jb = 0; jb < NW; ++jb) {
+                        bool need = false;
+#pragma unroll
+                        for (int qb = jb; qb < NW; ++qb) need = need || Cfg::pwave(qb) == hw;
+                        if (need) kf[jb] = kfrag_rows<Cfg>(st.K, jb * 16, kk * KS);
+                    }
+#pragma unroll
+                    for (int qb = 0; qb < NW; ++qb) {
+                        if (Cfg::pwave(qb) != hw) continue;
+                        const Frag aq = kfrag_rows<Cfg>(st.Q, qb * 16, kk * KS);
+#pragma unroll
+                        for (int jb = 0; jb <= qb; ++jb) Pt[qb][jb] = St16::mma(kf[jb], aq, Pt[qb][jb]);
+                    }
+                }
+#pragma unroll
+                for (int qb = 0; qb < NW; ++qb) {
+                    if (Cfg::pwave(qb) != hw) continue;
+                    const int cq = qb * 16 + n;
+                    const float gq = st.g[cq];
+#pragma unroll
+                    for (int jb = 0; jb <= qb; ++jb) {
+                        const float4 gj = *reinterpret_cast<const float4*>(st.g + jb * 16 + g4);
+                        const int j0 = jb * 16 + g4;
+                        f32x4& P = Pt[qb][jb];
+                        P[0] = j0 + 0 <= cq ? P[0] * __expf(gq - gj.x) : 0.f;
+                        P[1] = j0 + 1 <= cq ? P[1] * __expf(gq - gj.y) : 0.f;
+                        P[2] = j0 + 2 <= cq ? P[2] * __expf(gq - gj.z) : 0.f;
+                        P[3] = j0 + 3 <= cq ? P[3] * __expf(gq - gj.w) : 0.f;
+                    }
+                    T* prow = pb + Cfg::prow(qb) * 64 * (16 / ES);
+                    if constexpr (Cfg::BF) {
+#pragma unroll
+                        for (int p = 0; p <= qb / 2; ++p)
+                            *reinterpret_cast<s16x8*>(prow + p * 64 * 8) = __builtin_shufflevector(
+                                KO::tile(Pt[qb][2 * p]), KO::tile(Pt[qb][2 * p + 1]), 0, 1, 2, 3, 4, 5, 6, 7);
+                    } else {
+#pragma unroll
+                        for (int jb = 0; jb <= qb; ++jb) *reinterpret_cast<f32x4*>(prow + jb * 64 * 4) = Pt[qb][jb];
+                    }
+                }
+            }
+            wait_vm_lgkm0<63>();
+            barrier();
+        };
+        int cc = 0;
+        for (; cc + 2 <= count; cc += 2) {
+            step(cc, rb);
+            step(cc + 1, ra);
+        }
+        if (cc < count) step(cc, rb);
+    };
+
+    if (w < NVW) {
+        if (w == 0) run_col(std::integral_constant<int, 0>{});
+        else if constexpr (NVW > 1) run_col(std::integral_constant<int, (NVW > 1 ? 1 : 0)>{});
+    } else {
+        switch (w - NVW) {
+            case 0: run_help(std::integral_constant<int, 0>{}); break;
+            case 1: run_help(std::integral_constant<int, 1>{}); break;
+            case 2: run_help(std::integral_constant<int, 2>{}); break;
+            default: run_help(std::integral_constant<int, 3>{}); break;
+        }
+    }
+}
+
+}  // namespace gdn
