@@ -22,7 +22,9 @@
 // helpers get a SIMD each and the staging-only helpers share the column
 // waves' SIMDs.
 // One barrier per chunk.  A column wave forms the output of chunk cc - 1 during
-// step cc, when the helpers' P^T tiles of that chunk are published.
+// step cc, when the helpers' P^T tiles of that chunk are published, and leaves
+// it in LDS; the helpers write it out in step cc + 1 as 16-byte pieces of its
+// rows (the slice's rows are 2 DVT bytes long in memory).
 //
 // State tile layout.  Column wave vb keeps Dk / 16 tiles; lane (g, n) of tile i
 // holds S^T[drow(i, 4g + r)][vb*16 + n], r = 0..3.  bf16: tile 2m + h covers
@@ -68,6 +70,7 @@ struct ColCfg {
     static constexpr int NBK = cdiv(NIK, NF), NBT = cdiv(NIT, NF);
     static constexpr int NBVG = VG1 ? 1 : cdiv(NIV, NF) + cdiv(NIG, NF);
     static constexpr int NL = 2 * NBK + NBT + NBVG;        // staging loads per lane per chunk
+    static constexpr int NSET = 2;                         // chunks in flight per helper lane
     static constexpr int JQ = NBK, JT = 2 * NBK, JV = JT + NBT;
     static constexpr int JG = VG1 ? JV : JV + cdiv(NIV, NF);
     static constexpr int BG0 = VG1 ? JV * NF + NIV : JG * NF;
@@ -85,7 +88,15 @@ struct ColCfg {
     }
     static constexpr size_t SZ_P = (size_t)prow(NW) * 1024;
     static constexpr size_t OFF_P = 2 * SZ_STAGE;
-    static constexpr size_t SMEM = OFF_P + 2 * SZ_P;
+    // the chunk's output slice, handed from the column waves to the helpers,
+    // which write it out as whole 16-byte pieces of its rows: rows of DVT values
+    // padded by 16 bytes; two buffers (chunk parity)
+    static constexpr int LDO = DVT * ES + 16;                  // row pitch (bytes)
+    static constexpr int OPR = DVT * ES / 16;                  // 16-byte pieces per row
+    static constexpr int NOPL = cdiv(C * OPR, NPW * 64);       // pieces per helper lane
+    static constexpr size_t SZ_O = (size_t)C * LDO;
+    static constexpr size_t OFF_O = OFF_P + 2 * SZ_P;
+    static constexpr size_t SMEM = OFF_O + 2 * SZ_O;
     static constexpr bool FITS = SMEM <= 160 * 1024;
     // P helper of query block qb: 0 takes blocks 0 and NW - 1, 1 the middle ones
     static constexpr int pwave(int qb) { return (qb < NW - 1 - qb ? qb : NW - 1 - qb) % NPP; }
@@ -243,6 +254,8 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
     auto pbuf = [&](int cd) __attribute__((always_inline)) {
         return reinterpret_cast<T*>(smem + Cfg::OFF_P + (cd & 1) * Cfg::SZ_P);
     };
+    // output slice of chunk cd
+    auto obuf = [&](int cd) __attribute__((always_inline)) { return smem + Cfg::OFF_O + (cd & 1) * Cfg::SZ_O; };
 
     // ---- column wave vb
     auto run_col = [&](auto vb_const) __attribute__((always_inline)) {
@@ -257,7 +270,6 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         // Z^T (scaled) and V' (operand form) of the chunk whose output is pending
         f32x4 Zp[NW];
         Op Vo[NW];
-        const uint32_t ooff = (uint32_t)(n * rs_v) + (vb * 16 + g4) * ES;
         // P^T operands of one query block: bf16 pairs of key blocks, fp32 blocks
         constexpr int NPQ = Cfg::BF ? NP : NW;
         typedef typename std::conditional<Cfg::BF, s16x8, f32x4>::type PFrag;
@@ -271,12 +283,10 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                         pf[qb][p] = *reinterpret_cast<const PFrag*>(pb + (Cfg::prow(qb) + p) * 64 * (16 / ES));
         };
         // O^T = Z^T + V'^T P^T of chunk cd for every query block qb (A: the V'
-        // tiles as V'^T; B: the P^T tiles); lane (g, n) stores
-        // O[token qb*16 + n][v0 + vb*16 + 4g .. + 3]
+        // tiles as V'^T; B: the P^T tiles); lane (g, n) leaves
+        // O[token qb*16 + n][vb*16 + 4g .. + 3] in the chunk's output slice
         auto output = [&](const PFrag (*pf)[NPQ], int cd) __attribute__((always_inline)) {
-            const int t0 = ts + cd * C, len = min(C, te - t0);
-            const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(O + ((int64_t)t0 * H + h) * DV + v0, (len - 1) * rs_v + DVT * ES);
+            unsigned char* ob = obuf(cd) + n * Cfg::LDO + (vb * 16 + g4) * ES;
 #pragma unroll
             for (int qb = 0; qb < NW; ++qb) {
                 f32x4 acc = Zp[qb];
@@ -285,21 +295,18 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                     for (int p = 0; p <= qb / 2; ++p)
                         acc = KO::mma2(Vo[2 * p], Vo[2 * p + 1], __builtin_shufflevector(pf[qb][p], pf[qb][p], 0, 1, 2, 3),
                                        __builtin_shufflevector(pf[qb][p], pf[qb][p], 4, 5, 6, 7), acc);
-                    const bf16x4 o4 = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), ro,
-                                                          ooff + (uint32_t)(qb * 16 * rs_v), 0, 0);
                 } else {
 #pragma unroll
                     for (int jb = 0; jb <= qb; ++jb) acc = KO::mma1(Vo[jb], pf[qb][jb], acc);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro,
-                                                           ooff + (uint32_t)(qb * 16 * rs_v), 0, 0);
                 }
+                store4(reinterpret_cast<T*>(ob + qb * 16 * Cfg::LDO), acc[0], acc[1], acc[2], acc[3]);
             }
         };
 
-        // One chunk.  The LDS operands of each group of MFMAs are requested one
-        // group ahead (scheduling fences keep the compiler from pulling the
-        // requests next to their uses).
+        // One chunk.  LDS operands are requested a group of MFMAs ahead of their
+        // use (scheduling fences keep the compiler from pulling the requests next
+        // to their uses); the previous chunk's output goes out after the first
+        // group, which frees its registers for the later requests.
         auto step = [&](const int cc) __attribute__((always_inline)) {
             const Staged st = staged(cc);
             PFrag pf[NW][NPQ];
@@ -320,8 +327,13 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 fk[0][tb] = kfrag_rows<Cfg>(st.K, tb * 16, 0);
                 fq[0][tb] = kfrag_rows<Cfg>(st.Q, tb * 16, 0);
             }
-            float4 gam4[NW];
+            // the gates and the Tb rows, requested with the last K / Q group
+            float4 gam4[NW], dec4[NW];
+            float gamq[NW], gamma_n;
             f32x4 vv[NW];
+            typedef typename std::conditional<Cfg::BF, bf16x8, f32x4>::type TFrag;
+            constexpr int NTP = Cfg::BF ? NP : NW;
+            TFrag ta[NW][NTP];
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const int cur = kk & 1;
@@ -335,8 +347,23 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
 #pragma unroll
                     for (int tb = 0; tb < NW; ++tb) {
                         gam4[tb] = *reinterpret_cast<const float4*>(st.gam + tb * 16 + g4);
+                        dec4[tb] = *reinterpret_cast<const float4*>(st.dec + tb * 16 + g4);
+                        gamq[tb] = st.gam[tb * 16 + n];
                         vv[tb] = vcol4<Cfg>(st.V, tb, vb);
                     }
+                    gamma_n = st.gam[C - 1];
+#pragma unroll
+                    for (int ib = 0; ib < NW; ++ib)
+#pragma unroll
+                        for (int p = 0; p < NTP; ++p) {
+                            if constexpr (Cfg::BF) {
+                                if (2 * p <= ib)
+                                    ta[ib][p] = *reinterpret_cast<const bf16x8*>(st.Tb + tidx<Cfg>(ib * 16 + n, 32 * p + 2 * g4));
+                            } else {
+                                if (p <= ib)
+                                    ta[ib][p] = *reinterpret_cast<const f32x4*>(st.Tb + tidx<Cfg>(ib * 16 + n, 16 * p + g4));
+                            }
+                        }
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -352,43 +379,25 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-            }
-
-            // Tb rows for V' = Tb X, requested now
-            typedef typename std::conditional<Cfg::BF, bf16x8, f32x4>::type TFrag;
-            TFrag ta[NW][Cfg::BF ? NP : NW];
-#pragma unroll
-            for (int ib = 0; ib < NW; ++ib) {
-                const int ar = ib * 16 + n;
-#pragma unroll
-                for (int p = 0; p < (Cfg::BF ? NP : NW); ++p) {
-                    if constexpr (Cfg::BF) {
-                        if (2 * p <= ib) ta[ib][p] = *reinterpret_cast<const bf16x8*>(st.Tb + tidx<Cfg>(ar, 32 * p + 2 * g4));
-                    } else {
-                        if (p <= ib) ta[ib][p] = *reinterpret_cast<const f32x4*>(st.Tb + tidx<Cfg>(ar, 16 * p + g4));
-                    }
+                if (kk == 0 && cc > 0) {
+                    output(pf, cc - 1);   // its P^T tiles were published by the last barrier
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // the previous chunk's output while they arrive
-            if (cc > 0) output(pf, cc - 1);
+
+            // K^T operands of the state update, requested now
+            Op kt[NDB][NW];
+#pragma unroll
+            for (int i = 0; i < NDB; ++i)
+#pragma unroll
+                for (int kb = 0; kb < NW; ++kb) kt[i][kb] = kT_tile<Cfg>(st.K, kb, i);
             // X = V - diag(gamma) Y, as the B operand of V' = Tb X
             Op Xo[NW];
 #pragma unroll
             for (int tb = 0; tb < NW; ++tb)
                 Xo[tb] = KO::tile(f32x4{vv[tb][0] - gam4[tb].x * Y[tb][0], vv[tb][1] - gam4[tb].y * Y[tb][1],
                                         vv[tb][2] - gam4[tb].z * Y[tb][2], vv[tb][3] - gam4[tb].w * Y[tb][3]});
-            // K^T operands and the decays of the state update, requested now
-            Op kt[NDB][NW];
-#pragma unroll
-            for (int i = 0; i < NDB; ++i)
-#pragma unroll
-                for (int kb = 0; kb < NW; ++kb) kt[i][kb] = kT_tile<Cfg>(st.K, kb, i);
-            float4 dec4[NW];
-#pragma unroll
-            for (int jb = 0; jb < NW; ++jb) dec4[jb] = *reinterpret_cast<const float4*>(st.dec + jb * 16 + g4);
-            const float gamma_n = st.gam[C - 1];
             __builtin_amdgcn_sched_barrier(0);
-
             // V' = Tb X (A: Tb rows, token pairs as X)
             f32x4 Vp[NW];
 #pragma unroll
@@ -404,20 +413,15 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 }
                 Vp[ib] = acc;
             }
-            // this chunk's Z^T (scaled by gamma) and V' for the next step's output
+            // gamma_n S^T while V' completes
 #pragma unroll
-            for (int qb = 0; qb < NW; ++qb) {
-                Zp[qb] = Z[qb] * st.gam[qb * 16 + n];
-                Vo[qb] = KO::tile(Vp[qb]);
-            }
+            for (int i = 0; i < NDB; ++i) St[i] *= gamma_n;
             // S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V'
             Op Vd[NW];
 #pragma unroll
             for (int jb = 0; jb < NW; ++jb)
                 Vd[jb] = KO::tile(f32x4{Vp[jb][0] * dec4[jb].x, Vp[jb][1] * dec4[jb].y, Vp[jb][2] * dec4[jb].z,
                                         Vp[jb][3] * dec4[jb].w});
-#pragma unroll
-            for (int i = 0; i < NDB; ++i) St[i] *= gamma_n;
 #pragma unroll
             for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -427,6 +431,12 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                     else
                         St[i] = KO::mma1(kt[i][2 * p], Vd[2 * p], St[i]);
                 }
+            // this chunk's Z^T (scaled by gamma) and V' for the next step's output
+#pragma unroll
+            for (int qb = 0; qb < NW; ++qb) {
+                Zp[qb] = Z[qb] * gamq[qb];
+                Vo[qb] = KO::tile(Vp[qb]);
+            }
             wait_vm_lgkm0<63>();
             barrier();
         };
@@ -441,6 +451,8 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             load_p(pf, count - 1);
             output(pf, count - 1);
         }
+        wait_vm_lgkm0<63>();
+        __syncthreads();   // the helpers write out the last output slices
 
         if (S_T) {
 #pragma unroll
@@ -490,21 +502,40 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             for (int j = 0; j < Cfg::NL; ++j)
                 if (col_region<Cfg>(j, hw) != 5) *reinterpret_cast<u32x4*>(base + j * Cfg::NF * 1024) = R[j];
         };
-        // Two register sets take turns: step cc writes the one holding chunk
-        // cc + 1 to LDS as it starts (that buffer's readers are past the previous
-        // barrier) and refills it with chunk cc + 3.
-        u32x4 ra[Cfg::NL], rb[Cfg::NL];
+        // chunk cd's output slice from LDS to memory, 16 bytes per lane, rows
+        // past the chunk end dropped by the buffer range; streamed past the caches
+        auto write_out = [&](int cd) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(O + ((int64_t)t0 * H + h) * DV + v0, (len - 1) * rs_v + DVT * ES);
+            const unsigned char* ob = obuf(cd);
+#pragma unroll
+            for (int j = 0; j < Cfg::NOPL; ++j) {
+                const int piece = (j * Cfg::NPW + hw) * 64 + l;
+                if (Cfg::NOPL * Cfg::NPW * 64 == C * Cfg::OPR || piece < C * Cfg::OPR) {
+                    const int r = piece / Cfg::OPR, b = piece - r * Cfg::OPR;
+                    const u32x4 d = *reinterpret_cast<const u32x4*>(ob + r * Cfg::LDO + b * 16);
+                    __builtin_amdgcn_raw_buffer_store_b128(d, ro, (uint32_t)(r * rs_v) + b * 16, 0, 2);
+                }
+            }
+        };
+        // NSET register sets take turns, chunk j in set j % NSET: step cc writes
+        // the one holding chunk cc + 1 to LDS as it starts (that buffer's readers
+        // are past the previous barrier) and refills it with chunk cc + 1 + NSET.
+        constexpr int NSET = Cfg::NSET;
+        u32x4 rs[NSET][Cfg::NL];
         if (count > 0) {
-            stage_load(ra, 0);
-            stage_load(rb, min(1, count - 1));
-            stage_store(ra, 0);
-            stage_load(ra, min(2, count - 1));
+#pragma unroll
+            for (int j = 0; j < NSET; ++j) stage_load(rs[j], min(j, count - 1));
+            stage_store(rs[0], 0);
+            stage_load(rs[0], min(NSET, count - 1));
         }
         __syncthreads();
 
         auto step = [&](const int cc, u32x4* rnext) __attribute__((always_inline)) {
             stage_store(rnext, cc + 1);
-            stage_load(rnext, min(cc + 3, count - 1));   // past the end: re-read, unused
+            stage_load(rnext, min(cc + 1 + NSET, count - 1));   // past the end: re-read, unused
+            if (cc >= 2) write_out(cc - 2);                      // left by the column waves last step
             if constexpr (hw < Cfg::NPP) {
                 const Staged st = staged(cc);
                 T* pb = pbuf(cc) + l * (16 / ES);
@@ -561,12 +592,19 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             wait_vm_lgkm0<63>();
             barrier();
         };
+        // unrolled over the register sets and the two staging buffers
+        constexpr int UN = NSET % 2 ? 2 * NSET : NSET;
         int cc = 0;
-        for (; cc + 2 <= count; cc += 2) {
-            step(cc, rb);
-            step(cc + 1, ra);
+        for (; cc + UN <= count; cc += UN) {
+#pragma unroll
+            for (int i = 0; i < UN; ++i) step(cc + i, rs[(i + 1) % NSET]);
         }
-        if (cc < count) step(cc, rb);
+#pragma unroll
+        for (int i = 0; i < UN - 1; ++i)
+            if (cc + i < count) step(cc + i, rs[(i + 1) % NSET]);
+        __syncthreads();   // the column waves have left the last output slice
+        if (count >= 2) write_out(count - 2);
+        if (count >= 1) write_out(count - 1);
     };
 
     if (w < NVW) {
