@@ -106,6 +106,25 @@ void allow_smem(size_t bytes) {
     (void)done;
 }
 
+// Workgroups of `threads` threads and `smem` bytes of LDS that one CU holds at
+// once (occupancy query, cached per kernel and device; at least 1).
+template <auto Kernel>
+int resident_per_cu(int threads, size_t smem) {
+    static int cached[64] = {0};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    int& c = cached[dev & 63];
+    if (c == 0) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(Kernel), threads, smem) !=
+                hipSuccess ||
+            nb < 1)
+            nb = 1;
+        c = nb;
+    }
+    return c;
+}
+
 // Optional per-kernel timing: events recorded on the launch stream around each
 // kernel (table, prep, scan).
 struct KernelTimer {
@@ -157,12 +176,12 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         using P = PrepCfg<T, DK, C>;
         constexpr auto kp = gdn_prep_kernel<T, DK, C>;
         allow_smem<kp>(P::SMEM);
-        // persistent: as many workgroups as fit on the device at once, each
-        // walking units (slot, head) with a stride of the grid
+        // persistent: as many workgroups as are resident on the device at once,
+        // each wave walking units (slot, head) with a stride of all waves
         const int64_t units = L.slots * a.H;
-        constexpr int per_cu = (int)(160 * 1024 / P::SMEM) < 8 ? (int)(160 * 1024 / P::SMEM) : 8;
-        const int64_t resident = (int64_t)device_cu_count() * per_cu;
-        const unsigned grid = (unsigned)(units < resident ? units : resident);
+        const int64_t resident = (int64_t)device_cu_count() * resident_per_cu<kp>(kThreads, P::SMEM);
+        const int64_t need = (units + P::WAVES - 1) / P::WAVES;
+        const unsigned grid = (unsigned)(need < resident ? need : resident);
         tm->mark(a.stream);
         hipLaunchKernelGGL(kp, dim3(grid), dim3(kThreads), P::SMEM, a.stream,
                            k, a.log_alpha, a.beta, geom, a.H, (int)units, g_ws, Tb_ws);

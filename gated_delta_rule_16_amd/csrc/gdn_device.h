@@ -48,6 +48,28 @@ template <> struct Mfma<float> {
     }
 };
 
+// One 16-byte step of a contraction along the rows of two row-major operands:
+// lane (g, n) holds elements [k0 + g*EV, k0 + (g+1)*EV) of row n (EV = 16 / sizeof(T)).
+// bf16: one 16x16x32 MFMA; fp32: four 16x16x4 MFMAs, step r contracting
+// k0 + 4g + r (the same assignment on both operands).
+template <typename T> struct Step;
+template <> struct Step<bf16> {
+    static constexpr int KS = 32;
+    typedef bf16x8 frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Step<float> {
+    static constexpr int KS = 16;
+    typedef f32x4 frag;
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], c, 0, 0, 0);
+        return c;
+    }
+};
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
@@ -93,6 +115,14 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // a byte offset past every reco
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// lds + 16 l (lds must be the same for the whole wave); out-of-range offsets
+// land as zeros.  Completion is counted by vmcnt, like any other load.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
 // XOR swizzles of 16-byte blocks in LDS rows: data block b of row r sits at

@@ -23,10 +23,25 @@
 // Padding: rows i >= n act as tokens with k = 0, beta = 0, log alpha = 0, which
 // makes their rows and columns of Tb zero.
 //
-// The kernel is persistent: each workgroup walks units (chunk slot, head)
-// u = blockIdx.x, blockIdx.x + gridDim.x, ... and loads the next unit's keys
-// and gates into registers while it works on the current one, so that the
-// loads' latency overlaps computation.
+// Work split: one wave prepares one unit (chunk slot, head) at a time, with no
+// synchronisation beyond the wave.  Waves are persistent: wave w of workgroup
+// b walks units b*4 + w, then that plus 4 gridDim, ... and loads the next
+// unit's keys and gates into registers while it works on the current one.
+// Per unit:
+//  - the keys arrive as MFMA row fragments (lane (g, n): row 16b + n, 16 bytes
+//    at contraction offset 16 g of each step), so K K^T needs no LDS;
+//  - tile (i, m) of K K^T is formed as K_m K_i^T, whose accumulator layout is
+//    the A operand layout of tile (i, m) -- lane (g, n) holds row 16i + n,
+//    columns 16m + 4g .. + 3 -- and gated and masked there into A;
+//  - each diagonal 16 x 16 block of T is found by forward substitution in
+//    registers (lane (b, c): column c of block b) from the block's columns of
+//    A in LDS; the blocks below the diagonal follow one block diagonal at a
+//    time, T_ij = -T_ii sum_{j <= m < i} A_im T_mj, on fp32 MFMA straight from
+//    registers (the diagonal blocks of T pass through LDS once, for the two
+//    operand layouts they serve in), each block also formed in row layout as
+//    T_ij^T = -R^T T_ii^T;
+//  - Tb = T diag(beta) leaves from that row layout as whole 16-byte pieces of
+//    its rows.
 #pragma once
 
 #include "gdn_device.h"
@@ -37,24 +52,31 @@ template <typename T, int DK, int C>
 struct PrepCfg {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr int ES = sizeof(T), EV = 16 / ES;
-    static constexpr int NB = C / 16;                     // 16-row blocks
-    static constexpr int NT = NB * (NB + 1) / 2;          // lower 16x16 tiles of A
-    // K rows: bf16 unpadded with the XOR swizzle of kind 1 (16-byte row reads of
-    // 8 consecutive rows hit disjoint banks); fp32 padded by one block
-    static constexpr int KB = DK / EV, KP = BF ? KB : KB + 1, KSW = BF ? 1 : 0;
-    static constexpr int LDK = KP * EV;
-    static constexpr int LDA = C + 4;                     // fp32 A and T rows
-    static constexpr int NL = (C * KB + kThreads - 1) / kThreads;   // 16-byte K loads per lane
-    static constexpr size_t SZ_K = (size_t)C * LDK * ES;
-    static constexpr size_t SZ_T = sizeof(float) * C * LDA;
-    static constexpr size_t OFF_K = 0;                    // K, then T (K is dead by then)
-    static constexpr size_t OFF_A = ((SZ_K > SZ_T ? SZ_K : SZ_T) + 15) / 16 * 16;
-    static constexpr size_t OFF_G = OFF_A + SZ_T;
-    static constexpr size_t OFF_B = OFF_G + sizeof(float) * C;
-    static constexpr size_t SMEM = OFF_B + sizeof(float) * C;
-    static_assert(C <= 64 && C % 16 == 0, "at most four 16-row blocks");
-    static_assert(!BF || KB % 8 == 0, "bf16 K rows of at least 8 blocks");
+    static constexpr int NB = C / 16;                      // 16-row blocks
+    static constexpr int KS = Step<T>::KS, NKK = DK / KS;  // contraction steps over d
+    static constexpr int NKF = NB * NKK;                   // key fragments per lane
+    static constexpr bool PREFETCH = NKF <= 16;            // next unit's keys held meanwhile
+    static constexpr int WAVES = kThreads / 64;
+    static constexpr int MIN_WAVES_SIMD = 1;               // register budget: 512 / this per wave
+    // per-wave LDS (bytes): g, beta; the diagonal blocks of A and of T, both
+    // column-major
+    static constexpr int OFF_G = 0, OFF_B = 4 * C, OFF_AD = 8 * C;
+    static constexpr int OFF_TD = OFF_AD + NB * 1024;
+    static constexpr int WAVE_LDS = OFF_TD + NB * 1024;
+    static constexpr size_t SMEM = (size_t)WAVES * WAVE_LDS;
+    static_assert(C <= 64 && C % 16 == 0 && DK % KS == 0, "at most four 16-row blocks");
+    static_assert(!BF || C % 32 == 0, "bf16 Tb in 32-column groups");
 };
+
+// Exchange point between lanes of one wave that pass values through LDS: the
+// hardware keeps one wave's LDS accesses in order, so it is enough that the
+// compiler does not move memory accesses across this point (no wait is
+// issued, which leaves outstanding global loads and stores in flight)
+__device__ __forceinline__ void wave_lds_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // c += A B over one 16-deep block with fp32 MFMA: lane (g, n) holds a = A[n][4g .. 4g+3]
 // and b = B[4g .. 4g+3][n] (the 16x16 accumulator layout of B)
@@ -65,197 +87,210 @@ __device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
 }
 
 template <typename T, int DK, int C>
-__global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
+__global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void gdn_prep_kernel(
     const T* __restrict__ k, const float* __restrict__ log_alpha,
     const float* __restrict__ beta, SeqGeom geom, int H, int units,
     float* __restrict__ g_ws, T* __restrict__ Tb_ws) {
     using Cfg = PrepCfg<T, DK, C>;
-    using M = Mfma<T>;
-    using MF = Mfma<float>;
+    using St = Step<T>;
+    using Frag = typename St::frag;
+    constexpr int NB = Cfg::NB, NKK = Cfg::NKK, KS = Cfg::KS, ES = Cfg::ES;
     extern __shared__ __align__(16) unsigned char smem[];
-    T* sK = reinterpret_cast<T*>(smem + Cfg::OFF_K);
-    float* sT = reinterpret_cast<float*>(smem + Cfg::OFF_K);
-    float* sA = reinterpret_cast<float*>(smem + Cfg::OFF_A);
-    float* sg = reinterpret_cast<float*>(smem + Cfg::OFF_G);
-    float* sb = reinterpret_cast<float*>(smem + Cfg::OFF_B);
-
-    const int tid = threadIdx.x, l = lane_id(), w = wave_id();
-    const int64_t rs_k = (int64_t)H * DK * Cfg::ES;
-
-    // this lane's K loads: slot s = tid + kThreads j is row s / KB, block s % KB
-    uint32_t koff[Cfg::NL];
-    int kdst[Cfg::NL];
-#pragma unroll
-    for (int j = 0; j < Cfg::NL; ++j) {
-        const int s = tid + kThreads * j, r = s / Cfg::KB, b = s - r * Cfg::KB;
-        const bool ok = r < C;
-        koff[j] = ok ? (uint32_t)(r * rs_k + b * 16) : kOutOfRange;
-        kdst[j] = ok ? (r * Cfg::KP + (b ^ swz<Cfg::KSW>(r))) * 16 : -1;
-    }
-    auto kidx = [](int r, int c) __attribute__((always_inline)) {
-        return (r * Cfg::KP + ((c / Cfg::EV) ^ swz<Cfg::KSW>(r))) * Cfg::EV + (c % Cfg::EV);
-    };
+    const int l = lane_id(), w = wave_id();
+    const int n = l & 15, g = l >> 4;
+    unsigned char* wl = smem + w * Cfg::WAVE_LDS;
+    float* sg = reinterpret_cast<float*>(wl + Cfg::OFF_G);
+    float* sb = reinterpret_cast<float*>(wl + Cfg::OFF_B);
+    float* sAd = reinterpret_cast<float*>(wl + Cfg::OFF_AD);   // [b][col][row]
+    float* sTd = reinterpret_cast<float*>(wl + Cfg::OFF_TD);   // [b][col][row]
+    const int64_t rs_k = (int64_t)H * DK * ES;
+    const int stride = (int)gridDim.x * Cfg::WAVES;
 
     // keys and gates of unit u into registers (rows past the chunk end read as 0)
-    u32x4 kv[Cfg::NL];
     float la_n = 0.f, be_n = 0.f;
     ChunkInfo ci_n{};
-    auto fetch = [&](int u) __attribute__((always_inline)) {
+    auto fetch = [&](Frag (*dst)[NKK], int u) __attribute__((always_inline)) {
         const int slot = u / H, h = u - slot * H;
         ci_n = chunk_info(geom, slot);
         const int len = ci_n.len;
         const int64_t row0 = (int64_t)ci_n.t0 * H + h;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + row0 * DK, len > 0 ? (len - 1) * rs_k + DK * Cfg::ES : 0);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + row0 * DK, len > 0 ? (len - 1) * rs_k + DK * ES : 0);
 #pragma unroll
-        for (int j = 0; j < Cfg::NL; ++j) kv[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[j], 0, 0);
-        if (w == 0) {   // wave 0 takes the gates: lane l holds token l's
-            const int64_t gbytes = len > 0 ? ((int64_t)(len - 1) * H + 1) * 4 : 0;
-            const uint32_t goff = l < C ? (uint32_t)(l * H * 4) : kOutOfRange;
-            be_n = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(beta + row0, gbytes),
-                                                                                  goff, 0, 0));
-            la_n = log_alpha ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                   make_rsrc(log_alpha + row0, gbytes), goff, 0, 0))
-                             : 0.f;
-        }
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
+                dst[b][kk] = __builtin_bit_cast(
+                    Frag, __builtin_amdgcn_raw_buffer_load_b128(
+                              rk, (uint32_t)((b * 16 + n) * rs_k) + kk * KS * ES + g * 16, 0, 0));
+        const int64_t gbytes = len > 0 ? ((int64_t)(len - 1) * H + 1) * 4 : 0;
+        const uint32_t goff = l < C ? (uint32_t)(l * H * 4) : kOutOfRange;
+        be_n = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(beta + row0, gbytes), goff, 0, 0));
+        la_n = log_alpha ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                               make_rsrc(log_alpha + row0, gbytes), goff, 0, 0))
+                         : 0.f;
     };
 
-    int u = blockIdx.x;
-    if (u < units) fetch(u);
-    for (; u < units; u += gridDim.x) {
+    // one unit whose keys are in cur (and whose gates and geometry fetch left in
+    // la_n, be_n, ci_n); starts the loads of unit u + stride into nxt
+    auto process = [&](int u, Frag (*cur)[NKK], Frag (*nxt)[NKK]) __attribute__((always_inline)) {
+        if constexpr (!Cfg::PREFETCH) fetch(cur, u);
         const ChunkInfo ci = ci_n;
-        const int slot = u / H, h = u - slot * H;
-        const int64_t unit = (int64_t)slot * H + h;
-        // this unit's keys into LDS and its gates into registers, then start the next unit's loads
-#pragma unroll
-        for (int j = 0; j < Cfg::NL; ++j)
-            if (kdst[j] >= 0) *reinterpret_cast<u32x4*>(smem + Cfg::OFF_K + kdst[j]) = kv[j];
         float la = la_n;
         const float be = be_n;
-        if (u + (int)gridDim.x < units) fetch(u + gridDim.x);
-        if (ci.len <= 0) continue;   // unused packed-batch slot (uniform)
-
-        // gates: inclusive prefix sum of log alpha inside the chunk (wave 0)
-        if (w == 0) {
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(la, off, 64);
-                if (l >= off) la += y;
-            }
-            const float glast = __shfl(la, C - 1, 64);
-            if (l < C) {
-                sg[l] = la;
-                sb[l] = be;
-                float* gout = g_ws + unit * 3 * C;
-                gout[l] = la;                            // g_i
-                gout[C + l] = __expf(la);                // gamma_i = exp(g_i)
-                gout[2 * C + l] = __expf(glast - la);    // gamma_n / gamma_i
-            }
+        if constexpr (Cfg::PREFETCH) {
+            if (u + stride < units) fetch(nxt, u + stride);
         }
-        __syncthreads();
+        if (ci.len <= 0) return;   // unused packed-batch slot (uniform)
+        const int slot = u / H, h = u - slot * H;
+        const int64_t unit = (int64_t)slot * H + h;
 
-        // A = strict_lower(diag(beta) (K K^T o Gamma)) on MFMA: lower tile t = w, w + 4, ...
-        for (int t = w; t < Cfg::NT; t += kThreads / 64) {
-            const int ti = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-            const int tj = t - ti * (ti + 1) / 2;
-            f32x4 acc = zero4();
+        // gates: inclusive prefix sum of log alpha inside the chunk (lane = token)
 #pragma unroll
-            for (int kk = 0; kk < DK; kk += M::KS) {
-                const int c = kk + (l >> 4) * M::KPL;
-                typename M::frag a, b;
-                if constexpr (M::KPL == 8) {
-                    a = *reinterpret_cast<const bf16x8*>(sK + kidx(ti * 16 + (l & 15), c));
-                    b = *reinterpret_cast<const bf16x8*>(sK + kidx(tj * 16 + (l & 15), c));
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(la, off, 64);
+            if (l >= off) la += y;
+        }
+        const float glast = __shfl(la, C - 1, 64);
+        if (l < C) {
+            sg[l] = la;
+            sb[l] = be;
+            float* gout = g_ws + unit * 3 * C;
+            gout[l] = la;                            // g_i
+            gout[C + l] = __expf(la);                // gamma_i = exp(g_i)
+            gout[2 * C + l] = __expf(glast - la);    // gamma_n / gamma_i
+        }
+        wave_lds_sync();
+
+        // A = strict_lower(diag(beta) (K K^T o Gamma)).  Tile (i, m), m < i, in A
+        // operand layout: lane (g, n) holds A[16i + n][16m + 4g + r]; the product
+        // K_m K_i^T puts exactly those entries of K K^T in the lane.  Diagonal
+        // tiles in accumulator layout -- lane (g, n) holds A[16b + 4g + r][16b + n]
+        // (K K^T is symmetric) -- go to LDS as the columns of the block.
+        f32x4 A[NB][NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int row = 16 * i + n;
+            const float gr = sg[row], br = sb[row];
+#pragma unroll
+            for (int m = 0; m <= i; ++m) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) acc = St::mma(cur[m][kk], cur[i][kk], acc);
+                const int c0 = 16 * m + 4 * g;
+                const float4 gc = *reinterpret_cast<const float4*>(sg + c0);
+                if (m < i) {
+                    A[i][m][0] = br * acc[0] * __expf(gr - gc.x);
+                    A[i][m][1] = br * acc[1] * __expf(gr - gc.y);
+                    A[i][m][2] = br * acc[2] * __expf(gr - gc.z);
+                    A[i][m][3] = br * acc[3] * __expf(gr - gc.w);
                 } else {
-                    a = sK[kidx(ti * 16 + (l & 15), c)];
-                    b = sK[kidx(tj * 16 + (l & 15), c)];
+                    // rows c0 + r, column row: A = beta_rows S exp(g_rows - g_col) below the diagonal
+                    const float4 bc = *reinterpret_cast<const float4*>(sb + c0);
+                    f32x4 d;
+                    d[0] = c0 + 0 > row ? bc.x * acc[0] * __expf(gc.x - gr) : 0.f;
+                    d[1] = c0 + 1 > row ? bc.y * acc[1] * __expf(gc.y - gr) : 0.f;
+                    d[2] = c0 + 2 > row ? bc.z * acc[2] * __expf(gc.z - gr) : 0.f;
+                    d[3] = c0 + 3 > row ? bc.w * acc[3] * __expf(gc.w - gr) : 0.f;
+                    *reinterpret_cast<f32x4*>(sAd + i * 256 + n * 16 + 4 * g) = d;   // column n, rows 4g..
                 }
-                acc = M::mma(a, b, acc);
             }
-            const int j = tj * 16 + (l & 15), i0 = ti * 16 + 4 * (l >> 4);
-            const float gj = sg[j];
-            const float4 gi = *reinterpret_cast<const float4*>(sg + i0);
-            const float4 bi = *reinterpret_cast<const float4*>(sb + i0);
-            sA[(i0 + 0) * Cfg::LDA + j] = (j < i0 + 0) ? bi.x * acc[0] * __expf(gi.x - gj) : 0.f;
-            sA[(i0 + 1) * Cfg::LDA + j] = (j < i0 + 1) ? bi.y * acc[1] * __expf(gi.y - gj) : 0.f;
-            sA[(i0 + 2) * Cfg::LDA + j] = (j < i0 + 2) ? bi.z * acc[2] * __expf(gi.z - gj) : 0.f;
-            sA[(i0 + 3) * Cfg::LDA + j] = (j < i0 + 3) ? bi.w * acc[3] * __expf(gi.w - gj) : 0.f;
         }
-        __syncthreads();
+        wave_lds_sync();
 
-        // T = (I + A)^-1, blocked by 16 rows.  Diagonal blocks by forward
-        // substitution (wave 0, lane = 16 b + column); then, one block diagonal
-        // at a time, T_ij = -T_ii (sum_{j<=m<i} A_im T_mj) on fp32 MFMA.
-        if (w == 0 && l < C) {
-            const int b = l >> 4, c = l & 15;
+        // diagonal blocks of T = (I + A)^-1: lane (b, c) solves (I + A_bb) x = e_c
+        // right-looking -- once x_j is known, it leaves the rows below -- so the
+        // dependent chain is one FMA per row
+        if (g < NB) {
+            const float* ab = sAd + g * 256;   // column j of the block at ab + 16 j
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float* arow = sA + (16 * b + i) * Cfg::LDA + 16 * b;
-                float acc = (i == c) ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = i == n ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < i; ++j) acc -= arow[j] * x[j];
-                x[i] = acc;
+            for (int j = 0; j < 15; ++j) {
+                const float xj = x[j];
+#pragma unroll
+                for (int i4 = (j + 1) / 4; i4 < 4; ++i4) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(ab + j * 16 + 4 * i4);
+                    if (4 * i4 + 0 > j) x[4 * i4 + 0] -= a4.x * xj;
+                    if (4 * i4 + 1 > j) x[4 * i4 + 1] -= a4.y * xj;
+                    if (4 * i4 + 2 > j) x[4 * i4 + 2] -= a4.z * xj;
+                    if (4 * i4 + 3 > j) x[4 * i4 + 3] -= a4.w * xj;
+                }
             }
+            float* tc = sTd + g * 256 + n * 16;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sT[(16 * b + i) * Cfg::LDA + 16 * b + c] = x[i];
+            for (int i4 = 0; i4 < 4; ++i4)
+                *reinterpret_cast<f32x4*>(tc + 4 * i4) = f32x4{x[4 * i4], x[4 * i4 + 1], x[4 * i4 + 2], x[4 * i4 + 3]};
         }
-        __syncthreads();
+        wave_lds_sync();   // the columns of T, and the columns of A read above, are settled
+        // the diagonal blocks of T as B operands (T_bb[4g + r][n]) and as A
+        // operands (T_bb[n][4g + r], also the row layout of the output)
+        f32x4 Tb_op[NB], Ta_op[NB];
 #pragma unroll
-        for (int d = 1; d < Cfg::NB; ++d) {
-            const int j = w, i = w + d;          // wave w builds block (j + d, j)
-            if (w < Cfg::NB - d) {
-                // R = sum_m A_im T_mj (accumulator layout), then T_ij = -T_ii R with R
-                // as the B operand straight from the accumulators
-                f32x4 acc = zero4();
-                for (int kk = 16 * j; kk < 16 * i; kk += MF::KS)
-                    acc = MF::mma(frag_kc(sA, Cfg::LDA, 16 * i, kk), frag_ks(sT, Cfg::LDA, kk, 16 * j), acc);
-                const f32x4 tii = *reinterpret_cast<const f32x4*>(sT + (16 * i + (l & 15)) * Cfg::LDA + 16 * i +
-                                                                   4 * (l >> 4));
-                const f32x4 tij = mma16_f32(tii, acc, zero4());
+        for (int b = 0; b < NB; ++b) {
+            Tb_op[b] = *reinterpret_cast<const f32x4*>(sTd + b * 256 + n * 16 + 4 * g);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sT[(16 * i + 4 * (l >> 4) + r) * Cfg::LDA + 16 * j + (l & 15)] = -tij[r];
+            for (int r = 0; r < 4; ++r) Ta_op[b][r] = sTd[b * 256 + (4 * g + r) * 16 + n];
+        }
+        // blocks below the diagonal, one block diagonal at a time.  To: accumulator
+        // layout (T[16i + 4g + r][16j + n]) for the blocks later levels take as B
+        // operands; Tr: row layout (T[16i + n][16j + 4g + r]), from
+        // T_ij^T = -R^T T_ii^T, for the output
+        f32x4 To[NB][NB], Tr[NB][NB];
+#pragma unroll
+        for (int d = 1; d < NB; ++d)
+#pragma unroll
+            for (int j = 0; j + d < NB; ++j) {
+                const int i = j + d;
+                f32x4 R = zero4();
+#pragma unroll
+                for (int m = j; m < i; ++m) R = mma16_f32(A[i][m], m == j ? Tb_op[j] : To[m][j], R);
+                if (i < NB - 1) To[i][j] = -mma16_f32(Ta_op[i], R, zero4());
+                Tr[i][j] = -mma16_f32(R, Ta_op[i], zero4());
             }
-            __syncthreads();
-        }
 
-        // Tb = T diag(beta), zero above the diagonal; 16-byte stores.  fp32 rows are
-        // plain; a bf16 row stores each 32-column group as the 4-column runs
-        // (0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31), so that the 16 bytes at
-        // group offset 8g are the operand of a 16-deep block pair (4g .. 4g+3 of both).
-        // Blocks above the diagonal block are not computed (masked); inside a
-        // diagonal block the substitution leaves exact zeros above the diagonal.
-        static_assert(sizeof(T) == 4 || C % 32 == 0, "bf16 Tb groups of 32 columns");
-        constexpr int EV = Cfg::EV, VPR = C / EV;
+        // Tb = T diag(beta), zero above the diagonal, straight from the row
+        // layout: lane (g, n) stores row 16 ti + n.  fp32 rows are plain (16 bytes
+        // = columns 16 tj + 4g ..); a bf16 row stores each 32-column group as the
+        // 4-column runs (0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31), so the
+        // 16 bytes at group offset 8g -- columns 4g.. of both 16-column tiles of
+        // the group -- are the operand of a 16-deep block pair.
         T* out = Tb_ws + unit * C * C;
-        for (int idx = tid; idx < C * VPR; idx += kThreads) {
-            const int i = idx / VPR, c0 = (idx - i * VPR) * EV;
-            if constexpr (sizeof(T) == 4) {
-                const bool keep = (c0 >> 4) <= (i >> 4);
-                const f32x4 t4 = *reinterpret_cast<const f32x4*>(sT + i * Cfg::LDA + c0);
-                const float4 b4 = *reinterpret_cast<const float4*>(sb + c0);
-                const f32x4 o = keep ? f32x4{t4[0] * b4.x, t4[1] * b4.y, t4[2] * b4.z, t4[3] * b4.w} : zero4();
-                *reinterpret_cast<f32x4*>(out + i * C + c0) = o;
+        auto trow = [&](int ti, int tj) __attribute__((always_inline)) {
+            const f32x4 t = tj < ti ? Tr[ti][tj] : tj == ti ? Ta_op[ti] : zero4();
+            const float4 b4 = *reinterpret_cast<const float4*>(sb + 16 * tj + 4 * g);
+            return f32x4{t[0] * b4.x, t[1] * b4.y, t[2] * b4.z, t[3] * b4.w};
+        };
+#pragma unroll
+        for (int ti = 0; ti < NB; ++ti) {
+            T* orow = out + (16 * ti + n) * C;
+            if constexpr (Cfg::BF) {
+#pragma unroll
+                for (int q = 0; q < NB / 2; ++q) {
+                    const f32x4 t0 = trow(ti, 2 * q), t1 = trow(ti, 2 * q + 1);
+                    const bf16x8 o = {(bf16)t0[0], (bf16)t0[1], (bf16)t0[2], (bf16)t0[3],
+                                      (bf16)t1[0], (bf16)t1[1], (bf16)t1[2], (bf16)t1[3]};
+                    *reinterpret_cast<bf16x8*>(orow + 32 * q + 8 * g) = o;
+                }
             } else {
-                const int lc = (c0 & ~31) + ((c0 & 31) >> 1);   // logical columns lc .. lc+3, lc+16 .. lc+19
-                const bool keep0 = (lc >> 4) <= (i >> 4), keep1 = ((lc + 16) >> 4) <= (i >> 4);
-                const f32x4 t0 = *reinterpret_cast<const f32x4*>(sT + i * Cfg::LDA + lc);
-                const f32x4 t1 = *reinterpret_cast<const f32x4*>(sT + i * Cfg::LDA + lc + 16);
-                const float4 b0 = *reinterpret_cast<const float4*>(sb + lc);
-                const float4 b1 = *reinterpret_cast<const float4*>(sb + lc + 16);
-                bf16x8 o;
-                o[0] = (bf16)(keep0 ? t0[0] * b0.x : 0.f);
-                o[1] = (bf16)(keep0 ? t0[1] * b0.y : 0.f);
-                o[2] = (bf16)(keep0 ? t0[2] * b0.z : 0.f);
-                o[3] = (bf16)(keep0 ? t0[3] * b0.w : 0.f);
-                o[4] = (bf16)(keep1 ? t1[0] * b1.x : 0.f);
-                o[5] = (bf16)(keep1 ? t1[1] * b1.y : 0.f);
-                o[6] = (bf16)(keep1 ? t1[2] * b1.z : 0.f);
-                o[7] = (bf16)(keep1 ? t1[3] * b1.w : 0.f);
-                *reinterpret_cast<bf16x8*>(out + i * C + c0) = o;
+#pragma unroll
+                for (int tj = 0; tj < NB; ++tj) *reinterpret_cast<f32x4*>(orow + 16 * tj + 4 * g) = trow(ti, tj);
             }
         }
-        __syncthreads();   // the next unit's keys overwrite T
+        wave_lds_sync();   // before the next unit overwrites what was read
+    };
+
+    int u = blockIdx.x * Cfg::WAVES + w;
+    if constexpr (Cfg::PREFETCH) {
+        Frag ka[NB][NKK], kb[NB][NKK];
+        if (u < units) fetch(ka, u);
+        for (; u < units; u += 2 * stride) {
+            process(u, ka, kb);
+            if (u + stride < units) process(u + stride, kb, ka);
+        }
+    } else {
+        Frag ka[NB][NKK];
+        for (; u < units; u += stride) process(u, ka, ka);
     }
 }
 

@@ -66,28 +66,6 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
 }
 
-// One 16-byte step of a contraction along the rows of two row-major operands:
-// lane (g, n) holds elements [k0 + g*EV, k0 + (g+1)*EV) of row n (EV = 16 / sizeof(T)).
-// bf16: one 16x16x32 MFMA; fp32: four 16x16x4 MFMAs, step r contracting
-// k0 + 4g + r (the same assignment on both operands).
-template <typename T> struct Step;
-template <> struct Step<bf16> {
-    static constexpr int KS = 32;
-    typedef bf16x8 frag;
-    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-};
-template <> struct Step<float> {
-    static constexpr int KS = 16;
-    typedef f32x4 frag;
-    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], c, 0, 0, 0);
-        return c;
-    }
-};
-
 // Operand of one 16-deep contraction block: lane (g, n) holds k = 4g .. 4g+3
 // for row / column n of the other dimension.  A 16x16 accumulator tile has
 // exactly this layout, with k = its row.

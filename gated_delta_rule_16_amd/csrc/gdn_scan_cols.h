@@ -44,10 +44,10 @@ struct ColCfg {
     static constexpr int ES = sizeof(T);
     static constexpr int NW = C / 16;                      // 16-token blocks of a chunk
     static constexpr int NVW = DVT / 16;                   // column waves
-    static constexpr int NPW = 4;                          // helper waves: all stage,
-    static constexpr int NPP = 2;                          // the first NPP also form P
-    static constexpr int NWG = NVW + NPW, NTHR = NWG * 64;
-    static constexpr int NF = NPW;                         // staging waves: the helpers
+    static constexpr int NPW = 4;                          // helper waves: the first NPP
+    static constexpr int NPP = 2;                          // form P, the others stage the
+    static constexpr int NWG = NVW + NPW, NTHR = NWG * 64; // chunks and write out O
+    static constexpr int NF = NPW - NPP;                   // staging waves
     static constexpr int EV = 16 / ES;                     // elements per 16 bytes
     // staged rows: bf16 unpadded with XOR swizzles (K and Q: kind 1; V: kind 2
     // for rows of 4+ blocks; Tb: kind 3), fp32 padded by one block
@@ -58,25 +58,20 @@ struct ColCfg {
     static constexpr int NDB = DK / 16;                    // state tiles per column wave
     static constexpr int NP = (NW + 1) / 2;                // pairs of token blocks
     static constexpr int KS = Step<T>::KS, NKK = DK / KS;  // contraction steps over d
-    // staging buffer: regions K | Q | Tb | V slice | gates, whole 1 KB blocks;
-    // batch j holds blocks j*NF .. j*NF + NF - 1, block j*NF + f filled by
-    // helper wave f (one 16-byte load per lane); regions start on batch
-    // boundaries except the gates, which follow V in its last batch when they fit
+    // staging buffer: regions K | Q | Tb | V slice | gates, in whole 1 KB
+    // blocks, each one direct-to-LDS load of 16 bytes per lane; block i is
+    // loaded by staging wave i % NF, as its load i / NF
     static constexpr int blocks(int bytes) { return (bytes + 1023) / 1024; }
     static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
     static constexpr int NIK = blocks(C * LDK * ES), NIV = blocks(C * LDV * ES);
     static constexpr int NIT = blocks(C * LDC * ES), NIG = blocks(3 * C * 4);
-    static constexpr bool VG1 = NIV + NIG <= NF;
-    static constexpr int NBK = cdiv(NIK, NF), NBT = cdiv(NIT, NF);
-    static constexpr int NBVG = VG1 ? 1 : cdiv(NIV, NF) + cdiv(NIG, NF);
-    static constexpr int NL = 2 * NBK + NBT + NBVG;        // staging loads per lane per chunk
-    static constexpr int NSET = 2;                         // chunks in flight per helper lane
-    static constexpr int JQ = NBK, JT = 2 * NBK, JV = JT + NBT;
-    static constexpr int JG = VG1 ? JV : JV + cdiv(NIV, NF);
-    static constexpr int BG0 = VG1 ? JV * NF + NIV : JG * NF;
-    static constexpr size_t SZ_STAGE = (size_t)NL * NF * 1024;
-    static constexpr size_t OFF_Q = (size_t)JQ * NF * 1024, OFF_T = (size_t)JT * NF * 1024;
-    static constexpr size_t OFF_V = (size_t)JV * NF * 1024, OFF_G = (size_t)BG0 * 1024;
+    static constexpr int BQ = NIK, BT = 2 * NIK, BV = BT + NIT, BG = BV + NIV, NI = BG + NIG;
+    static constexpr int NL = cdiv(NI, NF);                // loads per helper lane per chunk
+    // loads staging wave f issues per chunk
+    static constexpr int nload(int f) { return NI / NF + (f < NI % NF ? 1 : 0); }
+    static constexpr size_t SZ_STAGE = (size_t)NI * 1024;
+    static constexpr size_t OFF_Q = (size_t)BQ * 1024, OFF_T = (size_t)BT * 1024;
+    static constexpr size_t OFF_V = (size_t)BV * 1024, OFF_G = (size_t)BG * 1024;
     // P^T tiles of a chunk in MFMA operand order: 1 KB slots of 16 bytes per
     // lane; bf16 one slot per pair of key blocks (the lane's 4 values of block
     // 2p, then those of 2p + 1), fp32 one per key block; query block qb starts
@@ -87,15 +82,18 @@ struct ColCfg {
         return s;
     }
     static constexpr size_t SZ_P = (size_t)prow(NW) * 1024;
-    static constexpr size_t OFF_P = 2 * SZ_STAGE;
     // the chunk's output slice, handed from the column waves to the helpers,
     // which write it out as whole 16-byte pieces of its rows: rows of DVT values
     // padded by 16 bytes; two buffers (chunk parity)
     static constexpr int LDO = DVT * ES + 16;                  // row pitch (bytes)
     static constexpr int OPR = DVT * ES / 16;                  // 16-byte pieces per row
-    static constexpr int NOPL = cdiv(C * OPR, NPW * 64);       // pieces per helper lane
+    static constexpr int NOPL = cdiv(C * OPR, NF * 64);        // pieces per staging lane
     static constexpr size_t SZ_O = (size_t)C * LDO;
-    static constexpr size_t OFF_O = OFF_P + 2 * SZ_P;
+    // staging buffers: three (loads run two chunks ahead) where they fit, else two
+    static constexpr size_t SZ_REST = 2 * SZ_P + 2 * SZ_O;
+    static constexpr int NSTG = 3 * SZ_STAGE + SZ_REST <= 160 * 1024 ? 3 : 2;
+    static constexpr int DIST = NSTG - 1;                  // chunks staged ahead
+    static constexpr size_t OFF_PB = NSTG * SZ_STAGE, OFF_O = OFF_PB + 2 * SZ_P;
     static constexpr size_t SMEM = OFF_O + 2 * SZ_O;
     static constexpr bool FITS = SMEM <= 160 * 1024;
     // P helper of query block qb: 0 takes blocks 0 and NW - 1, 1 the middle ones
@@ -113,19 +111,14 @@ __device__ __forceinline__ constexpr int drow(int i, int rho) {
     else return 16 * i + rho;
 }
 
-// region of staging batch j for helper wave f: 0 K, 1 Q, 2 Tb, 3 V, 4 gates, 5 padding
+// region of staging load j of helper wave f: 0 K, 1 Q, 2 Tb, 3 V, 4 gates, 5 none
 template <typename Cfg>
-__device__ __forceinline__ int col_region(int j, int f) {
-    if (j < Cfg::JQ) return 0;
-    if (j < Cfg::JT) return 1;
-    if (j < Cfg::JV) return 2;
+__device__ __forceinline__ constexpr int col_region(int j, int f) {
     const int i = j * Cfg::NF + f;
-    if (i < Cfg::JV * Cfg::NF + Cfg::NIV) return 3;
-    if (i >= Cfg::BG0 && i < Cfg::BG0 + Cfg::NIG) return 4;
-    return 5;
+    return i < Cfg::BQ ? 0 : i < Cfg::BT ? 1 : i < Cfg::BV ? 2 : i < Cfg::BG ? 3 : i < Cfg::NI ? 4 : 5;
 }
 // byte offset, relative to the chunk's first row, of lane l's 16 bytes of
-// staging batch j for helper wave f (kOutOfRange for padding)
+// staging load j of helper wave f (kOutOfRange for padding)
 template <typename Cfg>
 __device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_t rs_k, int64_t rs_v) {
     constexpr int C = Cfg::NW * 16;
@@ -142,11 +135,11 @@ __device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_
     };
     switch (col_region<Cfg>(j, f)) {
         case 0: off = region(i * 64 + l, Cfg::KP, Cfg::KB, Cfg::KSW, rs_k); break;
-        case 1: off = region((i - Cfg::JQ * Cfg::NF) * 64 + l, Cfg::KP, Cfg::KB, Cfg::KSW, rs_k); break;
-        case 2: off = region((i - Cfg::JT * Cfg::NF) * 64 + l, Cfg::TP, Cfg::TB, Cfg::TSW, (int64_t)C * Cfg::ES); break;
-        case 3: off = region((i - Cfg::JV * Cfg::NF) * 64 + l, Cfg::VP, Cfg::VB, Cfg::VSW, rs_v); break;
+        case 1: off = region((i - Cfg::BQ) * 64 + l, Cfg::KP, Cfg::KB, Cfg::KSW, rs_k); break;
+        case 2: off = region((i - Cfg::BT) * 64 + l, Cfg::TP, Cfg::TB, Cfg::TSW, (int64_t)C * Cfg::ES); break;
+        case 3: off = region((i - Cfg::BV) * 64 + l, Cfg::VP, Cfg::VB, Cfg::VSW, rs_v); break;
         case 4: {
-            const int s = (i - Cfg::BG0) * 64 + l;
+            const int s = (i - Cfg::BG) * 64 + l;
             off = s < 3 * C / 4 ? (int64_t)s * 16 : -1;
             break;
         }
@@ -239,7 +232,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         const float *g, *gam, *dec;
     };
     auto staged = [&](int cc) __attribute__((always_inline)) {
-        const unsigned char* sb = smem + (cc & 1) * Cfg::SZ_STAGE;
+        const unsigned char* sb = smem + (cc % Cfg::NSTG) * Cfg::SZ_STAGE;
         Staged st;
         st.K = reinterpret_cast<const T*>(sb);
         st.Q = reinterpret_cast<const T*>(sb + Cfg::OFF_Q);
@@ -252,7 +245,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
     };
     // P^T slots of chunk cd
     auto pbuf = [&](int cd) __attribute__((always_inline)) {
-        return reinterpret_cast<T*>(smem + Cfg::OFF_P + (cd & 1) * Cfg::SZ_P);
+        return reinterpret_cast<T*>(smem + Cfg::OFF_PB + (cd & 1) * Cfg::SZ_P);
     };
     // output slice of chunk cd
     auto obuf = [&](int cd) __attribute__((always_inline)) { return smem + Cfg::OFF_O + (cd & 1) * Cfg::SZ_O; };
@@ -461,18 +454,24 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         }
     };
 
-    // ---- helper wave hw: stages its share of each chunk; helpers hw < NPP also
-    // form P^T = ((Q K^T) o Gamma o M)^T (rows: key tokens) for their query
-    // blocks, decayed and masked, into the P^T slots of the chunk
+    // ---- helper wave hw: helpers hw < NPP form P^T = ((Q K^T) o Gamma o M)^T
+    // (rows: key tokens) for their query blocks, decayed and masked, into the
+    // P^T slots of the chunk; staging wave f = hw - NPP loads its share of each
+    // chunk and writes out its share of each output slice.  (A wave that reads
+    // LDS after issuing direct-to-LDS loads may be made to wait for them by the
+    // compiler, hence the split.)
     auto run_help = [&](auto hw_const) __attribute__((always_inline)) {
         constexpr int hw = decltype(hw_const)::value;
-        // staging: chunk cd's K, Q, Tb, V slice and gates into registers (rows
-        // past the chunk end fall outside the buffer ranges and read as zeros),
-        // then into the staging buffer of its parity
+        constexpr bool STAGER = hw >= Cfg::NPP;
+        constexpr int f = STAGER ? hw - Cfg::NPP : 0;
+        // staging: chunk cd's K, Q, Tb, V slice and gates straight into the
+        // staging buffer of cd % NSTG (rows past the chunk end fall outside the
+        // buffer ranges and land as zeros); ND loads per call
+        constexpr int ND = STAGER ? Cfg::nload(f) : 0;
         uint32_t soff[Cfg::NL];
 #pragma unroll
-        for (int j = 0; j < Cfg::NL; ++j) soff[j] = col_stage_offset<Cfg>(j, hw, l, rs_k, rs_v);
-        auto stage_load = [&](u32x4* R, int cd) __attribute__((always_inline)) {
+        for (int j = 0; j < Cfg::NL; ++j) soff[j] = col_stage_offset<Cfg>(j, f, l, rs_k, rs_v);
+        auto stage = [&](int cd) __attribute__((always_inline)) {
             const int t0 = ts + cd * C, len = min(C, te - t0);
             const int64_t unit = (int64_t)(first + cd) * H + h;
             const T* kb = k + ((int64_t)t0 * H + h) * DK;
@@ -481,26 +480,16 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             const T* tb = Tb_ws + unit * C * C;
             const float* gb = g_ws + unit * 3 * C;
             const int nk = (int)((len - 1) * rs_k + DK * ES), nv = (int)((len - 1) * rs_v + DVT * ES);
+            unsigned char* dst = smem + (cd % Cfg::NSTG) * Cfg::SZ_STAGE + f * 1024;
 #pragma unroll
             for (int j = 0; j < Cfg::NL; ++j) {
-                const void* base;
-                int nrec;
-                if (j < Cfg::JQ) { base = kb; nrec = nk; }
-                else if (j < Cfg::JT) { base = qb; nrec = nk; }
-                else if (j < Cfg::JV) { base = tb; nrec = C * C * ES; }
-                else {
-                    const int r = col_region<Cfg>(j, hw);
-                    base = r == 3 ? (const void*)vb_ : (const void*)gb;
-                    nrec = r == 3 ? nv : r == 4 ? 3 * C * 4 : 0;
-                }
-                R[j] = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(base, nrec), soff[j], 0, 0);
+                const int r = col_region<Cfg>(j, f);
+                if (r == 5) continue;
+                const void* base = r == 0 ? (const void*)kb : r == 1 ? (const void*)qb : r == 2 ? (const void*)tb
+                                 : r == 3 ? (const void*)vb_ : (const void*)gb;
+                const int nrec = r <= 1 ? nk : r == 2 ? C * C * ES : r == 3 ? nv : 3 * C * 4;
+                lds_load16(make_rsrc(base, nrec), dst + j * Cfg::NF * 1024, soff[j]);
             }
-        };
-        auto stage_store = [&](const u32x4* R, int cd) __attribute__((always_inline)) {
-            unsigned char* base = smem + (cd & 1) * Cfg::SZ_STAGE + (hw * 64 + l) * 16;
-#pragma unroll
-            for (int j = 0; j < Cfg::NL; ++j)
-                if (col_region<Cfg>(j, hw) != 5) *reinterpret_cast<u32x4*>(base + j * Cfg::NF * 1024) = R[j];
         };
         // chunk cd's output slice from LDS to memory, 16 bytes per lane, rows
         // past the chunk end dropped by the buffer range; streamed past the caches
@@ -511,32 +500,31 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             const unsigned char* ob = obuf(cd);
 #pragma unroll
             for (int j = 0; j < Cfg::NOPL; ++j) {
-                const int piece = (j * Cfg::NPW + hw) * 64 + l;
-                if (Cfg::NOPL * Cfg::NPW * 64 == C * Cfg::OPR || piece < C * Cfg::OPR) {
+                const int piece = (j * Cfg::NF + f) * 64 + l;
+                if (Cfg::NOPL * Cfg::NF * 64 == C * Cfg::OPR || piece < C * Cfg::OPR) {
                     const int r = piece / Cfg::OPR, b = piece - r * Cfg::OPR;
                     const u32x4 d = *reinterpret_cast<const u32x4*>(ob + r * Cfg::LDO + b * 16);
                     __builtin_amdgcn_raw_buffer_store_b128(d, ro, (uint32_t)(r * rs_v) + b * 16, 0, 2);
                 }
             }
         };
-        // NSET register sets take turns, chunk j in set j % NSET: step cc writes
-        // the one holding chunk cc + 1 to LDS as it starts (that buffer's readers
-        // are past the previous barrier) and refills it with chunk cc + 1 + NSET.
-        constexpr int NSET = Cfg::NSET;
-        u32x4 rs[NSET][Cfg::NL];
-        if (count > 0) {
+        // the loads of chunk cc + DIST go out as step cc starts, into the buffer
+        // whose readers passed the previous barrier; before its closing barrier
+        // step cc waits for all but the newest ND loads, i.e. for chunk cc + 1
+        // (loads complete in issue order)
+        static_assert(ND * (Cfg::DIST - 1) < 64, "vmcnt range");
+        if (STAGER && count > 0) {
 #pragma unroll
-            for (int j = 0; j < NSET; ++j) stage_load(rs[j], min(j, count - 1));
-            stage_store(rs[0], 0);
-            stage_load(rs[0], min(NSET, count - 1));
+            for (int d = 0; d < Cfg::DIST; ++d) stage(min(d, count - 1));
+            wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
         }
         __syncthreads();
 
-        auto step = [&](const int cc, u32x4* rnext) __attribute__((always_inline)) {
-            stage_store(rnext, cc + 1);
-            stage_load(rnext, min(cc + 1 + NSET, count - 1));   // past the end: re-read, unused
-            if (cc >= 2) write_out(cc - 2);                      // left by the column waves last step
-            if constexpr (hw < Cfg::NPP) {
+        auto step = [&](const int cc) __attribute__((always_inline)) {
+            if constexpr (STAGER) {
+                if (cc >= 2) write_out(cc - 2);                  // left by the column waves last step
+                stage(min(cc + Cfg::DIST, count - 1));           // past the end: re-read, unused
+            } else {
                 const Staged st = staged(cc);
                 T* pb = pbuf(cc) + l * (16 / ES);
                 f32x4 Pt[NW][NW];
@@ -589,22 +577,16 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                     }
                 }
             }
-            wait_vm_lgkm0<63>();
+            wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
             barrier();
         };
-        // unrolled over the register sets and the two staging buffers
-        constexpr int UN = NSET % 2 ? 2 * NSET : NSET;
-        int cc = 0;
-        for (; cc + UN <= count; cc += UN) {
-#pragma unroll
-            for (int i = 0; i < UN; ++i) step(cc + i, rs[(i + 1) % NSET]);
-        }
-#pragma unroll
-        for (int i = 0; i < UN - 1; ++i)
-            if (cc + i < count) step(cc + i, rs[(i + 1) % NSET]);
+        for (int cc = 0; cc < count; ++cc) step(cc);
+        wait_vm_lgkm0<0>();   // no load still writing LDS when the workgroup ends
         __syncthreads();   // the column waves have left the last output slice
-        if (count >= 2) write_out(count - 2);
-        if (count >= 1) write_out(count - 1);
+        if constexpr (STAGER) {
+            if (count >= 2) write_out(count - 2);
+            if (count >= 1) write_out(count - 1);
+        }
     };
 
     if (w < NVW) {

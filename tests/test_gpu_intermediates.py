@@ -35,7 +35,8 @@ def chunk_algebra(K, V, beta, la):
     return g, T @ np.diag(beta)
 
 
-@pytest.mark.parametrize("dtype,Dk,Dv,C,tol", [("f32", 64, 64, 64, 1e-5), ("bf16", 128, 128, 64, 2e-2)])
+@pytest.mark.parametrize("dtype,Dk,Dv,C,tol", [("f32", 64, 64, 64, 1e-5), ("f32", 128, 128, 64, 1e-5),
+                                                ("f32", 16, 16, 16, 1e-5), ("bf16", 128, 128, 64, 2e-2)])
 def test_prep_intermediates(dtype, Dk, Dv, C, tol):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
