@@ -49,11 +49,13 @@ struct ColCfg {
     static constexpr int NWG = NVW + NPW, NTHR = NWG * 64; // chunks and write out O
     static constexpr int NF = NPW - NPP;                   // staging waves
     static constexpr int EV = 16 / ES;                     // elements per 16 bytes
-    // staged rows: bf16 unpadded with XOR swizzles (K and Q: kind 1; V: kind 2
-    // for rows of 4+ blocks; Tb: kind 3), fp32 padded by one block
+    // staged rows: bf16 unpadded with XOR swizzles (K and Q: kind 4 for rows of
+    // 16+ blocks, else 1; V: kind 5 for rows of 4 blocks, 2 for longer ones;
+    // Tb: kind 3), fp32 padded by one block
     static constexpr int KB = DK / EV, VB = DVT / EV, TB = C / EV;
     static constexpr int KP = BF ? KB : KB + 1, VP = BF ? VB : VB + 1, TP = BF ? TB : TB + 1;
-    static constexpr int KSW = BF ? 1 : 0, VSW = BF && VB >= 4 ? 2 : 0, TSW = BF ? 3 : 0;
+    static constexpr int KSW = BF ? (KB >= 16 ? 4 : 1) : 0, TSW = BF ? 3 : 0;
+    static constexpr int VSW = BF && VB == 4 ? 5 : BF && VB > 4 ? 2 : 0;
     static constexpr int LDK = KP * EV, LDV = VP * EV, LDC = TP * EV;
     static constexpr int NDB = DK / 16;                    // state tiles per column wave
     static constexpr int NP = (NW + 1) / 2;                // pairs of token blocks
@@ -131,6 +133,8 @@ __device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_
         if (W == 1) x ^= swz<1>(r);
         else if (W == 2) x ^= swz<2>(r);
         else if (W == 3) x ^= swz<3>(r);
+        else if (W == 4) x ^= swz<4>(r);
+        else if (W == 5) x ^= swz<5>(r);
         return r * row_bytes + (int64_t)(x * 16);
     };
     switch (col_region<Cfg>(j, f)) {
