@@ -130,6 +130,36 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
                          : 0.f;
     };
 
+    // With the next unit's keys prefetched, a unit's results are held in
+    // registers and stored as the next unit starts, next to that prefetch: the
+    // wait for a unit's keys then finds the previous unit's stores long done
+    // (the compiler waits for all vector memory operations of a wave at once
+    // when loads and stores are both outstanding).
+    typedef typename std::conditional<Cfg::BF, bf16x8, f32x4>::type HFrag;
+    constexpr int NHQ = Cfg::BF ? NB / 2 : NB;
+    HFrag hold[NB][NHQ];
+    float hold_g[3] = {0.f, 0.f, 0.f};
+    T* hold_out = nullptr;
+    float* hold_gout = nullptr;
+    auto flush_hold = [&]() __attribute__((always_inline)) {
+        if (hold_out) {
+#pragma unroll
+            for (int ti = 0; ti < NB; ++ti) {
+                T* orow = hold_out + (16 * ti + n) * C;
+#pragma unroll
+                for (int q = 0; q < NHQ; ++q) {
+                    if constexpr (Cfg::BF) *reinterpret_cast<bf16x8*>(orow + 32 * q + 8 * g) = hold[ti][q];
+                    else *reinterpret_cast<f32x4*>(orow + 16 * q + 4 * g) = hold[ti][q];
+                }
+            }
+            if (l < C) {
+                hold_gout[l] = hold_g[0];
+                hold_gout[C + l] = hold_g[1];
+                hold_gout[2 * C + l] = hold_g[2];
+            }
+        }
+    };
+
     // one unit whose keys are in cur (and whose gates and geometry fetch left in
     // la_n, be_n, ci_n); starts the loads of unit u + stride into nxt
     auto process = [&](int u, Frag (*cur)[NKK], Frag (*nxt)[NKK]) __attribute__((always_inline)) {
@@ -139,6 +169,8 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
         const float be = be_n;
         if constexpr (Cfg::PREFETCH) {
             if (u + stride < units) fetch(nxt, u + stride);
+            flush_hold();
+            hold_out = nullptr;
         }
         if (ci.len <= 0) return;   // unused packed-batch slot (uniform)
         const int slot = u / H, h = u - slot * H;
@@ -154,10 +186,19 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
         if (l < C) {
             sg[l] = la;
             sb[l] = be;
+        }
+        {
+            // g_i, gamma_i = exp(g_i), gamma_n / gamma_i
             float* gout = g_ws + unit * 3 * C;
-            gout[l] = la;                            // g_i
-            gout[C + l] = __expf(la);                // gamma_i = exp(g_i)
-            gout[2 * C + l] = __expf(glast - la);    // gamma_n / gamma_i
+            const float g3[3] = {la, __expf(la), __expf(glast - la)};
+            if constexpr (Cfg::PREFETCH) {
+                hold_gout = gout;
+                hold_g[0] = g3[0], hold_g[1] = g3[1], hold_g[2] = g3[2];
+            } else if (l < C) {
+                gout[l] = g3[0];
+                gout[C + l] = g3[1];
+                gout[2 * C + l] = g3[2];
+            }
         }
         wave_lds_sync();
 
@@ -264,19 +305,22 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
 #pragma unroll
         for (int ti = 0; ti < NB; ++ti) {
             T* orow = out + (16 * ti + n) * C;
-            if constexpr (Cfg::BF) {
 #pragma unroll
-                for (int q = 0; q < NB / 2; ++q) {
+            for (int q = 0; q < NHQ; ++q) {
+                HFrag o;
+                if constexpr (Cfg::BF) {
                     const f32x4 t0 = trow(ti, 2 * q), t1 = trow(ti, 2 * q + 1);
-                    const bf16x8 o = {(bf16)t0[0], (bf16)t0[1], (bf16)t0[2], (bf16)t0[3],
-                                      (bf16)t1[0], (bf16)t1[1], (bf16)t1[2], (bf16)t1[3]};
-                    *reinterpret_cast<bf16x8*>(orow + 32 * q + 8 * g) = o;
+                    o = bf16x8{(bf16)t0[0], (bf16)t0[1], (bf16)t0[2], (bf16)t0[3],
+                               (bf16)t1[0], (bf16)t1[1], (bf16)t1[2], (bf16)t1[3]};
+                } else {
+                    o = trow(ti, q);
                 }
-            } else {
-#pragma unroll
-                for (int tj = 0; tj < NB; ++tj) *reinterpret_cast<f32x4*>(orow + 16 * tj + 4 * g) = trow(ti, tj);
+                if constexpr (Cfg::PREFETCH) hold[ti][q] = o;
+                else if constexpr (Cfg::BF) *reinterpret_cast<bf16x8*>(orow + 32 * q + 8 * g) = o;
+                else *reinterpret_cast<f32x4*>(orow + 16 * q + 4 * g) = o;
             }
         }
+        if constexpr (Cfg::PREFETCH) hold_out = out;
         wave_lds_sync();   // before the next unit overwrites what was read
     };
 
@@ -288,6 +332,7 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
             process(u, ka, kb);
             if (u + stride < units) process(u + stride, kb, ka);
         }
+        flush_hold();
     } else {
         Frag ka[NB][NKK];
         for (; u < units; u += stride) process(u, ka, ka);

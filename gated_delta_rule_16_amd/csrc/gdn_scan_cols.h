@@ -11,20 +11,22 @@
 //
 // Work split.  A workgroup owns a DVT-column slice of one (sequence, head):
 //  - column waves (DVT / 16): wave vb holds all Dk rows of columns vb*16 ..
-//    vb*16 + 15 of S^T in MFMA accumulators, so that Y, X, V', the state update
-//    and the output of its columns never leave the wave -- the recurrence has no
-//    synchronisation inside a chunk;
-//  - four helper waves stage the next chunks (K, Q, Tb, the V slice, gates)
-//    through registers into a double-buffered LDS area, and the first two of
-//    them compute P for the chunk (query blocks split between them) and leave
-//    its decayed, masked tiles in LDS.
-// With waves dealt to the four SIMDs in turn, the column waves and the P
-// helpers get a SIMD each and the staging-only helpers share the column
-// waves' SIMDs.
-// One barrier per chunk.  A column wave forms the output of chunk cc - 1 during
-// step cc, when the helpers' P^T tiles of that chunk are published, and leaves
-// it in LDS; the helpers write it out in step cc + 1 as 16-byte pieces of its
-// rows (the slice's rows are 2 DVT bytes long in memory).
+//    vb*16 + 15 of S^T in MFMA accumulators and runs the recurrence alone --
+//    Y, X, V' and the state update never leave the wave, so there is no
+//    synchronisation inside a chunk.  At the end of a chunk it leaves V' and
+//    the new state (as MFMA operands in the input dtype) in LDS;
+//  - two output helpers, each owning half of the chunk's query blocks, form
+//    P^T = ((Q K^T) o Gamma o M)^T and Z^T = S Q^T for them in registers (Q
+//    comes straight from memory into registers, three chunks ahead), and one step
+//    later, when V' of that chunk is published, the output
+//    O^T = Z^T diag(gamma) + V'^T P^T, which they leave in LDS;
+//  - two staging waves: one loads the chunks (K, Tb, the V slice, gates)
+//    straight into LDS up to three chunks ahead, the other writes the output slices
+//    out as whole 16-byte pieces of their rows (apart, so that the loader's
+//    wait for its loads does not also wait for stores).
+// With waves dealt to the four SIMDs in turn, the column waves and the output
+// helpers get a SIMD each; the staging waves, which issue little, share the
+// column waves' SIMDs.  One barrier per chunk.
 //
 // State tile layout.  Column wave vb keeps Dk / 16 tiles; lane (g, n) of tile i
 // holds S^T[drow(i, 4g + r)][vb*16 + n], r = 0..3.  bf16: tile 2m + h covers
@@ -45,13 +47,14 @@ struct ColCfg {
     static constexpr int NW = C / 16;                      // 16-token blocks of a chunk
     static constexpr int NVW = DVT / 16;                   // column waves
     static constexpr int NPW = 4;                          // helper waves: the first NPP
-    static constexpr int NPP = 2;                          // form P, the others stage the
-    static constexpr int NWG = NVW + NPW, NTHR = NWG * 64; // chunks and write out O
-    static constexpr int NF = NPW - NPP;                   // staging waves
+    static constexpr int NPP = 2;                          // form the output, the others
+    static constexpr int NWG = NVW + NPW, NTHR = NWG * 64; // stage chunks and write out O
+    static constexpr int NF = NPW - NPP;                   // staging waves: NLD load
+    static constexpr int NLD = NF - 1;                     // chunks, the last writes out O
     static constexpr int EV = 16 / ES;                     // elements per 16 bytes
-    // staged rows: bf16 unpadded with XOR swizzles (K and Q: kind 4 for rows of
-    // 16+ blocks, else 1; V: kind 5 for rows of 4 blocks, 2 for longer ones;
-    // Tb: kind 3), fp32 padded by one block
+    // staged rows: bf16 unpadded with XOR swizzles (K: kind 4 for rows of 16+
+    // blocks, else 1; V: kind 5 for rows of 4 blocks, 2 for longer ones; Tb:
+    // kind 3), fp32 padded by one block
     static constexpr int KB = DK / EV, VB = DVT / EV, TB = C / EV;
     static constexpr int KP = BF ? KB : KB + 1, VP = BF ? VB : VB + 1, TP = BF ? TB : TB + 1;
     static constexpr int KSW = BF ? (KB >= 16 ? 4 : 1) : 0, TSW = BF ? 3 : 0;
@@ -60,46 +63,54 @@ struct ColCfg {
     static constexpr int NDB = DK / 16;                    // state tiles per column wave
     static constexpr int NP = (NW + 1) / 2;                // pairs of token blocks
     static constexpr int KS = Step<T>::KS, NKK = DK / KS;  // contraction steps over d
-    // staging buffer: regions K | Q | Tb | V slice | gates, in whole 1 KB
-    // blocks, each one direct-to-LDS load of 16 bytes per lane; block i is
-    // loaded by staging wave i % NF, as its load i / NF
+    // staging buffer: regions K | Tb | V slice | gates, in whole 1 KB blocks,
+    // each one direct-to-LDS load of 16 bytes per lane; block i is loaded by
+    // loading wave i % NLD, as its load i / NLD
     static constexpr int blocks(int bytes) { return (bytes + 1023) / 1024; }
     static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
     static constexpr int NIK = blocks(C * LDK * ES), NIV = blocks(C * LDV * ES);
     static constexpr int NIT = blocks(C * LDC * ES), NIG = blocks(3 * C * 4);
-    static constexpr int BQ = NIK, BT = 2 * NIK, BV = BT + NIT, BG = BV + NIV, NI = BG + NIG;
-    static constexpr int NL = cdiv(NI, NF);                // loads per helper lane per chunk
-    // loads staging wave f issues per chunk
-    static constexpr int nload(int f) { return NI / NF + (f < NI % NF ? 1 : 0); }
+    static constexpr int BT = NIK, BV = BT + NIT, BG = BV + NIV, NI = BG + NIG;
+    static constexpr int NL = cdiv(NI, NLD);               // loads per loading lane per chunk
+    // loads loading wave f issues per chunk
+    static constexpr int nload(int f) { return NI / NLD + (f < NI % NLD ? 1 : 0); }
     static constexpr size_t SZ_STAGE = (size_t)NI * 1024;
-    static constexpr size_t OFF_Q = (size_t)BQ * 1024, OFF_T = (size_t)BT * 1024;
-    static constexpr size_t OFF_V = (size_t)BV * 1024, OFF_G = (size_t)BG * 1024;
-    // P^T tiles of a chunk in MFMA operand order: 1 KB slots of 16 bytes per
-    // lane; bf16 one slot per pair of key blocks (the lane's 4 values of block
-    // 2p, then those of 2p + 1), fp32 one per key block; query block qb starts
-    // at slot prow(qb); two buffers (chunk parity)
-    static constexpr int prow(int qb) {
-        int s = 0;
-        for (int c = 0; c < qb; ++c) s += BF ? c / 2 + 1 : c + 1;
-        return s;
-    }
-    static constexpr size_t SZ_P = (size_t)prow(NW) * 1024;
-    // the chunk's output slice, handed from the column waves to the helpers,
-    // which write it out as whole 16-byte pieces of its rows: rows of DVT values
-    // padded by 16 bytes; two buffers (chunk parity)
+    static constexpr size_t OFF_T = (size_t)BT * 1024, OFF_V = (size_t)BV * 1024, OFF_G = (size_t)BG * 1024;
+    // column-wave hand-over, lane by lane in MFMA operand form (one tile is 64
+    // lanes of 4 values): the state at the next chunk's start (NDB tiles per
+    // column wave) and V' (NW tiles per column wave); two buffers each (chunk
+    // parity)
+    static constexpr int TILE = 64 * 4 * ES;
+    static constexpr size_t SZ_SB = (size_t)NVW * NDB * TILE, SZ_VO = (size_t)NVW * NW * TILE;
+    // the chunk's output slice, handed from the output helpers to the staging
+    // waves: rows of DVT values padded by 16 bytes; two buffers (chunk parity)
     static constexpr int LDO = DVT * ES + 16;                  // row pitch (bytes)
     static constexpr int OPR = DVT * ES / 16;                  // 16-byte pieces per row
-    static constexpr int NOPL = cdiv(C * OPR, NF * 64);        // pieces per staging lane
+    static constexpr int NOPL = cdiv(C * OPR, 64);             // pieces per writing lane
     static constexpr size_t SZ_O = (size_t)C * LDO;
-    // staging buffers: three (loads run two chunks ahead) where they fit, else two
-    static constexpr size_t SZ_REST = 2 * SZ_P + 2 * SZ_O;
-    static constexpr int NSTG = 3 * SZ_STAGE + SZ_REST <= 160 * 1024 ? 3 : 2;
+    // staging buffers: as many as fit, up to four (loads run NSTG - 1 chunks ahead)
+    static constexpr size_t SZ_REST = 2 * SZ_SB + 2 * SZ_VO + 2 * SZ_O;
+    static constexpr int NSTG = 4 * SZ_STAGE + SZ_REST <= 160 * 1024 ? 4 : 3 * SZ_STAGE + SZ_REST <= 160 * 1024 ? 3 : 2;
     static constexpr int DIST = NSTG - 1;                  // chunks staged ahead
-    static constexpr size_t OFF_PB = NSTG * SZ_STAGE, OFF_O = OFF_PB + 2 * SZ_P;
+    static constexpr size_t OFF_SB = NSTG * SZ_STAGE, OFF_VO = OFF_SB + 2 * SZ_SB;
+    static constexpr size_t OFF_O = OFF_VO + 2 * SZ_VO;
     static constexpr size_t SMEM = OFF_O + 2 * SZ_O;
     static constexpr bool FITS = SMEM <= 160 * 1024;
-    // P helper of query block qb: 0 takes blocks 0 and NW - 1, 1 the middle ones
+    // output helper of query block qb: 0 takes blocks 0 and NW - 1, 1 the middle ones
     static constexpr int pwave(int qb) { return (qb < NW - 1 - qb ? qb : NW - 1 - qb) % NPP; }
+    // the query blocks of helper hw, and how many
+    static constexpr int nmine(int hw) {
+        int c = 0;
+        for (int qb = 0; qb < NW; ++qb) c += pwave(qb) == hw;
+        return c;
+    }
+    static constexpr int mine(int hw, int j) {
+        for (int qb = 0; qb < NW; ++qb)
+            if (pwave(qb) == hw && j-- == 0) return qb;
+        return 0;
+    }
+    static constexpr int NQB = (NW + 1) / 2;               // query blocks per helper, at most
+    static constexpr int NQS = 3;                          // Q register sets: chunks loaded ahead
     static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && NVW <= 2, "tile counts");
     static_assert(DV % DVT == 0 && DVT % 16 == 0 && DK % KS == 0 && DK % 16 == 0, "tile shapes");
     static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && (VB % 4 == 0 || VB == 2) && TB % 8 == 0 && DK % 32 == 0),
@@ -113,18 +124,18 @@ __device__ __forceinline__ constexpr int drow(int i, int rho) {
     else return 16 * i + rho;
 }
 
-// region of staging load j of helper wave f: 0 K, 1 Q, 2 Tb, 3 V, 4 gates, 5 none
+// region of staging load j of loading wave f: 0 K, 2 Tb, 3 V, 4 gates, 5 none
 template <typename Cfg>
 __device__ __forceinline__ constexpr int col_region(int j, int f) {
-    const int i = j * Cfg::NF + f;
-    return i < Cfg::BQ ? 0 : i < Cfg::BT ? 1 : i < Cfg::BV ? 2 : i < Cfg::BG ? 3 : i < Cfg::NI ? 4 : 5;
+    const int i = j * Cfg::NLD + f;
+    return i < Cfg::BT ? 0 : i < Cfg::BV ? 2 : i < Cfg::BG ? 3 : i < Cfg::NI ? 4 : 5;
 }
 // byte offset, relative to the chunk's first row, of lane l's 16 bytes of
-// staging load j of helper wave f (kOutOfRange for padding)
+// staging load j of loading wave f (kOutOfRange for padding)
 template <typename Cfg>
 __device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_t rs_k, int64_t rs_v) {
     constexpr int C = Cfg::NW * 16;
-    const int i = j * Cfg::NF + f;
+    const int i = j * Cfg::NLD + f;
     int64_t off = -1;
     auto region = [&](int s, int P, int B, int W, int64_t row_bytes) {
         const int r = s / P, p = s - r * P;
@@ -139,7 +150,6 @@ __device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_
     };
     switch (col_region<Cfg>(j, f)) {
         case 0: off = region(i * 64 + l, Cfg::KP, Cfg::KB, Cfg::KSW, rs_k); break;
-        case 1: off = region((i - Cfg::BQ) * 64 + l, Cfg::KP, Cfg::KB, Cfg::KSW, rs_k); break;
         case 2: off = region((i - Cfg::BT) * 64 + l, Cfg::TP, Cfg::TB, Cfg::TSW, (int64_t)C * Cfg::ES); break;
         case 3: off = region((i - Cfg::BV) * 64 + l, Cfg::VP, Cfg::VB, Cfg::VSW, rs_v); break;
         case 4: {
@@ -152,7 +162,7 @@ __device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_
     return (off < 0 || off >= (int64_t)kOutOfRange) ? kOutOfRange : (uint32_t)off;
 }
 
-// element (r, c) of the staged K / Q (swizzled 16-byte blocks)
+// element (r, c) of the staged K (swizzled 16-byte blocks)
 template <typename Cfg>
 __device__ __forceinline__ int ckidx(int r, int c) { return sidx<Cfg, Cfg::KP, Cfg::KSW>(r, c); }
 
@@ -232,14 +242,13 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         asm volatile("" ::: "memory");
     };
     struct Staged {
-        const T *K, *Q, *V, *Tb;
+        const T *K, *V, *Tb;
         const float *g, *gam, *dec;
     };
     auto staged = [&](int cc) __attribute__((always_inline)) {
         const unsigned char* sb = smem + (cc % Cfg::NSTG) * Cfg::SZ_STAGE;
         Staged st;
         st.K = reinterpret_cast<const T*>(sb);
-        st.Q = reinterpret_cast<const T*>(sb + Cfg::OFF_Q);
         st.V = reinterpret_cast<const T*>(sb + Cfg::OFF_V);
         st.Tb = reinterpret_cast<const T*>(sb + Cfg::OFF_T);
         st.g = reinterpret_cast<const float*>(sb + Cfg::OFF_G);
@@ -247,9 +256,12 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         st.dec = st.g + 2 * C;
         return st;
     };
-    // P^T slots of chunk cd
-    auto pbuf = [&](int cd) __attribute__((always_inline)) {
-        return reinterpret_cast<T*>(smem + Cfg::OFF_PB + (cd & 1) * Cfg::SZ_P);
+    // hand-over tiles: tile i of column wave vb, this lane's 4 values
+    auto sb_tile = [&](int cd, int vb, int i) __attribute__((always_inline)) {
+        return reinterpret_cast<Op*>(smem + Cfg::OFF_SB + (cd & 1) * Cfg::SZ_SB + (vb * NDB + i) * Cfg::TILE) + l;
+    };
+    auto vo_tile = [&](int cd, int vb, int jb) __attribute__((always_inline)) {
+        return reinterpret_cast<Op*>(smem + Cfg::OFF_VO + (cd & 1) * Cfg::SZ_VO + (vb * NW + jb) * Cfg::TILE) + l;
     };
     // output slice of chunk cd
     auto obuf = [&](int cd) __attribute__((always_inline)) { return smem + Cfg::OFF_O + (cd & 1) * Cfg::SZ_O; };
@@ -262,127 +274,64 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
 #pragma unroll
         for (int i = 0; i < NDB; ++i)
             St[i] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (int64_t)vcol * DK + drow<Cfg>(i, g4)) : zero4();
+        // the state slice as MFMA operands (input dtype), for this wave's Y and
+        // for the output helpers' Z^T of chunk 0
+        Op Sb[NDB];
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) {
+            Sb[i] = KO::tile(St[i]);
+            *sb_tile(0, vb, i) = Sb[i];
+        }
         __syncthreads();
 
-        // Z^T (scaled) and V' (operand form) of the chunk whose output is pending
-        f32x4 Zp[NW];
-        Op Vo[NW];
-        // P^T operands of one query block: bf16 pairs of key blocks, fp32 blocks
-        constexpr int NPQ = Cfg::BF ? NP : NW;
-        typedef typename std::conditional<Cfg::BF, s16x8, f32x4>::type PFrag;
-        auto load_p = [&](PFrag (*pf)[NPQ], int cd) __attribute__((always_inline)) {
-            const T* pb = pbuf(cd) + l * (16 / ES);
-#pragma unroll
-            for (int qb = 0; qb < NW; ++qb)
-#pragma unroll
-                for (int p = 0; p < NPQ; ++p)
-                    if ((Cfg::BF ? 2 * p : p) <= qb)
-                        pf[qb][p] = *reinterpret_cast<const PFrag*>(pb + (Cfg::prow(qb) + p) * 64 * (16 / ES));
-        };
-        // O^T = Z^T + V'^T P^T of chunk cd for every query block qb (A: the V'
-        // tiles as V'^T; B: the P^T tiles); lane (g, n) leaves
-        // O[token qb*16 + n][vb*16 + 4g .. + 3] in the chunk's output slice
-        auto output = [&](const PFrag (*pf)[NPQ], int cd) __attribute__((always_inline)) {
-            unsigned char* ob = obuf(cd) + n * Cfg::LDO + (vb * 16 + g4) * ES;
-#pragma unroll
-            for (int qb = 0; qb < NW; ++qb) {
-                f32x4 acc = Zp[qb];
-                if constexpr (Cfg::BF) {
-#pragma unroll
-                    for (int p = 0; p <= qb / 2; ++p)
-                        acc = KO::mma2(Vo[2 * p], Vo[2 * p + 1], __builtin_shufflevector(pf[qb][p], pf[qb][p], 0, 1, 2, 3),
-                                       __builtin_shufflevector(pf[qb][p], pf[qb][p], 4, 5, 6, 7), acc);
-                } else {
-#pragma unroll
-                    for (int jb = 0; jb <= qb; ++jb) acc = KO::mma1(Vo[jb], pf[qb][jb], acc);
-                }
-                store4(reinterpret_cast<T*>(ob + qb * 16 * Cfg::LDO), acc[0], acc[1], acc[2], acc[3]);
-            }
-        };
-
-        // One chunk.  LDS operands are requested a group of MFMAs ahead of their
-        // use (scheduling fences keep the compiler from pulling the requests next
-        // to their uses); the previous chunk's output goes out after the first
-        // group, which frees its registers for the later requests.
+        // One chunk.  All K fragments of Y and the chunk's Tb rows, gates and V
+        // values are requested as it starts, the K^T operands of the state
+        // update right after the Y instructions.
         auto step = [&](const int cc) __attribute__((always_inline)) {
             const Staged st = staged(cc);
-            PFrag pf[NW][NPQ];
-            if (cc > 0) load_p(pf, cc - 1);   // published by the last barrier
-
-            // the state slice as MFMA operands (input dtype)
-            Op Sb[NDB];
+            Frag fk[NKK][NW];
 #pragma unroll
-            for (int i = 0; i < NDB; ++i) Sb[i] = KO::tile(St[i]);
-            // Y = K S^T (A: K rows; B: the state tiles) and Z^T = S Q^T (A: the
-            // state tiles as S; B: Q rows) for every token block
-            f32x4 Y[NW], Z[NW];
+            for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-            for (int tb = 0; tb < NW; ++tb) Y[tb] = Z[tb] = zero4();
-            Frag fk[2][NW], fq[2][NW];
-#pragma unroll
-            for (int tb = 0; tb < NW; ++tb) {
-                fk[0][tb] = kfrag_rows<Cfg>(st.K, tb * 16, 0);
-                fq[0][tb] = kfrag_rows<Cfg>(st.Q, tb * 16, 0);
-            }
-            // the gates and the Tb rows, requested with the last K / Q group
+                for (int tb = 0; tb < NW; ++tb) fk[kk][tb] = kfrag_rows<Cfg>(st.K, tb * 16, kk * KS);
             float4 gam4[NW], dec4[NW];
-            float gamq[NW], gamma_n;
+            float gamma_n;
             f32x4 vv[NW];
             typedef typename std::conditional<Cfg::BF, bf16x8, f32x4>::type TFrag;
             constexpr int NTP = Cfg::BF ? NP : NW;
             TFrag ta[NW][NTP];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const int cur = kk & 1;
-                if (kk + 1 < NKK) {
+            for (int tb = 0; tb < NW; ++tb) {
+                gam4[tb] = *reinterpret_cast<const float4*>(st.gam + tb * 16 + g4);
+                dec4[tb] = *reinterpret_cast<const float4*>(st.dec + tb * 16 + g4);
+                vv[tb] = vcol4<Cfg>(st.V, tb, vb);
+            }
+            gamma_n = st.gam[C - 1];
 #pragma unroll
-                    for (int tb = 0; tb < NW; ++tb) {
-                        fk[cur ^ 1][tb] = kfrag_rows<Cfg>(st.K, tb * 16, (kk + 1) * KS);
-                        fq[cur ^ 1][tb] = kfrag_rows<Cfg>(st.Q, tb * 16, (kk + 1) * KS);
+            for (int ib = 0; ib < NW; ++ib)
+#pragma unroll
+                for (int p = 0; p < NTP; ++p) {
+                    if constexpr (Cfg::BF) {
+                        if (2 * p <= ib)
+                            ta[ib][p] = *reinterpret_cast<const bf16x8*>(st.Tb + tidx<Cfg>(ib * 16 + n, 32 * p + 2 * g4));
+                    } else {
+                        if (p <= ib)
+                            ta[ib][p] = *reinterpret_cast<const f32x4*>(st.Tb + tidx<Cfg>(ib * 16 + n, 16 * p + g4));
                     }
-                } else {
-#pragma unroll
-                    for (int tb = 0; tb < NW; ++tb) {
-                        gam4[tb] = *reinterpret_cast<const float4*>(st.gam + tb * 16 + g4);
-                        dec4[tb] = *reinterpret_cast<const float4*>(st.dec + tb * 16 + g4);
-                        gamq[tb] = st.gam[tb * 16 + n];
-                        vv[tb] = vcol4<Cfg>(st.V, tb, vb);
-                    }
-                    gamma_n = st.gam[C - 1];
-#pragma unroll
-                    for (int ib = 0; ib < NW; ++ib)
-#pragma unroll
-                        for (int p = 0; p < NTP; ++p) {
-                            if constexpr (Cfg::BF) {
-                                if (2 * p <= ib)
-                                    ta[ib][p] = *reinterpret_cast<const bf16x8*>(st.Tb + tidx<Cfg>(ib * 16 + n, 32 * p + 2 * g4));
-                            } else {
-                                if (p <= ib)
-                                    ta[ib][p] = *reinterpret_cast<const f32x4*>(st.Tb + tidx<Cfg>(ib * 16 + n, 16 * p + g4));
-                            }
-                        }
                 }
-                __builtin_amdgcn_sched_barrier(0);
+            // Y = K S^T (A: K rows; B: the state tiles) for every token block
+            f32x4 Y[NW];
+#pragma unroll
+            for (int tb = 0; tb < NW; ++tb) Y[tb] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
                 for (int tb = 0; tb < NW; ++tb) {
-                    if constexpr (Cfg::BF) {
-                        const s16x8 qs = __builtin_bit_cast(s16x8, fq[cur][tb]);
-                        Y[tb] = KO::mma2p(fk[cur][tb], Sb[2 * kk], Sb[2 * kk + 1], Y[tb]);
-                        Z[tb] = KO::mma2(Sb[2 * kk], Sb[2 * kk + 1], __builtin_shufflevector(qs, qs, 0, 1, 2, 3),
-                                         __builtin_shufflevector(qs, qs, 4, 5, 6, 7), Z[tb]);
-                    } else {
-                        Y[tb] = St16::mma(fk[cur][tb], Sb[kk], Y[tb]);
-                        Z[tb] = St16::mma(Sb[kk], fq[cur][tb], Z[tb]);
-                    }
+                    if constexpr (Cfg::BF) Y[tb] = KO::mma2p(fk[kk][tb], Sb[2 * kk], Sb[2 * kk + 1], Y[tb]);
+                    else Y[tb] = St16::mma(fk[kk][tb], Sb[kk], Y[tb]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                if (kk == 0 && cc > 0) {
-                    output(pf, cc - 1);   // its P^T tiles were published by the last barrier
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-
-            // K^T operands of the state update, requested now
+            __builtin_amdgcn_sched_barrier(0);
+            // K^T operands of the state update
             Op kt[NDB][NW];
 #pragma unroll
             for (int i = 0; i < NDB; ++i)
@@ -394,7 +343,6 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             for (int tb = 0; tb < NW; ++tb)
                 Xo[tb] = KO::tile(f32x4{vv[tb][0] - gam4[tb].x * Y[tb][0], vv[tb][1] - gam4[tb].y * Y[tb][1],
                                         vv[tb][2] - gam4[tb].z * Y[tb][2], vv[tb][3] - gam4[tb].w * Y[tb][3]});
-            __builtin_amdgcn_sched_barrier(0);
             // V' = Tb X (A: Tb rows, token pairs as X)
             f32x4 Vp[NW];
 #pragma unroll
@@ -419,6 +367,9 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             for (int jb = 0; jb < NW; ++jb)
                 Vd[jb] = KO::tile(f32x4{Vp[jb][0] * dec4[jb].x, Vp[jb][1] * dec4[jb].y, Vp[jb][2] * dec4[jb].z,
                                         Vp[jb][3] * dec4[jb].w});
+            // V' for the output helpers (A operand of O^T = V'^T P^T)
+#pragma unroll
+            for (int jb = 0; jb < NW; ++jb) *vo_tile(cc, vb, jb) = KO::tile(Vp[jb]);
 #pragma unroll
             for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -428,28 +379,17 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                     else
                         St[i] = KO::mma1(kt[i][2 * p], Vd[2 * p], St[i]);
                 }
-            // this chunk's Z^T (scaled by gamma) and V' for the next step's output
+            // the next chunk's state as operands, here and for the output helpers
 #pragma unroll
-            for (int qb = 0; qb < NW; ++qb) {
-                Zp[qb] = Z[qb] * gamq[qb];
-                Vo[qb] = KO::tile(Vp[qb]);
+            for (int i = 0; i < NDB; ++i) {
+                Sb[i] = KO::tile(St[i]);
+                *sb_tile(cc + 1, vb, i) = Sb[i];
             }
             wait_vm_lgkm0<63>();
             barrier();
         };
-        int cc = 0;
-        for (; cc + 2 <= count; cc += 2) {
-            step(cc);
-            step(cc + 1);
-        }
-        if (cc < count) step(cc);
-        if (count > 0) {   // the last chunk's P^T tiles were published by the last barrier
-            PFrag pf[NW][NPQ];
-            load_p(pf, count - 1);
-            output(pf, count - 1);
-        }
-        wait_vm_lgkm0<63>();
-        __syncthreads();   // the helpers write out the last output slices
+        for (int cc = 0; cc < count; ++cc) step(cc);
+        __syncthreads();   // the output helpers form the last output slice, the staging waves write it
 
         if (S_T) {
 #pragma unroll
@@ -458,20 +398,202 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         }
     };
 
-    // ---- helper wave hw: helpers hw < NPP form P^T = ((Q K^T) o Gamma o M)^T
-    // (rows: key tokens) for their query blocks, decayed and masked, into the
-    // P^T slots of the chunk; staging wave f = hw - NPP loads its share of each
-    // chunk and writes out its share of each output slice.  (A wave that reads
-    // LDS after issuing direct-to-LDS loads may be made to wait for them by the
-    // compiler, hence the split.)
-    auto run_help = [&](auto hw_const) __attribute__((always_inline)) {
+    // ---- output helper hw: P^T and Z^T of its query blocks for chunk cc in
+    // step cc (kept in registers), their output in step cc + 1
+    auto run_out = [&](auto hw_const) __attribute__((always_inline)) {
         constexpr int hw = decltype(hw_const)::value;
-        constexpr bool STAGER = hw >= Cfg::NPP;
-        constexpr int f = STAGER ? hw - Cfg::NPP : 0;
-        // staging: chunk cd's K, Q, Tb, V slice and gates straight into the
-        // staging buffer of cd % NSTG (rows past the chunk end fall outside the
-        // buffer ranges and land as zeros); ND loads per call
-        constexpr int ND = STAGER ? Cfg::nload(f) : 0;
+        constexpr int NM = Cfg::nmine(hw);
+        // Q rows of this helper's query blocks, straight into registers: lane
+        // (g, n) gets Q[qb*16 + n][kk*KS + g*EV ..] (rows past the chunk end
+        // read as zeros)
+        auto q_load = [&](Frag (*qf)[NKK], int cd) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const __amdgpu_buffer_rsrc_t rq =
+                make_rsrc(q + ((int64_t)t0 * H + h) * DK, (len - 1) * rs_k + DK * ES);
+#pragma unroll
+            for (int j = 0; j < NM; ++j)
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk)
+                    qf[j][kk] = __builtin_bit_cast(
+                        Frag, __builtin_amdgcn_raw_buffer_load_b128(
+                                  rq, (uint32_t)((Cfg::mine(hw, j) * 16 + n) * rs_k) + kk * KS * ES + (l >> 4) * 16, 0, 0));
+        };
+        // P^T pairs (bf16: key blocks 2p, 2p + 1 in one operand) or tiles, and
+        // Z^T diag(gamma) of the pending chunk
+        constexpr int NPQ = Cfg::BF ? NP : NW;
+        typedef typename std::conditional<Cfg::BF, s16x8, f32x4>::type PFrag;
+        PFrag pp[Cfg::NQB][NPQ];
+        f32x4 zp[Cfg::NQB][NVW];
+        // output of chunk cd (its V' published by the last barrier, read into vo)
+        auto out = [&](int cd, const Op (*vo)[NW]) __attribute__((always_inline)) {
+            unsigned char* ob = obuf(cd) + n * Cfg::LDO + g4 * ES;
+#pragma unroll
+            for (int vb = 0; vb < NVW; ++vb) {
+#pragma unroll
+                for (int j = 0; j < NM; ++j) {
+                    const int qb = Cfg::mine(hw, j);
+                    f32x4 acc = zp[j][vb];
+                    if constexpr (Cfg::BF) {
+#pragma unroll
+                        for (int p = 0; p < NP; ++p)
+                            if (2 * p <= qb)
+                                acc = KO::mma2(vo[vb][2 * p], vo[vb][2 * p + 1], __builtin_shufflevector(pp[j][p], pp[j][p], 0, 1, 2, 3),
+                                               __builtin_shufflevector(pp[j][p], pp[j][p], 4, 5, 6, 7), acc);
+                    } else {
+#pragma unroll
+                        for (int jb = 0; jb < NW; ++jb)
+                            if (jb <= qb) acc = KO::mma1(vo[vb][jb], pp[j][jb], acc);
+                    }
+                    store4(reinterpret_cast<T*>(ob + qb * 16 * Cfg::LDO + vb * 16 * ES), acc[0], acc[1], acc[2], acc[3]);
+                }
+            }
+        };
+        constexpr int QMAX = Cfg::mine(hw, NM - 1);   // the largest query block
+        auto step = [&](const int cc, Frag (*qcur)[NKK]) __attribute__((always_inline)) {
+            const Staged st = staged(cc);
+            // K fragments and state tiles of one contraction step, requested a
+            // step ahead of their use (two register sets)
+            Frag kf[2][NW];
+            Op sbk[2][NVW][2];
+            auto fetch = [&](int kk, int s) __attribute__((always_inline)) {
+#pragma unroll
+                for (int jb = 0; jb <= QMAX; ++jb) kf[s][jb] = kfrag_rows<Cfg>(st.K, jb * 16, kk * KS);
+#pragma unroll
+                for (int vb = 0; vb < NVW; ++vb) {
+                    sbk[s][vb][0] = *sb_tile(cc, vb, Cfg::BF ? 2 * kk : kk);
+                    if constexpr (Cfg::BF) sbk[s][vb][1] = *sb_tile(cc, vb, 2 * kk + 1);
+                }
+            };
+            // the first contraction step's operands and V' of the pending chunk
+            // (whose output goes out after the first step's instructions)
+            fetch(0, 0);
+            Op vo[NVW][NW];
+            if (cc > 0) {
+#pragma unroll
+                for (int vb = 0; vb < NVW; ++vb)
+#pragma unroll
+                    for (int jb = 0; jb < NW; ++jb) vo[vb][jb] = *vo_tile(cc - 1, vb, jb);
+            }
+            float gq[Cfg::NQB], gamq[Cfg::NQB];
+#pragma unroll
+            for (int j = 0; j < NM; ++j) {
+                gq[j] = st.g[Cfg::mine(hw, j) * 16 + n];
+                gamq[j] = st.gam[Cfg::mine(hw, j) * 16 + n];
+            }
+            // decay factors of the P^T tiles of key block jb (zero above the
+            // diagonal), formed between the instructions of a contraction step
+            f32x4 dfac[Cfg::NQB][NW];
+            auto decay = [&](int jb) __attribute__((always_inline)) {
+                const float4 gj = *reinterpret_cast<const float4*>(st.g + jb * 16 + g4);
+                const int j0 = jb * 16 + g4;
+#pragma unroll
+                for (int j = 0; j < NM; ++j) {
+                    const int cq = Cfg::mine(hw, j) * 16 + n;
+                    if (jb <= Cfg::mine(hw, j))
+                        dfac[j][jb] = f32x4{j0 + 0 <= cq ? __expf(gq[j] - gj.x) : 0.f, j0 + 1 <= cq ? __expf(gq[j] - gj.y) : 0.f,
+                                            j0 + 2 <= cq ? __expf(gq[j] - gj.z) : 0.f, j0 + 3 <= cq ? __expf(gq[j] - gj.w) : 0.f};
+                }
+            };
+            // P^T tiles (rows: key tokens) and Z^T (rows: state columns) of this
+            // helper's query blocks
+            f32x4 Pt[Cfg::NQB][NW], Zt[Cfg::NQB][NVW];
+#pragma unroll
+            for (int j = 0; j < Cfg::NQB; ++j) {
+#pragma unroll
+                for (int jb = 0; jb < NW; ++jb) Pt[j][jb] = zero4();
+#pragma unroll
+                for (int vb = 0; vb < NVW; ++vb) Zt[j][vb] = zero4();
+            }
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int s = kk & 1;
+                if (kk + 1 < NKK) fetch(kk + 1, s ^ 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < NM; ++j) {
+                    const int qb = Cfg::mine(hw, j);
+#pragma unroll
+                    for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] = St16::mma(kf[s][jb], qcur[j][kk], Pt[j][jb]);
+#pragma unroll
+                    for (int vb = 0; vb < NVW; ++vb) {
+                        if constexpr (Cfg::BF) {
+                            const s16x8 qs = __builtin_bit_cast(s16x8, qcur[j][kk]);
+                            Zt[j][vb] = KO::mma2(sbk[s][vb][0], sbk[s][vb][1], __builtin_shufflevector(qs, qs, 0, 1, 2, 3),
+                                                 __builtin_shufflevector(qs, qs, 4, 5, 6, 7), Zt[j][vb]);
+                        } else {
+                            Zt[j][vb] = St16::mma(sbk[s][vb][0], qcur[j][kk], Zt[j][vb]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int jb = kk; jb < NW; jb += NKK) decay(jb);
+                if (kk == NKK - 1) {
+#pragma unroll
+                    for (int jb = NKK; jb < NW; ++jb) decay(jb);
+                }
+                if (kk == 0 && cc > 0) out(cc - 1, vo);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // decay and mask P^T, scale Z^T by gamma at the query token; keep both
+#pragma unroll
+            for (int j = 0; j < NM; ++j) {
+                const int qb = Cfg::mine(hw, j);
+#pragma unroll
+                for (int vb = 0; vb < NVW; ++vb) zp[j][vb] = Zt[j][vb] * gamq[j];
+#pragma unroll
+                for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] *= dfac[j][jb];
+                if constexpr (Cfg::BF) {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+                        if (2 * p <= qb)
+                            pp[j][p] = __builtin_shufflevector(KO::tile(Pt[j][2 * p]),
+                                                               KO::tile(2 * p + 1 < NW ? Pt[j][2 * p + 1] : zero4()),
+                                                               0, 1, 2, 3, 4, 5, 6, 7);
+                } else {
+#pragma unroll
+                    for (int jb = 0; jb <= qb; ++jb) pp[j][jb] = Pt[j][jb];
+                }
+            }
+            q_load(qcur, min(cc + Cfg::NQS, count - 1));   // refill the set just used; past the end: re-read, unused
+            wait_vm_lgkm0<63>();
+            barrier();
+        };
+        constexpr int NQS = Cfg::NQS;
+        Frag qs[NQS][Cfg::NQB][NKK];
+        if (count > 0) {
+#pragma unroll
+            for (int d = 0; d < NQS; ++d) q_load(qs[d], min(d, count - 1));
+        }
+        __syncthreads();
+        int cc = 0;
+        for (; cc + NQS <= count; cc += NQS) {
+#pragma unroll
+            for (int i = 0; i < NQS; ++i) step(cc + i, qs[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NQS - 1; ++i)
+            if (cc + i < count) step(cc + i, qs[i]);
+        if (count > 0) {   // its V' was published by the last barrier
+            Op vo[NVW][NW];
+#pragma unroll
+            for (int vb = 0; vb < NVW; ++vb)
+#pragma unroll
+                for (int jb = 0; jb < NW; ++jb) vo[vb][jb] = *vo_tile(count - 1, vb, jb);
+            out(count - 1, vo);
+        }
+        __syncthreads();
+    };
+
+    // ---- staging waves: wave f < NF - 1 loads its share of each chunk (so that
+    // its vmcnt counts these loads alone), the last one writes out the output
+    // slices
+    auto run_stage = [&](auto f_const) __attribute__((always_inline)) {
+        constexpr int f = decltype(f_const)::value;
+        constexpr bool LOADER = f < Cfg::NLD;
+        // staging: chunk cd's K, Tb, V slice and gates straight into the staging
+        // buffer of cd % NSTG (rows past the chunk end fall outside the buffer
+        // ranges and land as zeros); ND loads per call
+        constexpr int ND = LOADER ? Cfg::nload(f) : 0;
         uint32_t soff[Cfg::NL];
 #pragma unroll
         for (int j = 0; j < Cfg::NL; ++j) soff[j] = col_stage_offset<Cfg>(j, f, l, rs_k, rs_v);
@@ -479,7 +601,6 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             const int t0 = ts + cd * C, len = min(C, te - t0);
             const int64_t unit = (int64_t)(first + cd) * H + h;
             const T* kb = k + ((int64_t)t0 * H + h) * DK;
-            const T* qb = q + ((int64_t)t0 * H + h) * DK;
             const T* vb_ = v + ((int64_t)t0 * H + h) * DV + v0;
             const T* tb = Tb_ws + unit * C * C;
             const float* gb = g_ws + unit * 3 * C;
@@ -489,10 +610,10 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             for (int j = 0; j < Cfg::NL; ++j) {
                 const int r = col_region<Cfg>(j, f);
                 if (r == 5) continue;
-                const void* base = r == 0 ? (const void*)kb : r == 1 ? (const void*)qb : r == 2 ? (const void*)tb
-                                 : r == 3 ? (const void*)vb_ : (const void*)gb;
-                const int nrec = r <= 1 ? nk : r == 2 ? C * C * ES : r == 3 ? nv : 3 * C * 4;
-                lds_load16(make_rsrc(base, nrec), dst + j * Cfg::NF * 1024, soff[j]);
+                const void* base = r == 0 ? (const void*)kb : r == 2 ? (const void*)tb : r == 3 ? (const void*)vb_
+                                 : (const void*)gb;
+                const int nrec = r == 0 ? nk : r == 2 ? C * C * ES : r == 3 ? nv : 3 * C * 4;
+                lds_load16(make_rsrc(base, nrec), dst + j * Cfg::NLD * 1024, soff[j]);
             }
         };
         // chunk cd's output slice from LDS to memory, 16 bytes per lane, rows
@@ -504,8 +625,8 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             const unsigned char* ob = obuf(cd);
 #pragma unroll
             for (int j = 0; j < Cfg::NOPL; ++j) {
-                const int piece = (j * Cfg::NF + f) * 64 + l;
-                if (Cfg::NOPL * Cfg::NF * 64 == C * Cfg::OPR || piece < C * Cfg::OPR) {
+                const int piece = j * 64 + l;
+                if (Cfg::NOPL * 64 == C * Cfg::OPR || piece < C * Cfg::OPR) {
                     const int r = piece / Cfg::OPR, b = piece - r * Cfg::OPR;
                     const u32x4 d = *reinterpret_cast<const u32x4*>(ob + r * Cfg::LDO + b * 16);
                     __builtin_amdgcn_raw_buffer_store_b128(d, ro, (uint32_t)(r * rs_v) + b * 16, 0, 2);
@@ -517,77 +638,25 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         // step cc waits for all but the newest ND loads, i.e. for chunk cc + 1
         // (loads complete in issue order)
         static_assert(ND * (Cfg::DIST - 1) < 64, "vmcnt range");
-        if (STAGER && count > 0) {
+        if (LOADER && count > 0) {
 #pragma unroll
             for (int d = 0; d < Cfg::DIST; ++d) stage(min(d, count - 1));
             wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
         }
         __syncthreads();
-
-        auto step = [&](const int cc) __attribute__((always_inline)) {
-            if constexpr (STAGER) {
-                if (cc >= 2) write_out(cc - 2);                  // left by the column waves last step
+        for (int cc = 0; cc < count; ++cc) {
+            if constexpr (LOADER) {
                 stage(min(cc + Cfg::DIST, count - 1));           // past the end: re-read, unused
+                wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
             } else {
-                const Staged st = staged(cc);
-                T* pb = pbuf(cc) + l * (16 / ES);
-                f32x4 Pt[NW][NW];
-#pragma unroll
-                for (int qb = 0; qb < NW; ++qb)
-#pragma unroll
-                    for (int jb = 0; jb < NW; ++jb) Pt[qb][jb] = zero4();
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    Frag kf[NW];
-#pragma unroll
-                    for (int jb = 0; jb < NW; ++jb) {
-                        bool need = false;
-#pragma unroll
-                        for (int qb = jb; qb < NW; ++qb) need = need || Cfg::pwave(qb) == hw;
-                        if (need) kf[jb] = kfrag_rows<Cfg>(st.K, jb * 16, kk * KS);
-                    }
-#pragma unroll
-                    for (int qb = 0; qb < NW; ++qb) {
-                        if (Cfg::pwave(qb) != hw) continue;
-                        const Frag aq = kfrag_rows<Cfg>(st.Q, qb * 16, kk * KS);
-#pragma unroll
-                        for (int jb = 0; jb <= qb; ++jb) Pt[qb][jb] = St16::mma(kf[jb], aq, Pt[qb][jb]);
-                    }
-                }
-#pragma unroll
-                for (int qb = 0; qb < NW; ++qb) {
-                    if (Cfg::pwave(qb) != hw) continue;
-                    const int cq = qb * 16 + n;
-                    const float gq = st.g[cq];
-#pragma unroll
-                    for (int jb = 0; jb <= qb; ++jb) {
-                        const float4 gj = *reinterpret_cast<const float4*>(st.g + jb * 16 + g4);
-                        const int j0 = jb * 16 + g4;
-                        f32x4& P = Pt[qb][jb];
-                        P[0] = j0 + 0 <= cq ? P[0] * __expf(gq - gj.x) : 0.f;
-                        P[1] = j0 + 1 <= cq ? P[1] * __expf(gq - gj.y) : 0.f;
-                        P[2] = j0 + 2 <= cq ? P[2] * __expf(gq - gj.z) : 0.f;
-                        P[3] = j0 + 3 <= cq ? P[3] * __expf(gq - gj.w) : 0.f;
-                    }
-                    T* prow = pb + Cfg::prow(qb) * 64 * (16 / ES);
-                    if constexpr (Cfg::BF) {
-#pragma unroll
-                        for (int p = 0; p <= qb / 2; ++p)
-                            *reinterpret_cast<s16x8*>(prow + p * 64 * 8) = __builtin_shufflevector(
-                                KO::tile(Pt[qb][2 * p]), KO::tile(Pt[qb][2 * p + 1]), 0, 1, 2, 3, 4, 5, 6, 7);
-                    } else {
-#pragma unroll
-                        for (int jb = 0; jb <= qb; ++jb) *reinterpret_cast<f32x4*>(prow + jb * 64 * 4) = Pt[qb][jb];
-                    }
-                }
+                if (cc >= 2) write_out(cc - 2);                  // formed by the output helpers last step
+                wait_vm_lgkm0<63>();
             }
-            wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
             barrier();
-        };
-        for (int cc = 0; cc < count; ++cc) step(cc);
+        }
         wait_vm_lgkm0<0>();   // no load still writing LDS when the workgroup ends
-        __syncthreads();   // the column waves have left the last output slice
-        if constexpr (STAGER) {
+        __syncthreads();      // the output helpers have formed the last output slice
+        if constexpr (!LOADER) {
             if (count >= 2) write_out(count - 2);
             if (count >= 1) write_out(count - 1);
         }
@@ -598,10 +667,10 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         else if constexpr (NVW > 1) run_col(std::integral_constant<int, (NVW > 1 ? 1 : 0)>{});
     } else {
         switch (w - NVW) {
-            case 0: run_help(std::integral_constant<int, 0>{}); break;
-            case 1: run_help(std::integral_constant<int, 1>{}); break;
-            case 2: run_help(std::integral_constant<int, 2>{}); break;
-            default: run_help(std::integral_constant<int, 3>{}); break;
+            case 0: run_out(std::integral_constant<int, 0>{}); break;
+            case 1: run_out(std::integral_constant<int, 1>{}); break;
+            case 2: run_stage(std::integral_constant<int, 0>{}); break;
+            default: run_stage(std::integral_constant<int, 1>{}); break;
         }
     }
 }
