@@ -13,7 +13,6 @@
 #include "../../include/gdn.h"
 #include "gdn_device.h"
 #include "gdn_prep.h"
-#include "gdn_scan.h"
 #include "gdn_scan_cols.h"
 #include "gdn_step.h"
 
@@ -69,7 +68,7 @@ Layout make_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int6
     auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
     const size_t u = (size_t)(L.slots * H);
     L.g = take(u * 3 * C * sizeof(float));   // g, exp(g), exp(g_n - g) per chunk
-    L.Tb = take(u * C * C * es);
+    L.Tb = take(u * (size_t)tb_blocks((int)C, es == 2) * 1024);   // Tb blocks per chunk
     if (varlen) {
         L.bounds = take((size_t)(n_seqs + 1) * sizeof(int));
         L.seq_slot = take((size_t)(n_seqs + 1) * sizeof(int));
@@ -137,14 +136,6 @@ struct KernelTimer {
 };
 
 template <typename T, int DK, int DV, int C>
-constexpr int scan_columns() {
-    if constexpr (DV >= 32) {
-        if constexpr (ScanCfg<T, DK, DV, C, 32>::FITS) return 32;
-    }
-    return 16;
-}
-
-template <typename T, int DK, int DV, int C>
 gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     const bool varlen = a.cu != nullptr;
     const Layout L = make_layout(a.B, a.T, a.H, DK, DV, C, varlen, a.n_seqs, sizeof(T));
@@ -189,9 +180,8 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         tm->mark(a.stream);
     }
     {
-        // the column-wave scan where its double-buffered staging fits in LDS,
-        // with 32 state columns per workgroup when that still gives every CU a
-        // workgroup, else 16; the row-block scan otherwise
+        // the column-wave scan, with 32 state columns per workgroup where that
+        // fits in LDS and still gives every CU a workgroup, else 16
         using C32 = ColCfg<T, DK, DV, C, (DV >= 32 ? 32 : 16)>;
         using C16 = ColCfg<T, DK, DV, C, 16>;
         constexpr bool fit32 = DV >= 32 && C32::FITS, fit16 = C16::FITS;
@@ -213,24 +203,9 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
                 return GDN_ERR_INTERNAL;
             }
         };
-        if constexpr (fit32 || fit16) {
-            if (fit32 && (!fit16 || units * (DV / 32) >= device_cu_count())) return launch_cols(C32{});
-            return launch_cols(C16{});
-        } else {
-            // state columns per workgroup: 32 (two column blocks, 8 waves) where the
-            // staged chunk leaves room in LDS, else 16
-            constexpr int DVT = scan_columns<T, DK, DV, C>();
-            using S = ScanCfg<T, DK, DV, C, DVT>;
-            static_assert(S::NTHR <= 512, "scan launch bounds");
-            constexpr auto ks = gdn_scan_kernel<T, DK, DV, C, DVT>;
-            allow_smem<ks>(S::SMEM);
-            tm->mark(a.stream);
-            hipLaunchKernelGGL(ks, dim3(DV / DVT, a.H, (unsigned)L.N), dim3(S::NTHR), S::SMEM,
-                               a.stream, q, k, v, a.S0, geom, a.H, g_ws, Tb_ws,
-                               static_cast<T*>(a.O), a.S_T);
-            if (gdn_status s = check_launch(a.stream)) return s;
-            tm->mark(a.stream);
-        }
+        static_assert(fit32 || fit16, "no column-scan configuration fits the LDS of one CU");
+        if (fit32 && (!fit16 || units * (DV / 32) >= device_cu_count())) return launch_cols(C32{});
+        return launch_cols(C16{});
     }
     return GDN_OK;
 }

@@ -149,6 +149,20 @@ __device__ __forceinline__ constexpr int swz(int r) {
 }
 
 
+// Tb = T diag(beta) of one chunk, as handed from the prep kernel to the scan:
+// whole 1 KB blocks of MFMA operands (16 bytes per lane, lane-linear), only the
+// blocks of the lower block triangle.  bf16: block (ti, q), 2q <= ti, gives
+// lane (g, n) row 16 ti + n at columns 4g .. 4g+3 of 16-column tiles 2q and
+// 2q + 1 (the A operand of a 16x16x32 instruction over token pair (2q, 2q + 1));
+// fp32: block (ti, tj), tj <= ti, gives lane (g, n) row 16 ti + n at columns
+// 16 tj + 4g .. + 3.  Blocks are numbered row block by row block.
+constexpr int tb_block(int ti, int q, bool bf) {
+    int s = 0;
+    for (int t = 0; t < ti; ++t) s += bf ? t / 2 + 1 : t + 1;
+    return s + q;
+}
+constexpr int tb_blocks(int C, bool bf) { return tb_block(C / 16, 0, bf); }
+
 // ---------------------------------------------------------------------------
 // Chunk metadata.  A chunk slot is one chunk of one sequence (shared by all
 // heads).  Fixed-length batches compute it; packed batches read a table

@@ -40,8 +40,8 @@
 //    registers (the diagonal blocks of T pass through LDS once, for the two
 //    operand layouts they serve in), each block also formed in row layout as
 //    T_ij^T = -R^T T_ii^T;
-//  - Tb = T diag(beta) leaves from that row layout as whole 16-byte pieces of
-//    its rows.
+//  - Tb = T diag(beta) leaves from that row layout as lane-linear 1 KB blocks
+//    of MFMA operands, the blocks above the diagonal omitted (tb_block).
 #pragma once
 
 #include "gdn_device.h"
@@ -141,17 +141,17 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
     float hold_g[3] = {0.f, 0.f, 0.f};
     T* hold_out = nullptr;
     float* hold_gout = nullptr;
+    // block (ti, q) of a unit's Tb at out: this lane's 16 bytes
+    auto tb_store = [&](T* out, int ti, int q, HFrag v) __attribute__((always_inline)) {
+        *reinterpret_cast<HFrag*>(reinterpret_cast<unsigned char*>(out) + tb_block(ti, q, Cfg::BF) * 1024 + l * 16) = v;
+    };
     auto flush_hold = [&]() __attribute__((always_inline)) {
         if (hold_out) {
 #pragma unroll
-            for (int ti = 0; ti < NB; ++ti) {
-                T* orow = hold_out + (16 * ti + n) * C;
+            for (int ti = 0; ti < NB; ++ti)
 #pragma unroll
-                for (int q = 0; q < NHQ; ++q) {
-                    if constexpr (Cfg::BF) *reinterpret_cast<bf16x8*>(orow + 32 * q + 8 * g) = hold[ti][q];
-                    else *reinterpret_cast<f32x4*>(orow + 16 * q + 4 * g) = hold[ti][q];
-                }
-            }
+                for (int q = 0; q < NHQ; ++q)
+                    if ((Cfg::BF ? 2 * q : q) <= ti) tb_store(hold_out, ti, q, hold[ti][q]);
             if (l < C) {
                 hold_gout[l] = hold_g[0];
                 hold_gout[C + l] = hold_g[1];
@@ -290,13 +290,10 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
                 Tr[i][j] = -mma16_f32(R, Ta_op[i], zero4());
             }
 
-        // Tb = T diag(beta), zero above the diagonal, straight from the row
-        // layout: lane (g, n) stores row 16 ti + n.  fp32 rows are plain (16 bytes
-        // = columns 16 tj + 4g ..); a bf16 row stores each 32-column group as the
-        // 4-column runs (0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31), so the
-        // 16 bytes at group offset 8g -- columns 4g.. of both 16-column tiles of
-        // the group -- are the operand of a 16-deep block pair.
-        T* out = Tb_ws + unit * C * C;
+        // Tb = T diag(beta) straight from the row layout, in the block layout of
+        // tb_block: lane (g, n) holds row 16 ti + n at columns 4g .. 4g+3 of each
+        // 16-column tile (bf16: tiles 2q and 2q + 1 in one 16-byte piece).
+        T* out = Tb_ws + unit * (tb_blocks(C, Cfg::BF) * 1024 / ES);
         auto trow = [&](int ti, int tj) __attribute__((always_inline)) {
             const f32x4 t = tj < ti ? Tr[ti][tj] : tj == ti ? Ta_op[ti] : zero4();
             const float4 b4 = *reinterpret_cast<const float4*>(sb + 16 * tj + 4 * g);
@@ -304,9 +301,9 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
         };
 #pragma unroll
         for (int ti = 0; ti < NB; ++ti) {
-            T* orow = out + (16 * ti + n) * C;
 #pragma unroll
             for (int q = 0; q < NHQ; ++q) {
+                if ((Cfg::BF ? 2 * q : q) > ti) continue;   // above the diagonal: not stored
                 HFrag o;
                 if constexpr (Cfg::BF) {
                     const f32x4 t0 = trow(ti, 2 * q), t1 = trow(ti, 2 * q + 1);
@@ -316,8 +313,7 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
                     o = trow(ti, q);
                 }
                 if constexpr (Cfg::PREFETCH) hold[ti][q] = o;
-                else if constexpr (Cfg::BF) *reinterpret_cast<bf16x8*>(orow + 32 * q + 8 * g) = o;
-                else *reinterpret_cast<f32x4*>(orow + 16 * q + 4 * g) = o;
+                else tb_store(out, ti, q, o);
             }
         }
         if constexpr (Cfg::PREFETCH) hold_out = out;

@@ -1,8 +1,8 @@
 // gdn_scan_cols.h -- serial inter-chunk state scan with the chunk outputs fused
 // in, one wave per 16 state columns.
 //
-// Same arithmetic as gdn_scan.h (row form, per chunk, S = state at the chunk
-// start, Dv x Dk; gamma_i = exp(g_i); Tb = T diag(beta) from the prep kernel):
+// Per chunk (row form, S = state at the chunk start, Dv x Dk; gamma_i =
+// exp(g_i); Tb = T diag(beta) from the prep kernel):
 //   Y  = K S^T,   X = V - diag(gamma) Y,   V' = Tb X
 //   O^T = Z^T diag(gamma) + V'^T P^T,  Z^T = S Q^T, P = (Q K^T) o Gamma o M
 //   S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V'
@@ -36,7 +36,7 @@
 // fp32: tile i covers d = 16 i + rho (four 16x16x4 MFMAs per tile).
 #pragma once
 
-#include "gdn_scan.h"
+#include "gdn_ops.h"
 
 namespace gdn {
 
@@ -53,13 +53,13 @@ struct ColCfg {
     static constexpr int NLD = NF - 1;                     // chunks, the last writes out O
     static constexpr int EV = 16 / ES;                     // elements per 16 bytes
     // staged rows: bf16 unpadded with XOR swizzles (K: kind 4 for rows of 16+
-    // blocks, else 1; V: kind 5 for rows of 4 blocks, 2 for longer ones; Tb:
-    // kind 3), fp32 padded by one block
-    static constexpr int KB = DK / EV, VB = DVT / EV, TB = C / EV;
-    static constexpr int KP = BF ? KB : KB + 1, VP = BF ? VB : VB + 1, TP = BF ? TB : TB + 1;
-    static constexpr int KSW = BF ? (KB >= 16 ? 4 : 1) : 0, TSW = BF ? 3 : 0;
+    // blocks, else 1; V: kind 5 for rows of 4 blocks, 2 for longer ones), fp32
+    // padded by one block; Tb arrives as its lane-linear operand blocks
+    static constexpr int KB = DK / EV, VB = DVT / EV;
+    static constexpr int KP = BF ? KB : KB + 1, VP = BF ? VB : VB + 1;
+    static constexpr int KSW = BF ? (KB >= 16 ? 4 : 1) : 0;
     static constexpr int VSW = BF && VB == 4 ? 5 : BF && VB > 4 ? 2 : 0;
-    static constexpr int LDK = KP * EV, LDV = VP * EV, LDC = TP * EV;
+    static constexpr int LDK = KP * EV, LDV = VP * EV;
     static constexpr int NDB = DK / 16;                    // state tiles per column wave
     static constexpr int NP = (NW + 1) / 2;                // pairs of token blocks
     static constexpr int KS = Step<T>::KS, NKK = DK / KS;  // contraction steps over d
@@ -69,7 +69,7 @@ struct ColCfg {
     static constexpr int blocks(int bytes) { return (bytes + 1023) / 1024; }
     static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
     static constexpr int NIK = blocks(C * LDK * ES), NIV = blocks(C * LDV * ES);
-    static constexpr int NIT = blocks(C * LDC * ES), NIG = blocks(3 * C * 4);
+    static constexpr int NIT = tb_blocks(C, BF), NIG = blocks(3 * C * 4);
     static constexpr int BT = NIK, BV = BT + NIT, BG = BV + NIV, NI = BG + NIG;
     static constexpr int NL = cdiv(NI, NLD);               // loads per loading lane per chunk
     // loads loading wave f issues per chunk
@@ -88,9 +88,12 @@ struct ColCfg {
     static constexpr int OPR = DVT * ES / 16;                  // 16-byte pieces per row
     static constexpr int NOPL = cdiv(C * OPR, 64);             // pieces per writing lane
     static constexpr size_t SZ_O = (size_t)C * LDO;
-    // staging buffers: as many as fit, up to four (loads run NSTG - 1 chunks ahead)
+    // staging buffers: as many as fit, up to four (loads run NSTG - 1 chunks
+    // ahead; the loader's wait for all but its newest NSTG - 2 chunks must stay
+    // within the vmcnt range)
     static constexpr size_t SZ_REST = 2 * SZ_SB + 2 * SZ_VO + 2 * SZ_O;
-    static constexpr int NSTG = 4 * SZ_STAGE + SZ_REST <= 160 * 1024 ? 4 : 3 * SZ_STAGE + SZ_REST <= 160 * 1024 ? 3 : 2;
+    static constexpr bool fits(int ns) { return ns * SZ_STAGE + SZ_REST <= 160 * 1024 && cdiv(NI, NLD) * (ns - 2) < 64; }
+    static constexpr int NSTG = fits(4) ? 4 : fits(3) ? 3 : 2;
     static constexpr int DIST = NSTG - 1;                  // chunks staged ahead
     static constexpr size_t OFF_SB = NSTG * SZ_STAGE, OFF_VO = OFF_SB + 2 * SZ_SB;
     static constexpr size_t OFF_O = OFF_VO + 2 * SZ_VO;
@@ -110,10 +113,12 @@ struct ColCfg {
         return 0;
     }
     static constexpr int NQB = (NW + 1) / 2;               // query blocks per helper, at most
-    static constexpr int NQS = 3;                          // Q register sets: chunks loaded ahead
+    // Q register sets (chunks loaded ahead): three where a set takes at most 32
+    // registers, else two
+    static constexpr int NQS = NQB * NKK * 16 <= 128 ? 3 : 2;
     static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && NVW <= 2, "tile counts");
     static_assert(DV % DVT == 0 && DVT % 16 == 0 && DK % KS == 0 && DK % 16 == 0, "tile shapes");
-    static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && (VB % 4 == 0 || VB == 2) && TB % 8 == 0 && DK % 32 == 0),
+    static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && (VB % 4 == 0 || VB == 2) && DK % 32 == 0),
                   "bf16 swizzles and tile pairs");
 };
 
@@ -150,7 +155,7 @@ __device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_
     };
     switch (col_region<Cfg>(j, f)) {
         case 0: off = region(i * 64 + l, Cfg::KP, Cfg::KB, Cfg::KSW, rs_k); break;
-        case 2: off = region((i - Cfg::BT) * 64 + l, Cfg::TP, Cfg::TB, Cfg::TSW, (int64_t)C * Cfg::ES); break;
+        case 2: off = (int64_t)((i - Cfg::BT) * 64 + l) * 16; break;
         case 3: off = region((i - Cfg::BV) * 64 + l, Cfg::VP, Cfg::VB, Cfg::VSW, rs_v); break;
         case 4: {
             const int s = (i - Cfg::BG) * 64 + l;
@@ -287,11 +292,14 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         // One chunk.  All K fragments of Y and the chunk's Tb rows, gates and V
         // values are requested as it starts, the K^T operands of the state
         // update right after the Y instructions.
+        // K fragments in flight: all contraction steps of Y where they take at
+        // most 64 registers, else a ring of that many
+        constexpr int KPF = NKK * NW * (int)sizeof(Frag) <= 256 ? NKK : 256 / (NW * (int)sizeof(Frag));
         auto step = [&](const int cc) __attribute__((always_inline)) {
             const Staged st = staged(cc);
-            Frag fk[NKK][NW];
+            Frag fk[KPF][NW];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
+            for (int kk = 0; kk < KPF; ++kk)
 #pragma unroll
                 for (int tb = 0; tb < NW; ++tb) fk[kk][tb] = kfrag_rows<Cfg>(st.K, tb * 16, kk * KS);
             float4 gam4[NW], dec4[NW];
@@ -310,26 +318,26 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
 #pragma unroll
             for (int ib = 0; ib < NW; ++ib)
 #pragma unroll
-                for (int p = 0; p < NTP; ++p) {
-                    if constexpr (Cfg::BF) {
-                        if (2 * p <= ib)
-                            ta[ib][p] = *reinterpret_cast<const bf16x8*>(st.Tb + tidx<Cfg>(ib * 16 + n, 32 * p + 2 * g4));
-                    } else {
-                        if (p <= ib)
-                            ta[ib][p] = *reinterpret_cast<const f32x4*>(st.Tb + tidx<Cfg>(ib * 16 + n, 16 * p + g4));
-                    }
-                }
+                for (int p = 0; p < NTP; ++p)
+                    if ((Cfg::BF ? 2 * p : p) <= ib)
+                        ta[ib][p] = *reinterpret_cast<const TFrag*>(reinterpret_cast<const unsigned char*>(st.Tb) +
+                                                                    tb_block(ib, p, Cfg::BF) * 1024 + l * 16);
             // Y = K S^T (A: K rows; B: the state tiles) for every token block
             f32x4 Y[NW];
 #pragma unroll
             for (int tb = 0; tb < NW; ++tb) Y[tb] = zero4();
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
+            for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
                 for (int tb = 0; tb < NW; ++tb) {
-                    if constexpr (Cfg::BF) Y[tb] = KO::mma2p(fk[kk][tb], Sb[2 * kk], Sb[2 * kk + 1], Y[tb]);
-                    else Y[tb] = St16::mma(fk[kk][tb], Sb[kk], Y[tb]);
+                    if constexpr (Cfg::BF) Y[tb] = KO::mma2p(fk[kk % KPF][tb], Sb[2 * kk], Sb[2 * kk + 1], Y[tb]);
+                    else Y[tb] = St16::mma(fk[kk % KPF][tb], Sb[kk], Y[tb]);
                 }
+                if (kk + KPF < NKK) {
+#pragma unroll
+                    for (int tb = 0; tb < NW; ++tb) fk[kk % KPF][tb] = kfrag_rows<Cfg>(st.K, tb * 16, (kk + KPF) * KS);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
             // K^T operands of the state update
             Op kt[NDB][NW];
@@ -602,7 +610,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             const int64_t unit = (int64_t)(first + cd) * H + h;
             const T* kb = k + ((int64_t)t0 * H + h) * DK;
             const T* vb_ = v + ((int64_t)t0 * H + h) * DV + v0;
-            const T* tb = Tb_ws + unit * C * C;
+            const T* tb = Tb_ws + unit * (Cfg::NIT * 1024 / ES);
             const float* gb = g_ws + unit * 3 * C;
             const int nk = (int)((len - 1) * rs_k + DK * ES), nv = (int)((len - 1) * rs_v + DVT * ES);
             unsigned char* dst = smem + (cd % Cfg::NSTG) * Cfg::SZ_STAGE + f * 1024;
@@ -612,7 +620,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 if (r == 5) continue;
                 const void* base = r == 0 ? (const void*)kb : r == 2 ? (const void*)tb : r == 3 ? (const void*)vb_
                                  : (const void*)gb;
-                const int nrec = r == 0 ? nk : r == 2 ? C * C * ES : r == 3 ? nv : 3 * C * 4;
+                const int nrec = r == 0 ? nk : r == 2 ? Cfg::NIT * 1024 : r == 3 ? nv : 3 * C * 4;
                 lds_load16(make_rsrc(base, nrec), dst + j * Cfg::NLD * 1024, soff[j]);
             }
         };

@@ -23,6 +23,34 @@ def _align(x, a=256):
     return (x + a - 1) // a * a
 
 
+def tb_blocks(C, dtype):
+    nb = C // 16
+    return sum(t // 2 + 1 if dtype == "bf16" else t + 1 for t in range(nb))
+
+
+def unpack_tb(flat, C, dtype):
+    """Dense C x C Tb of every chunk from the lane-linear operand blocks of the
+    lower block triangle: lane (g, n) of block (ti, q) holds row 16 ti + n at
+    columns 4g .. 4g+3 of 16-column tile 2q and then of tile 2q + 1 (bf16), or of
+    tile q (fp32); blocks row block by row block; the rest is zero."""
+    nb, nblk = C // 16, tb_blocks(C, dtype)
+    per = 1024 // flat.element_size()          # values per block
+    x = flat.double().numpy().reshape(-1, nblk, 64, per // 64)
+    out = np.zeros((x.shape[0], C, C))
+    b = 0
+    for ti in range(nb):
+        for q in range(ti // 2 + 1 if dtype == "bf16" else ti + 1):
+            for lane in range(64):
+                g, n = lane >> 4, lane & 15
+                vals = x[:, b, lane]
+                tiles = (2 * q, 2 * q + 1) if dtype == "bf16" else (q,)
+                for k, tj in enumerate(tiles):
+                    if tj < nb:
+                        out[:, 16 * ti + n, 16 * tj + 4 * g:16 * tj + 4 * g + 4] = vals[:, 4 * k:4 * k + 4]
+            b += 1
+    return out
+
+
 def chunk_algebra(K, V, beta, la):
     n = K.shape[0]
     g = np.cumsum(la)
@@ -56,16 +84,8 @@ def test_prep_intermediates(dtype, Dk, Dv, C, tol):
     wsc = ws.cpu()
     g3 = wsc[off_g:off_g + u * 3 * C * 4].view(torch.float32).view(cps, H, 3, C).double().numpy()
     g_all = g3[:, :, 0]
-    Tb_all = wsc[off_t:off_t + u * C * C * es].view(tdt).view(cps, H, C, C).double().numpy()
-    if dtype == "bf16":
-        # bf16 rows store each 32-column group as the 4-column runs of columns
-        # 4g.. and 16+4g.. next to each other (g = 0..3)
-        p = np.arange(C)
-        logical = 32 * (p // 32) + 16 * ((p % 8) // 4) + 4 * ((p % 32) // 8) + p % 4
-        assert sorted(logical) == list(range(C))
-        unperm = np.empty_like(Tb_all)
-        unperm[..., logical] = Tb_all
-        Tb_all = unperm
+    Tb_all = unpack_tb(wsc[off_t:off_t + u * tb_blocks(C, dtype) * 1024].view(tdt), C, dtype)
+    Tb_all = Tb_all.reshape(cps, H, C, C)
     for c in range(cps):
         t0, n = c * C, min(C, T - c * C)
         for h in range(H):
