@@ -86,6 +86,26 @@ __device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
     return c;
 }
 
+// An fp32 operand of one 16-deep block as the sum of two bf16 parts, hi = bf16(x)
+// and lo = bf16(x - hi); three bf16 products (lo hi, hi lo, hi hi) then give
+// the fp32 product to about 2^-16 relative, at a third of the cost of the fp32
+// instructions.
+typedef short p16x4 __attribute__((ext_vector_type(4)));
+struct Split16 {
+    p16x4 hi, lo;
+};
+__device__ __forceinline__ Split16 split16(f32x4 x) {
+    const bf16x4 h = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    const f32x4 r = {x[0] - (float)h[0], x[1] - (float)h[1], x[2] - (float)h[2], x[3] - (float)h[3]};
+    const bf16x4 lo = {(bf16)r[0], (bf16)r[1], (bf16)r[2], (bf16)r[3]};
+    return Split16{__builtin_bit_cast(p16x4, h), __builtin_bit_cast(p16x4, lo)};
+}
+__device__ __forceinline__ f32x4 mma16_x3(const Split16& a, const Split16& b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, c, 0, 0, 0);
+}
+
 template <typename T, int DK, int C>
 __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void gdn_prep_kernel(
     const T* __restrict__ k, const float* __restrict__ log_alpha,
@@ -246,12 +266,22 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) x[i] = i == n ? 1.f : 0.f;
+            // the rows below the diagonal of column j, requested two columns ahead
+            float4 col[3][4];
+            auto ldcol = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i4 = (j + 1) / 4; i4 < 4; ++i4)
+                    col[j % 3][i4] = *reinterpret_cast<const float4*>(ab + j * 16 + 4 * i4);
+            };
+            ldcol(0);
+            ldcol(1);
 #pragma unroll
             for (int j = 0; j < 15; ++j) {
+                if (j + 2 < 15) ldcol(j + 2);
                 const float xj = x[j];
 #pragma unroll
                 for (int i4 = (j + 1) / 4; i4 < 4; ++i4) {
-                    const float4 a4 = *reinterpret_cast<const float4*>(ab + j * 16 + 4 * i4);
+                    const float4 a4 = col[j % 3][i4];
                     if (4 * i4 + 0 > j) x[4 * i4 + 0] -= a4.x * xj;
                     if (4 * i4 + 1 > j) x[4 * i4 + 1] -= a4.y * xj;
                     if (4 * i4 + 2 > j) x[4 * i4 + 2] -= a4.z * xj;
@@ -277,18 +307,45 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
         // layout (T[16i + 4g + r][16j + n]) for the blocks later levels take as B
         // operands; Tr: row layout (T[16i + n][16j + 4g + r]), from
         // T_ij^T = -R^T T_ii^T, for the output
+        // (bf16 inputs: on split-bf16 products, as Tb leaves in bf16 anyway)
         f32x4 To[NB][NB], Tr[NB][NB];
+        if constexpr (Cfg::BF) {
+            Split16 As[NB][NB], Tbs[NB], Tas[NB], Tos[NB][NB];
 #pragma unroll
-        for (int d = 1; d < NB; ++d)
+            for (int b = 0; b < NB; ++b) {
+                Tbs[b] = split16(Tb_op[b]);
+                Tas[b] = split16(Ta_op[b]);
 #pragma unroll
-            for (int j = 0; j + d < NB; ++j) {
-                const int i = j + d;
-                f32x4 R = zero4();
-#pragma unroll
-                for (int m = j; m < i; ++m) R = mma16_f32(A[i][m], m == j ? Tb_op[j] : To[m][j], R);
-                if (i < NB - 1) To[i][j] = -mma16_f32(Ta_op[i], R, zero4());
-                Tr[i][j] = -mma16_f32(R, Ta_op[i], zero4());
+                for (int m = 0; m < b; ++m) As[b][m] = split16(A[b][m]);
             }
+#pragma unroll
+            for (int d = 1; d < NB; ++d)
+#pragma unroll
+                for (int j = 0; j + d < NB; ++j) {
+                    const int i = j + d;
+                    f32x4 R = zero4();
+#pragma unroll
+                    for (int m = j; m < i; ++m) R = mma16_x3(As[i][m], m == j ? Tbs[j] : Tos[m][j], R);
+                    const Split16 Rs = split16(R);
+                    if (i < NB - 1) {
+                        To[i][j] = -mma16_x3(Tas[i], Rs, zero4());
+                        Tos[i][j] = split16(To[i][j]);
+                    }
+                    Tr[i][j] = -mma16_x3(Rs, Tas[i], zero4());
+                }
+        } else {
+#pragma unroll
+            for (int d = 1; d < NB; ++d)
+#pragma unroll
+                for (int j = 0; j + d < NB; ++j) {
+                    const int i = j + d;
+                    f32x4 R = zero4();
+#pragma unroll
+                    for (int m = j; m < i; ++m) R = mma16_f32(A[i][m], m == j ? Tb_op[j] : To[m][j], R);
+                    if (i < NB - 1) To[i][j] = -mma16_f32(Ta_op[i], R, zero4());
+                    Tr[i][j] = -mma16_f32(R, Ta_op[i], zero4());
+                }
+        }
 
         // Tb = T diag(beta) straight from the row layout, in the block layout of
         // tb_block: lane (g, n) holds row 16 ti + n at columns 4g .. 4g+3 of each
