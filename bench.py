@@ -167,7 +167,10 @@ def main():
     # Cache eviction between steps: one pass reading 512 MB (twice the MALL)
     # leaves L2 and MALL holding clean lines of this buffer, so every step reads
     # its inputs from HBM without paying write-backs that belong to other work.
-    flush = None if args.no_flush else torch.zeros(512 << 18, device=dev, dtype=torch.int32)
+    # fp32, so that the sum is one read pass with no widened temporary (an int32
+    # sum would first write a 1 GB int64 copy, whose dirty lines land in the
+    # timed kernels)
+    flush = None if args.no_flush else torch.zeros(512 << 18, device=dev, dtype=torch.float32)
 
     def evict():
         if flush is not None:
