@@ -16,12 +16,13 @@
 //    synchronisation inside a chunk.  At the end of a chunk it leaves V' and
 //    the new state (as MFMA operands in the input dtype) in LDS;
 //  - two output helpers, each owning half of the chunk's query blocks, form
-//    P^T = ((Q K^T) o Gamma o M)^T and Z^T = S Q^T for them in registers (Q
-//    comes straight from memory into registers, three chunks ahead), and one step
-//    later, when V' of that chunk is published, the output
+//    P^T = ((Q K^T) o Gamma o M)^T and Z^T = S Q^T for them in registers, and
+//    one step later, when V' of that chunk is published, the output
 //    O^T = Z^T diag(gamma) + V'^T P^T, which they leave in LDS;
-//  - two staging waves: one loads the chunks (K, Tb, the V slice, gates)
-//    straight into LDS up to three chunks ahead, the other writes the output slices
+//  - two staging waves: one loads the chunks straight into LDS (K, Tb, the V
+//    slice and the gates two chunks ahead, Q one chunk ahead; where Q does not
+//    fit in LDS, the output helpers load it into registers, three chunks
+//    ahead), the other writes the output slices
 //    out as whole 16-byte pieces of their rows (apart, so that the loader's
 //    wait for its loads does not also wait for stores).
 // With waves dealt to the four SIMDs in turn, the column waves and the output
@@ -88,14 +89,22 @@ struct ColCfg {
     static constexpr int OPR = DVT * ES / 16;                  // 16-byte pieces per row
     static constexpr int NOPL = cdiv(C * OPR, 64);             // pieces per writing lane
     static constexpr size_t SZ_O = (size_t)C * LDO;
-    // staging buffers: as many as fit, up to four (loads run NSTG - 1 chunks
-    // ahead; the loader's wait for all but its newest NSTG - 2 chunks must stay
-    // within the vmcnt range)
+    // Q of a chunk: staged by the loader one chunk ahead in two LDS buffers
+    // (rows as K's) where that fits next to three staging buffers (QLDS), else
+    // loaded by the output helpers straight into registers, NQS chunks ahead
+    static constexpr size_t SZ_Q = (size_t)NIK * 1024;
     static constexpr size_t SZ_REST = 2 * SZ_SB + 2 * SZ_VO + 2 * SZ_O;
-    static constexpr bool fits(int ns) { return ns * SZ_STAGE + SZ_REST <= 160 * 1024 && cdiv(NI, NLD) * (ns - 2) < 64; }
-    static constexpr int NSTG = fits(4) ? 4 : fits(3) ? 3 : 2;
+    // ns staging buffers (loads run ns - 1 chunks ahead), with or without the Q
+    // buffers; the loader's wait for all but its newest ns - 2 chunks must stay
+    // within the vmcnt range
+    static constexpr bool fits(int ns, bool q) {
+        return ns * SZ_STAGE + SZ_REST + (q ? 2 * SZ_Q : 0) <= 160 * 1024 && cdiv(NI, NLD) * (ns - 2) < 64;
+    }
+    static constexpr bool QLDS = fits(3, true);
+    static constexpr int NSTG = QLDS ? 3 : fits(4, false) ? 4 : fits(3, false) ? 3 : 2;
     static constexpr int DIST = NSTG - 1;                  // chunks staged ahead
-    static constexpr size_t OFF_SB = NSTG * SZ_STAGE, OFF_VO = OFF_SB + 2 * SZ_SB;
+    static constexpr size_t OFF_QB = NSTG * SZ_STAGE, OFF_SB = OFF_QB + (QLDS ? 2 * SZ_Q : 0);
+    static constexpr size_t OFF_VO = OFF_SB + 2 * SZ_SB;
     static constexpr size_t OFF_O = OFF_VO + 2 * SZ_VO;
     static constexpr size_t SMEM = OFF_O + 2 * SZ_O;
     static constexpr bool FITS = SMEM <= 160 * 1024;
@@ -113,8 +122,7 @@ struct ColCfg {
         return 0;
     }
     static constexpr int NQB = (NW + 1) / 2;               // query blocks per helper, at most
-    // Q register sets (chunks loaded ahead): three where a set takes at most 32
-    // registers, else two
+    // Q register sets without QLDS: three where a set takes at most 32 registers
     static constexpr int NQS = NQB * NKK * 16 <= 128 ? 3 : 2;
     static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && NVW <= 2, "tile counts");
     static_assert(DV % DVT == 0 && DVT % 16 == 0 && DK % KS == 0 && DK % 16 == 0, "tile shapes");
@@ -261,6 +269,8 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         st.dec = st.g + 2 * C;
         return st;
     };
+    // staged Q of chunk cd
+    auto qbuf = [&](int cd) __attribute__((always_inline)) { return smem + Cfg::OFF_QB + (cd & 1) * Cfg::SZ_Q; };
     // hand-over tiles: tile i of column wave vb, this lane's 4 values
     auto sb_tile = [&](int cd, int vb, int i) __attribute__((always_inline)) {
         return reinterpret_cast<Op*>(smem + Cfg::OFF_SB + (cd & 1) * Cfg::SZ_SB + (vb * NDB + i) * Cfg::TILE) + l;
@@ -411,10 +421,10 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
     auto run_out = [&](auto hw_const) __attribute__((always_inline)) {
         constexpr int hw = decltype(hw_const)::value;
         constexpr int NM = Cfg::nmine(hw);
-        // Q rows of this helper's query blocks, straight into registers: lane
-        // (g, n) gets Q[qb*16 + n][kk*KS + g*EV ..] (rows past the chunk end
-        // read as zeros)
-        auto q_load = [&](Frag (*qf)[NKK], int cd) __attribute__((always_inline)) {
+        // without QLDS: Q rows of this helper's query blocks straight into
+        // registers, lane (g, n) getting Q[qb*16 + n][kk*KS + g*EV ..] (rows past
+        // the chunk end read as zeros)
+        auto q_load = [&](Frag (*qr)[NKK], int cd) __attribute__((always_inline)) {
             const int t0 = ts + cd * C, len = min(C, te - t0);
             const __amdgpu_buffer_rsrc_t rq =
                 make_rsrc(q + ((int64_t)t0 * H + h) * DK, (len - 1) * rs_k + DK * ES);
@@ -422,7 +432,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             for (int j = 0; j < NM; ++j)
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk)
-                    qf[j][kk] = __builtin_bit_cast(
+                    qr[j][kk] = __builtin_bit_cast(
                         Frag, __builtin_amdgcn_raw_buffer_load_b128(
                                   rq, (uint32_t)((Cfg::mine(hw, j) * 16 + n) * rs_k) + kk * KS * ES + (l >> 4) * 16, 0, 0));
         };
@@ -459,13 +469,17 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         constexpr int QMAX = Cfg::mine(hw, NM - 1);   // the largest query block
         auto step = [&](const int cc, Frag (*qcur)[NKK]) __attribute__((always_inline)) {
             const Staged st = staged(cc);
-            // K fragments and state tiles of one contraction step, requested a
-            // step ahead of their use (two register sets)
-            Frag kf[2][NW];
+            const T* sQ = reinterpret_cast<const T*>(qbuf(cc));
+            // K and Q fragments and state tiles of one contraction step,
+            // requested a step ahead of their use (two register sets)
+            Frag kf[2][NW], qf[2][Cfg::NQB];
             Op sbk[2][NVW][2];
             auto fetch = [&](int kk, int s) __attribute__((always_inline)) {
 #pragma unroll
                 for (int jb = 0; jb <= QMAX; ++jb) kf[s][jb] = kfrag_rows<Cfg>(st.K, jb * 16, kk * KS);
+#pragma unroll
+                for (int j = 0; j < NM; ++j)
+                    qf[s][j] = Cfg::QLDS ? kfrag_rows<Cfg>(sQ, Cfg::mine(hw, j) * 16, kk * KS) : qcur[j][kk];
 #pragma unroll
                 for (int vb = 0; vb < NVW; ++vb) {
                     sbk[s][vb][0] = *sb_tile(cc, vb, Cfg::BF ? 2 * kk : kk);
@@ -521,15 +535,15 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 for (int j = 0; j < NM; ++j) {
                     const int qb = Cfg::mine(hw, j);
 #pragma unroll
-                    for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] = St16::mma(kf[s][jb], qcur[j][kk], Pt[j][jb]);
+                    for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] = St16::mma(kf[s][jb], qf[s][j], Pt[j][jb]);
 #pragma unroll
                     for (int vb = 0; vb < NVW; ++vb) {
                         if constexpr (Cfg::BF) {
-                            const s16x8 qs = __builtin_bit_cast(s16x8, qcur[j][kk]);
+                            const s16x8 qs = __builtin_bit_cast(s16x8, qf[s][j]);
                             Zt[j][vb] = KO::mma2(sbk[s][vb][0], sbk[s][vb][1], __builtin_shufflevector(qs, qs, 0, 1, 2, 3),
                                                  __builtin_shufflevector(qs, qs, 4, 5, 6, 7), Zt[j][vb]);
                         } else {
-                            Zt[j][vb] = St16::mma(sbk[s][vb][0], qcur[j][kk], Zt[j][vb]);
+                            Zt[j][vb] = St16::mma(sbk[s][vb][0], qf[s][j], Zt[j][vb]);
                         }
                     }
                 }
@@ -562,25 +576,30 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                     for (int jb = 0; jb <= qb; ++jb) pp[j][jb] = Pt[j][jb];
                 }
             }
-            q_load(qcur, min(cc + Cfg::NQS, count - 1));   // refill the set just used; past the end: re-read, unused
+            if constexpr (!Cfg::QLDS) q_load(qcur, min(cc + Cfg::NQS, count - 1));   // refill the set just used
             wait_vm_lgkm0<63>();
             barrier();
         };
-        constexpr int NQS = Cfg::NQS;
-        Frag qs[NQS][Cfg::NQB][NKK];
-        if (count > 0) {
+        if constexpr (Cfg::QLDS) {
+            __syncthreads();
+            for (int cc = 0; cc < count; ++cc) step(cc, nullptr);
+        } else {
+            constexpr int NQS = Cfg::NQS;
+            Frag qs[NQS][Cfg::NQB][NKK];
+            if (count > 0) {
 #pragma unroll
-            for (int d = 0; d < NQS; ++d) q_load(qs[d], min(d, count - 1));
+                for (int d = 0; d < NQS; ++d) q_load(qs[d], min(d, count - 1));
+            }
+            __syncthreads();
+            int cc = 0;
+            for (; cc + NQS <= count; cc += NQS) {
+#pragma unroll
+                for (int i = 0; i < NQS; ++i) step(cc + i, qs[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < NQS - 1; ++i)
+                if (cc + i < count) step(cc + i, qs[i]);
         }
-        __syncthreads();
-        int cc = 0;
-        for (; cc + NQS <= count; cc += NQS) {
-#pragma unroll
-            for (int i = 0; i < NQS; ++i) step(cc + i, qs[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < NQS - 1; ++i)
-            if (cc + i < count) step(cc + i, qs[i]);
         if (count > 0) {   // its V' was published by the last barrier
             Op vo[NVW][NW];
 #pragma unroll
@@ -624,6 +643,16 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 lds_load16(make_rsrc(base, nrec), dst + j * Cfg::NLD * 1024, soff[j]);
             }
         };
+        // chunk cd's Q into the Q buffer of its parity (the K blocks' offsets)
+        auto stage_q = [&](int cd) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const __amdgpu_buffer_rsrc_t rq =
+                make_rsrc(q + ((int64_t)t0 * H + h) * DK, (int)((len - 1) * rs_k + DK * ES));
+            unsigned char* dst = qbuf(cd) + f * 1024;
+#pragma unroll
+            for (int j = 0; j < Cfg::NL; ++j)
+                if (col_region<Cfg>(j, f) == 0) lds_load16(rq, dst + j * Cfg::NLD * 1024, soff[j]);
+        };
         // chunk cd's output slice from LDS to memory, 16 bytes per lane, rows
         // past the chunk end dropped by the buffer range; streamed past the caches
         auto write_out = [&](int cd) __attribute__((always_inline)) {
@@ -641,12 +670,14 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 }
             }
         };
-        // the loads of chunk cc + DIST go out as step cc starts, into the buffer
-        // whose readers passed the previous barrier; before its closing barrier
-        // step cc waits for all but the newest ND loads, i.e. for chunk cc + 1
-        // (loads complete in issue order)
+        // Step cc stages Q of chunk cc + 1, then K .. gates of chunk cc + DIST,
+        // each into the buffer whose readers passed the previous barrier; before
+        // its closing barrier it waits for all but the newest DIST - 1 chunks of
+        // staging loads, i.e. for everything chunk cc + 1 needs (loads complete
+        // in issue order)
         static_assert(ND * (Cfg::DIST - 1) < 64, "vmcnt range");
         if (LOADER && count > 0) {
+            if constexpr (Cfg::QLDS) stage_q(0);
 #pragma unroll
             for (int d = 0; d < Cfg::DIST; ++d) stage(min(d, count - 1));
             wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
@@ -654,7 +685,8 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         __syncthreads();
         for (int cc = 0; cc < count; ++cc) {
             if constexpr (LOADER) {
-                stage(min(cc + Cfg::DIST, count - 1));           // past the end: re-read, unused
+                if constexpr (Cfg::QLDS) stage_q(min(cc + 1, count - 1));   // past the end: re-read, unused
+                stage(min(cc + Cfg::DIST, count - 1));
                 wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
             } else {
                 if (cc >= 2) write_out(cc - 2);                  // formed by the output helpers last step
