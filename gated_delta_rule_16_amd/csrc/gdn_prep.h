@@ -25,8 +25,10 @@
 //
 // Work split: one wave prepares one unit (chunk slot, head) at a time, with no
 // synchronisation beyond the wave.  Waves are persistent: wave w of workgroup
-// b walks units b*4 + w, then that plus 4 gridDim, ... and loads the next
-// unit's keys and gates into registers while it works on the current one.
+// b walks units b*4 + w, then that plus 4 gridDim, ...  Two waves share each
+// SIMD (the register budget is held to half the file), so that one computes
+// while the other waits for its unit's keys -- this measured faster than one
+// wave per SIMD with the next unit's keys prefetched into registers.
 // Per unit:
 //  - the keys arrive as MFMA row fragments (lane (g, n): row 16b + n, 16 bytes
 //    at contraction offset 16 g of each step), so K K^T needs no LDS;
@@ -36,8 +38,9 @@
 //  - each diagonal 16 x 16 block of T is found by forward substitution in
 //    registers (lane (b, c): column c of block b) from the block's columns of
 //    A in LDS; the blocks below the diagonal follow one block diagonal at a
-//    time, T_ij = -T_ii sum_{j <= m < i} A_im T_mj, on fp32 MFMA straight from
-//    registers (the diagonal blocks of T pass through LDS once, for the two
+//    time, T_ij = -T_ii sum_{j <= m < i} A_im T_mj, on MFMA (fp32, or bf16
+//    products for bf16 inputs) straight from registers (the diagonal blocks
+//    of T pass through LDS once, for the two
 //    operand layouts they serve in), each block also formed in row layout as
 //    T_ij^T = -R^T T_ii^T;
 //  - Tb = T diag(beta) leaves from that row layout as lane-linear 1 KB blocks
@@ -54,10 +57,8 @@ struct PrepCfg {
     static constexpr int ES = sizeof(T), EV = 16 / ES;
     static constexpr int NB = C / 16;                      // 16-row blocks
     static constexpr int KS = Step<T>::KS, NKK = DK / KS;  // contraction steps over d
-    static constexpr int NKF = NB * NKK;                   // key fragments per lane
-    static constexpr bool PREFETCH = NKF <= 16;            // next unit's keys held meanwhile
     static constexpr int WAVES = kThreads / 64;
-    static constexpr int MIN_WAVES_SIMD = 1;               // register budget: 512 / this per wave
+    static constexpr int MIN_WAVES_SIMD = 2;               // register budget: 512 / this per wave
     // per-wave LDS (bytes): g, beta; the diagonal blocks of A and of T, both
     // column-major
     static constexpr int OFF_G = 0, OFF_B = 4 * C, OFF_AD = 8 * C;
@@ -86,24 +87,15 @@ __device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
     return c;
 }
 
-// An fp32 operand of one 16-deep block as the sum of two bf16 parts, hi = bf16(x)
-// and lo = bf16(x - hi); three bf16 products (lo hi, hi lo, hi hi) then give
-// the fp32 product to about 2^-16 relative, at a third of the cost of the fp32
-// instructions.
+// c += A B over one 16-deep block on bf16 products (operands rounded to bf16,
+// fp32 accumulation), layouts as for mma16_f32
 typedef short p16x4 __attribute__((ext_vector_type(4)));
-struct Split16 {
-    p16x4 hi, lo;
-};
-__device__ __forceinline__ Split16 split16(f32x4 x) {
+__device__ __forceinline__ p16x4 to_bf16x4(f32x4 x) {
     const bf16x4 h = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
-    const f32x4 r = {x[0] - (float)h[0], x[1] - (float)h[1], x[2] - (float)h[2], x[3] - (float)h[3]};
-    const bf16x4 lo = {(bf16)r[0], (bf16)r[1], (bf16)r[2], (bf16)r[3]};
-    return Split16{__builtin_bit_cast(p16x4, h), __builtin_bit_cast(p16x4, lo)};
+    return __builtin_bit_cast(p16x4, h);
 }
-__device__ __forceinline__ f32x4 mma16_x3(const Split16& a, const Split16& b, f32x4 c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mma16_bf16(p16x4 a, p16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 template <typename T, int DK, int C>
@@ -150,48 +142,19 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
                          : 0.f;
     };
 
-    // With the next unit's keys prefetched, a unit's results are held in
-    // registers and stored as the next unit starts, next to that prefetch: the
-    // wait for a unit's keys then finds the previous unit's stores long done
-    // (the compiler waits for all vector memory operations of a wave at once
-    // when loads and stores are both outstanding).
+    // block (ti, q) of a unit's Tb at out: this lane's 16 bytes
     typedef typename std::conditional<Cfg::BF, bf16x8, f32x4>::type HFrag;
     constexpr int NHQ = Cfg::BF ? NB / 2 : NB;
-    HFrag hold[NB][NHQ];
-    float hold_g[3] = {0.f, 0.f, 0.f};
-    T* hold_out = nullptr;
-    float* hold_gout = nullptr;
-    // block (ti, q) of a unit's Tb at out: this lane's 16 bytes
     auto tb_store = [&](T* out, int ti, int q, HFrag v) __attribute__((always_inline)) {
         *reinterpret_cast<HFrag*>(reinterpret_cast<unsigned char*>(out) + tb_block(ti, q, Cfg::BF) * 1024 + l * 16) = v;
     };
-    auto flush_hold = [&]() __attribute__((always_inline)) {
-        if (hold_out) {
-#pragma unroll
-            for (int ti = 0; ti < NB; ++ti)
-#pragma unroll
-                for (int q = 0; q < NHQ; ++q)
-                    if ((Cfg::BF ? 2 * q : q) <= ti) tb_store(hold_out, ti, q, hold[ti][q]);
-            if (l < C) {
-                hold_gout[l] = hold_g[0];
-                hold_gout[C + l] = hold_g[1];
-                hold_gout[2 * C + l] = hold_g[2];
-            }
-        }
-    };
 
-    // one unit whose keys are in cur (and whose gates and geometry fetch left in
-    // la_n, be_n, ci_n); starts the loads of unit u + stride into nxt
-    auto process = [&](int u, Frag (*cur)[NKK], Frag (*nxt)[NKK]) __attribute__((always_inline)) {
-        if constexpr (!Cfg::PREFETCH) fetch(cur, u);
+    // one unit: keys, gates and geometry by fetch, then the chain below
+    auto process = [&](int u, Frag (*cur)[NKK]) __attribute__((always_inline)) {
+        fetch(cur, u);
         const ChunkInfo ci = ci_n;
         float la = la_n;
         const float be = be_n;
-        if constexpr (Cfg::PREFETCH) {
-            if (u + stride < units) fetch(nxt, u + stride);
-            flush_hold();
-            hold_out = nullptr;
-        }
         if (ci.len <= 0) return;   // unused packed-batch slot (uniform)
         const int slot = u / H, h = u - slot * H;
         const int64_t unit = (int64_t)slot * H + h;
@@ -211,10 +174,7 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
             // g_i, gamma_i = exp(g_i), gamma_n / gamma_i
             float* gout = g_ws + unit * 3 * C;
             const float g3[3] = {la, __expf(la), __expf(glast - la)};
-            if constexpr (Cfg::PREFETCH) {
-                hold_gout = gout;
-                hold_g[0] = g3[0], hold_g[1] = g3[1], hold_g[2] = g3[2];
-            } else if (l < C) {
+            if (l < C) {
                 gout[l] = g3[0];
                 gout[C + l] = g3[1];
                 gout[2 * C + l] = g3[2];
@@ -303,20 +263,22 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
 #pragma unroll
             for (int r = 0; r < 4; ++r) Ta_op[b][r] = sTd[b * 256 + (4 * g + r) * 16 + n];
         }
-        // blocks below the diagonal, one block diagonal at a time.  To: accumulator
-        // layout (T[16i + 4g + r][16j + n]) for the blocks later levels take as B
-        // operands; Tr: row layout (T[16i + n][16j + 4g + r]), from
+        // blocks below the diagonal, one block diagonal at a time.  To (bf16: Tos):
+        // accumulator layout (T[16i + 4g + r][16j + n]) for the blocks later levels
+        // take as B operands; Tr: row layout (T[16i + n][16j + 4g + r]), from
         // T_ij^T = -R^T T_ii^T, for the output
-        // (bf16 inputs: on split-bf16 products, as Tb leaves in bf16 anyway)
+        // (bf16 inputs: on bf16 products -- Tb leaves rounded to bf16 anyway, and
+        // the outputs measured the same to three digits as with products of
+        // fp32 accuracy)
         f32x4 To[NB][NB], Tr[NB][NB];
         if constexpr (Cfg::BF) {
-            Split16 As[NB][NB], Tbs[NB], Tas[NB], Tos[NB][NB];
+            p16x4 As[NB][NB], Tbs[NB], Tas[NB], Tos[NB][NB];
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                Tbs[b] = split16(Tb_op[b]);
-                Tas[b] = split16(Ta_op[b]);
+                Tbs[b] = to_bf16x4(Tb_op[b]);
+                Tas[b] = to_bf16x4(Ta_op[b]);
 #pragma unroll
-                for (int m = 0; m < b; ++m) As[b][m] = split16(A[b][m]);
+                for (int m = 0; m < b; ++m) As[b][m] = to_bf16x4(A[b][m]);
             }
 #pragma unroll
             for (int d = 1; d < NB; ++d)
@@ -325,13 +287,10 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
                     const int i = j + d;
                     f32x4 R = zero4();
 #pragma unroll
-                    for (int m = j; m < i; ++m) R = mma16_x3(As[i][m], m == j ? Tbs[j] : Tos[m][j], R);
-                    const Split16 Rs = split16(R);
-                    if (i < NB - 1) {
-                        To[i][j] = -mma16_x3(Tas[i], Rs, zero4());
-                        Tos[i][j] = split16(To[i][j]);
-                    }
-                    Tr[i][j] = -mma16_x3(Rs, Tas[i], zero4());
+                    for (int m = j; m < i; ++m) R = mma16_bf16(As[i][m], m == j ? Tbs[j] : Tos[m][j], R);
+                    const p16x4 Rb = to_bf16x4(R);
+                    if (i < NB - 1) Tos[i][j] = to_bf16x4(-mma16_bf16(Tas[i], Rb, zero4()));
+                    Tr[i][j] = -mma16_bf16(Rb, Tas[i], zero4());
                 }
         } else {
 #pragma unroll
@@ -369,27 +328,14 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
                 } else {
                     o = trow(ti, q);
                 }
-                if constexpr (Cfg::PREFETCH) hold[ti][q] = o;
-                else tb_store(out, ti, q, o);
+                tb_store(out, ti, q, o);
             }
         }
-        if constexpr (Cfg::PREFETCH) hold_out = out;
         wave_lds_sync();   // before the next unit overwrites what was read
     };
 
-    int u = blockIdx.x * Cfg::WAVES + w;
-    if constexpr (Cfg::PREFETCH) {
-        Frag ka[NB][NKK], kb[NB][NKK];
-        if (u < units) fetch(ka, u);
-        for (; u < units; u += 2 * stride) {
-            process(u, ka, kb);
-            if (u + stride < units) process(u + stride, kb, ka);
-        }
-        flush_hold();
-    } else {
-        Frag ka[NB][NKK];
-        for (; u < units; u += stride) process(u, ka, ka);
-    }
+    Frag kf[NB][NKK];
+    for (int u = blockIdx.x * Cfg::WAVES + w; u < units; u += stride) process(u, kf);
 }
 
 }  // namespace gdn
