@@ -12,7 +12,9 @@ resident in HBM.  Prints ONE JSON line.
   cpu_baseline  the fp64 oracle on the host cores over the same inputs
 
 Options: --gpus (only 1), --steps, --warmup, --workload, --no-flush,
---profile-steps, --cpu-sample (heads per batch row the oracle runs on, 0 = skip).
+--profile-steps, --cpu-sample (heads per batch row the oracle runs on, 0 = skip),
+--recurrent N (instead: the single-token step, gdn_recurrent_step, over a decode
+batch of N sequences with the workload's H, Dk, Dv and dtype; its own JSON line).
 """
 from __future__ import annotations
 
@@ -126,6 +128,58 @@ def cpu_baseline(inp, heads_per_row: int):
                       f"{dt:.2f} s wall on {nt} threads); tokens/s scaled by {len(hs)}/{H}"}
 
 
+def bench_recurrent(args, w):
+    """Tokens/s of the single-token step over a decode batch: N sequences of one
+    token, H heads, the state read and written in place each step (HBM-bound:
+    2 Dv Dk 4 bytes of state per sequence-head and token)."""
+    import torch
+    import gated_delta_rule_16_amd as gdn
+    from gated_delta_rule_16_amd.inputs import make_inputs
+    N, H = args.recurrent, w.H
+    inp = make_inputs(B=N, T=1, H=H, Dk=w.Dk, Dv=w.Dv, dtype=w.dtype, gated=True, s0=True, seed=71)
+    dev = torch.device("cuda:0")
+    d = inp.to(dev)
+    q, k, v = (t[:, 0].contiguous() for t in (d.q, d.k, d.v))
+    la, be = d.log_alpha[:, 0].contiguous(), d.beta[:, 0].contiguous()
+    S = d.S0.clone()
+    o = torch.empty(N, H, w.Dv, device=dev, dtype=q.dtype)
+    flush = None if args.no_flush else torch.zeros(512 << 18, device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.sum()
+        gdn.gdn_recurrent_step(q, k, v, la, be, S, o=o, stream=stream)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.sum()
+        starts[i].record(stream)
+        gdn.gdn_recurrent_step(q, k, v, la, be, S, o=o, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms = statistics.mean(step_ms)
+    s_in = 2 if w.dtype == "bf16" else 4
+    nbytes = N * H * (2 * w.Dv * w.Dk * 4 + (2 * w.Dk + 2 * w.Dv) * s_in + 8)
+    flops = N * H * 8 * w.Dv * w.Dk
+    rl = roofline("recurrent_step", nbytes, flops, ms / 1e3, w.dtype)
+    out = {
+        "metric": "tokens/sec gated-DeltaNet single-token step (decode)", "value": round(N / (ms / 1e3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"decode_n{N}_h{H}_dk{w.Dk}_dv{w.Dv}", "N": N, "H": H, "Dk": w.Dk,
+                   "Dv": w.Dv, "state": "fp32", "flush_l2_mall": flush is not None},
+        "roofline": rl,
+        "step_ms": {"median": round(statistics.median(step_ms), 5), "min": round(min(step_ms), 5),
+                    "max": round(max(step_ms), 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +194,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="after timing, copy an MB-megabyte buffer a few times (a plain copy "
                          "kernel of known traffic, the scale for hardware byte counters)")
+    ap.add_argument("--recurrent", type=int, default=0, metavar="N",
+                    help="time gdn_recurrent_step over N sequences instead (one token each)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -153,6 +209,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     w = WORKLOADS[args.workload]
+    if args.recurrent > 0:
+        bench_recurrent(args, w)
+        return
     inp = workload_inputs(args.workload)
     dev = torch.device("cuda:0")
     d = inp.to(dev)

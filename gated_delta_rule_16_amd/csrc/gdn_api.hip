@@ -362,7 +362,7 @@ namespace {
 template <typename T, int DK, int DV>
 gdn_status launch_step(const void* q, const void* k, const void* v, const float* la,
                        const float* beta, float* S, void* o, int N, int H, hipStream_t st) {
-    hipLaunchKernelGGL((gdn_step_kernel<T, DK, DV>), dim3(DV / 16, H, N), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((gdn_step_kernel<T, DK, DV>), dim3(DV / StepCfg<DK, DV>::RPW, H, N), dim3(64), 0, st,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                        la, beta, S, static_cast<T*>(o), H);
     return check_launch(st);
@@ -403,7 +403,7 @@ extern "C" gdn_status gdn_recurrent_step(const void* q, const void* k, const voi
         if (!q || !k || !v || !beta || !S || !o) return GDN_ERR_NULL;
         if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
         if (N < 1 || N > 65535 || H < 1 || H > 65535 || Dk < 1 || Dv < 1) return GDN_ERR_SHAPE;
-        if ((int64_t)N * H * Dv * Dk > kMaxElems) return GDN_ERR_SHAPE;
+        if ((int64_t)N * H * Dv * Dk > kMaxElems || !aligned16(S)) return GDN_ERR_SHAPE;
         StepFn fn = dt == GDN_BF16 ? pick_step<bf16>(Dk, Dv) : pick_step<float>(Dk, Dv);
         if (!fn) return GDN_ERR_UNSUPPORTED;
         (void)hipGetLastError();

@@ -13,53 +13,75 @@
 
 namespace gdn {
 
-// One wave per state row; ROWS rows per workgroup.  Lanes stride over Dk.
+// Layout of the step: a workgroup is one wave and owns RPW consecutive rows of
+// one state.  A row of Dk fp32 values is LPR lanes of 16 bytes, so one load
+// instruction reads RPI = 64 / LPR whole rows (contiguous, as rows are), and a
+// wave issues all NI loads of its rows before it uses any: NI KB in flight per
+// wave, the step being a stream through the state.
+template <int DK, int DV>
+struct StepCfg {
+    static constexpr int LPR = DK / 4;                  // lanes per row
+    static constexpr int RPI = 64 / LPR;                // rows per load instruction
+    static constexpr int NI = DV / RPI < 8 ? DV / RPI : 8;
+    static constexpr int RPW = NI * RPI;                // rows per wave (= per workgroup)
+    static_assert(DK % 4 == 0 && 64 % LPR == 0 && NI >= 1 && DV % RPW == 0, "step tiling");
+};
+
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void gdn_step_kernel(
+__global__ __launch_bounds__(64) void gdn_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     float* __restrict__ S, T* __restrict__ o, int H) {
-    constexpr int ROWS_PER_WAVE = 4;
-    constexpr int ROWS = 4 * ROWS_PER_WAVE;
-    constexpr int PER_LANE = (DK + 63) / 64;
-    static_assert(DV % ROWS == 0, "Dv must be a multiple of 16");
+    using Cfg = StepCfg<DK, DV>;
+    constexpr int LPR = Cfg::LPR, RPI = Cfg::RPI, NI = Cfg::NI;
     const int h = blockIdx.y, seq = blockIdx.z;
-    const int l = lane_id(), w = wave_id();
+    const int l = lane_id();
+    const int ri = l / LPR, c4 = (l % LPR) * 4;         // row within an instruction, first d
     const int64_t x = (int64_t)seq * H + h;
+    const int row0 = blockIdx.x * Cfg::RPW + ri;
+    float* Sx = S + x * DV * DK + c4;
+    // the rows first: NI loads of 16 bytes per lane
+    f32x4 s[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) s[i] = *reinterpret_cast<const f32x4*>(Sx + (int64_t)(row0 + i * RPI) * DK);
+    float vr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vr[i] = to_f32(v[x * DV + row0 + i * RPI]);
     const float a = log_alpha ? __expf(log_alpha[x]) : 1.f;
     const float b = beta[x];
-    float kr[PER_LANE], qr[PER_LANE];
+    f32x4 kr, qr;
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-        const int d = l + 64 * j;
-        kr[j] = d < DK ? to_f32(k[x * DK + d]) : 0.f;
-        qr[j] = d < DK ? to_f32(q[x * DK + d]) : 0.f;
+    for (int e = 0; e < 4; ++e) {
+        kr[e] = to_f32(k[x * DK + c4 + e]);
+        qr[e] = to_f32(q[x * DK + c4 + e]);
     }
-    for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
-        const int row = blockIdx.x * ROWS + w * ROWS_PER_WAVE + rr;
-        float* Srow = S + (x * DV + row) * DK;
-        float s[PER_LANE];
-        float p = 0.f;
+    // p = (a S) k over the LPR lanes of each row
+    float p[NI];
 #pragma unroll
-        for (int j = 0; j < PER_LANE; ++j) {
-            const int d = l + 64 * j;
-            s[j] = d < DK ? a * Srow[d] : 0.f;
-            p += s[j] * kr[j];
-        }
+    for (int i = 0; i < NI; ++i) {
+        s[i] *= a;
+        p[i] = s[i][0] * kr[0] + s[i][1] * kr[1] + s[i][2] * kr[2] + s[i][3] * kr[3];
+    }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off, 64);
-        const float e = b * (to_f32(v[x * DV + row]) - p);
-        float ov = 0.f;
+    for (int off = LPR / 2; off > 0; off >>= 1)
 #pragma unroll
-        for (int j = 0; j < PER_LANE; ++j) {
-            const int d = l + 64 * j;
-            s[j] += e * kr[j];
-            ov += s[j] * qr[j];
-            if (d < DK) Srow[d] = s[j];
-        }
+        for (int i = 0; i < NI; ++i) p[i] += __shfl_xor(p[i], off, 64);
+    // S = a S + beta (v - p) k^T, then o = S q
+    float ov[NI];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) ov += __shfl_xor(ov, off, 64);
-        if (l == 0) o[x * DV + row] = from_f32<T>(ov);
+    for (int i = 0; i < NI; ++i) {
+        const float e = b * (vr[i] - p[i]);
+        s[i] += e * kr;
+        ov[i] = s[i][0] * qr[0] + s[i][1] * qr[1] + s[i][2] * qr[2] + s[i][3] * qr[3];
+        *reinterpret_cast<f32x4*>(Sx + (int64_t)(row0 + i * RPI) * DK) = s[i];
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) ov[i] += __shfl_xor(ov[i], off, 64);
+    if (l % LPR == 0) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) o[x * DV + row0 + i * RPI] = from_f32<T>(ov[i]);
     }
 }
 

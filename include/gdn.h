@@ -129,7 +129,8 @@ gdn_status gdn_chunk_fwd_profiled(const void *q, const void *k, const void *v,
  *     S <- alpha S (I - beta k k^T) + beta v k^T,   o = S q     (same section).
  *  q, k [N][H][Dk] in dt; v [N][H][Dv] in dt; log_alpha (nullable: alpha = 1)
  *  and beta [N][H] fp32; S [N][H][Dv][Dk] fp32, read and written in place;
- *  o [N][H][Dv] in dt.
+ *  o [N][H][Dv] in dt.  S must be 16-byte aligned (its rows are read and
+ *  written as 16-byte pieces; GDN_ERR_SHAPE otherwise).
  * Supported (Dk, Dv): any with Dk, Dv in {16, 64, 128, 256}, both dtypes.
  * Errors: GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_HIP. */
 gdn_status gdn_recurrent_step(const void *q, const void *k, const void *v,

@@ -113,6 +113,7 @@ def test_recurrent_step_argument_errors(lib):
     assert f(p, p, p, None, p, p, p, 0, 1, 16, 16, F32, None) == GDN_ERR_SHAPE
     assert f(p, p, p, None, p, p, p, 1, 1, 48, 16, F32, None) == GDN_ERR_UNSUPPORTED
     assert f(p, p, p, None, p, p, p, 1, 1, 16, 16, 9, None) == GDN_ERR_UNSUPPORTED
+    assert f(p, p, p, None, p, ctypes.c_void_p((1 << 20) + 4), p, 1, 1, 16, 16, F32, None) == GDN_ERR_SHAPE
 
 
 def test_python_binding_fails_loudly_without_gpu_tensors(lib):

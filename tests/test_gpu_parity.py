@@ -235,6 +235,21 @@ def test_recurrent_step(dtype, Dk, Dv, gated):
     assert rel(S.double().cpu().numpy(), Sr) <= 1e-5
 
 
+def test_recurrent_step_decode_batch():
+    """The decode batch that bench.py --recurrent 64 times: N = 64 sequences, H = 16,
+    Dk = Dv = 128, bf16, every workgroup of the launch."""
+    inp = make_inputs(B=64, T=1, H=16, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True, seed=71)
+    Or, Sr = run_oracle(inp)
+    d = inp.to(DEV)
+    S = d.S0.clone()
+    o = gdn.gdn_recurrent_step(d.q[:, 0].contiguous(), d.k[:, 0].contiguous(), d.v[:, 0].contiguous(),
+                               d.log_alpha[:, 0].contiguous(), d.beta[:, 0].contiguous(), S)
+    torch.cuda.synchronize()
+    eo, es = rel(o.double().cpu().numpy(), Or[:, 0]), rel(S.double().cpu().numpy(), Sr)
+    say(f"[gpu] decode batch 64x16 D128 bf16: o {eo:.3e}  S {es:.3e}")
+    assert eo <= TOL["bf16"] and es <= 1e-5
+
+
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
 def test_prefill_then_decode(dtype, D):
     T = 150
