@@ -165,6 +165,24 @@ def test_bitwise_deterministic():
     assert np.array_equal(O1, O2) and np.array_equal(S1, S2)
 
 
+def test_workspace_reused_across_inputs():
+    """One workspace, filled with 0xff bytes first, serves calls on different
+    inputs in turn: each call's results match the oracle, so nothing a previous
+    call left there (Tb, gates) reaches the next one."""
+    ins = [make_inputs(B=2, T=700, H=8, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True, seed=s)
+           for s in (81, 82)]
+    nbytes = gdn.gdn_chunk_fwd_workspace_bytes(2, 700, 8, 128, 128, 64, 0, torch.bfloat16)
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device=DEV)
+    refs = [run_oracle(x) for x in ins]
+    for i in (0, 1, 0):
+        d = ins[i].to(DEV)
+        O, S = gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, chunk_size=64, workspace=ws)
+        torch.cuda.synchronize()
+        eo, es = rel(O.double().cpu().numpy(), refs[i][0]), rel(S.double().cpu().numpy(), refs[i][1])
+        say(f"[gpu] workspace reuse, inputs {i}: O {eo:.3e}  S_T {es:.3e}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_chunk_size_invariance_f32():
     inp = make_inputs(B=2, T=333, H=2, Dk=64, Dv=64, dtype="f32", gated=True, s0=True, seed=9)
     O16, S16 = run_gpu(inp, 16)
