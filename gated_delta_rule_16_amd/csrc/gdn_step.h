@@ -144,17 +144,24 @@ __global__ __launch_bounds__(kTableThreads) void gdn_chunk_table_kernel(
     if (tid == 0) seq_slot[n_seqs] = carry;
     __syncthreads();
     const int total = carry;
-    // phase 3: fill the table
+    // phase 3: fill the table, one slot per thread: its sequence is the last i
+    // with seq_slot[i] <= slot (binary search; empty sequences own no slot)
     int4* tab = reinterpret_cast<int4*>(table);
-    for (int i = tid; i < n_seqs; i += kTableThreads) {
-        const int s0 = seq_slot[i], t0 = bounds[i], t1 = bounds[i + 1];
-        for (int c = 0; t0 + c * C < t1; ++c) {
-            const int st = t0 + c * C;
-            const int len = (t1 - st) < C ? (t1 - st) : C;
-            tab[s0 + c] = make_int4(i, st, len, 0);
+    for (int s = tid; s < max_slots; s += kTableThreads) {
+        if (s >= total) {
+            tab[s] = make_int4(0, 0, 0, 0);
+            continue;
         }
+        int lo = 0, hi = n_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seq_slot[mid] <= s) lo = mid;
+            else hi = mid - 1;
+        }
+        const int st = bounds[lo] + (s - seq_slot[lo]) * C;
+        const int len = (bounds[lo + 1] - st) < C ? (bounds[lo + 1] - st) : C;
+        tab[s] = make_int4(lo, st, len, 0);
     }
-    for (int s = total + tid; s < max_slots; s += kTableThreads) tab[s] = make_int4(0, 0, 0, 0);
 }
 
 }  // namespace gdn
