@@ -22,7 +22,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16 raw bytes
 
-constexpr int kThreads = 256;   // 4 waves per workgroup (prep, step)
+constexpr int kThreads = 256;   // 4 waves per workgroup (prep)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // wave index, known to the compiler to be uniform across the wave
