@@ -124,3 +124,15 @@ def test_python_binding_fails_loudly_without_gpu_tensors(lib):
     with pytest.raises(ValueError):
         gdn.gdn_chunk_fwd(x, x, x, None, b, chunk_size=16, workspace=None,
                           O=torch.zeros(1, 16, 1, 16), S_T=torch.zeros(1, 1, 16, 16))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says so
+    (before touching any device)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
