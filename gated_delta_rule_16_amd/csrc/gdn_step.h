@@ -93,29 +93,51 @@ __global__ __launch_bounds__(64) void gdn_step_kernel(
 // Scratch: bounds[N+1] holds c'.
 constexpr int kTableThreads = 1024;
 
+// Inclusive scan over the workgroup (max when MAX, else sum): each wave by
+// shuffles, then the 16 wave totals by the first wave; wsum holds 16 ints.
+template <bool MAX>
+__device__ __forceinline__ int block_scan(int x, int* wsum) {
+    const int l = lane_id(), w = threadIdx.x >> 6;
+    auto op = [](int a, int b) { return MAX ? (a > b ? a : b) : a + b; };
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (l >= off) x = op(x, y);
+    }
+    if (l == 63) wsum[w] = x;
+    __syncthreads();
+    if (w == 0) {
+        int t = l < kTableThreads / 64 ? wsum[l] : 0;
+#pragma unroll
+        for (int off = 1; off < kTableThreads / 64; off <<= 1) {
+            const int y = __shfl_up(t, off, 64);
+            if (l >= off) t = op(t, y);
+        }
+        if (l < kTableThreads / 64) wsum[l] = t;
+    }
+    __syncthreads();
+    if (w > 0) x = op(x, wsum[w - 1]);
+    __syncthreads();   // wsum free for the next scan
+    return x;
+}
+
 __global__ __launch_bounds__(kTableThreads) void gdn_chunk_table_kernel(
     const int* __restrict__ cu, int n_seqs, int T, int C, int max_slots,
     int* __restrict__ bounds, int* __restrict__ seq_slot, int* __restrict__ table) {
-    __shared__ int sbuf[kTableThreads];
+    __shared__ int wsum[kTableThreads / 64];
     __shared__ int carry;
     const int tid = threadIdx.x;
-    // phase 1: running max of cu, clamped to [0, T]
+    // phase 1: running max of cu, clamped to [0, T] (values are >= 0, so 0 is
+    // the identity of the max)
     if (tid == 0) carry = 0;
     __syncthreads();
     for (int base = 0; base <= n_seqs; base += kTableThreads) {
         const int i = base + tid;
         int x = (i <= n_seqs) ? cu[i] : 0;
         x = x < 0 ? 0 : (x > T ? T : x);
-        sbuf[tid] = x;
-        __syncthreads();
-        for (int off = 1; off < kTableThreads; off <<= 1) {
-            const int y = tid >= off ? sbuf[tid - off] : 0;
-            __syncthreads();
-            if (y > sbuf[tid]) sbuf[tid] = y;
-            __syncthreads();
-        }
+        x = block_scan<true>(x, wsum);
         const int c0 = carry;
-        const int val = sbuf[tid] > c0 ? sbuf[tid] : c0;
+        const int val = x > c0 ? x : c0;
         if (i <= n_seqs) bounds[i] = val;
         __syncthreads();
         if (tid == kTableThreads - 1) carry = val;
@@ -127,18 +149,11 @@ __global__ __launch_bounds__(kTableThreads) void gdn_chunk_table_kernel(
     for (int base = 0; base < n_seqs; base += kTableThreads) {
         const int i = base + tid;
         const int cnt = (i < n_seqs) ? (bounds[i + 1] - bounds[i] + C - 1) / C : 0;
-        sbuf[tid] = cnt;
-        __syncthreads();
-        for (int off = 1; off < kTableThreads; off <<= 1) {
-            const int y = tid >= off ? sbuf[tid - off] : 0;
-            __syncthreads();
-            sbuf[tid] += y;
-            __syncthreads();
-        }
+        const int inc = block_scan<false>(cnt, wsum);
         const int c0 = carry;
-        if (i < n_seqs) seq_slot[i] = c0 + sbuf[tid] - cnt;
+        if (i < n_seqs) seq_slot[i] = c0 + inc - cnt;
         __syncthreads();
-        if (tid == kTableThreads - 1) carry = c0 + sbuf[tid];
+        if (tid == kTableThreads - 1) carry = c0 + inc;
         __syncthreads();
     }
     if (tid == 0) seq_slot[n_seqs] = carry;
