@@ -1,5 +1,6 @@
 // gdn_device.h -- device-side building blocks shared by the gfx950 kernels:
-// element types, 16x16 MFMA tiles, LDS fragment loaders and chunk metadata.
+// element types, 16x16 MFMA contraction steps, buffer resources, LDS swizzles,
+// the Tb block layout and chunk metadata.
 //
 // MFMA tile conventions (wave64, 16x16 output tile):
 //   lane l = 0..63, column/row index inside the tile  n = l & 15,  lane group g = l >> 4.
@@ -7,8 +8,9 @@
 //   B fragment: B[k0 + g*KPL + e][n0 + n]
 //   D (4 fp32 per lane): D[4g + r][n], r = 0..3
 // bf16 uses v_mfma_f32_16x16x32_bf16 (KPL = 8), fp32 uses v_mfma_f32_16x16x4_f32
-// (KPL = 1).  A and B fragments assign contraction indices to (g, e) the same
-// way, so the product does not depend on how the hardware orders them.
+// (KPL = 1, four per 16-deep step).  A and B fragments assign contraction
+// indices to (g, e) the same way, so the product does not depend on how the
+// hardware orders them.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,26 +29,6 @@ constexpr int kThreads = 256;   // 4 waves per workgroup (prep)
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // wave index, known to the compiler to be uniform across the wave
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-template <typename T> struct Mfma;
-
-template <> struct Mfma<bf16> {
-    static constexpr int KS = 32;   // contraction length of one instruction
-    static constexpr int KPL = 8;   // contraction values held per lane
-    typedef bf16x8 frag;
-    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-};
-
-template <> struct Mfma<float> {
-    static constexpr int KS = 4;
-    static constexpr int KPL = 1;
-    typedef float frag;
-    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-    }
-};
 
 // One 16-byte step of a contraction along the rows of two row-major operands:
 // lane (g, n) holds elements [k0 + g*EV, k0 + (g+1)*EV) of row n (EV = 16 / sizeof(T)).
@@ -76,35 +58,6 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
-
-// Fragment whose contraction index is contiguous in memory:
-// element (mn, k) at p[mn * ld + k].  Serves A (mn = row) and B^T (mn = column).
-template <typename T>
-__device__ __forceinline__ typename Mfma<T>::frag frag_kc(const T* p, int ld, int mn0, int k0) {
-    const int l = lane_id();
-    const T* q = p + (mn0 + (l & 15)) * ld + k0 + (l >> 4) * Mfma<T>::KPL;
-    if constexpr (Mfma<T>::KPL == 8) {
-        return *reinterpret_cast<const bf16x8*>(q);
-    } else {
-        return *q;
-    }
-}
-
-// Fragment whose contraction index is the row of a row-major array:
-// element (k, mn) at p[k * ld + mn].  Gathers KPL scalars per lane.
-template <typename T>
-__device__ __forceinline__ typename Mfma<T>::frag frag_ks(const T* p, int ld, int k0, int mn0) {
-    const int l = lane_id();
-    const T* q = p + (k0 + (l >> 4) * Mfma<T>::KPL) * ld + mn0 + (l & 15);
-    if constexpr (Mfma<T>::KPL == 8) {
-        bf16x8 f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = q[e * ld];
-        return f;
-    } else {
-        return *q;
-    }
-}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -196,49 +149,6 @@ __device__ __forceinline__ ChunkInfo chunk_info(const SeqGeom& g, int slot) {
         ci.len = rem < g.C ? rem : g.C;
     }
     return ci;
-}
-
-__device__ __forceinline__ void seq_slots(const SeqGeom& g, int seq, int& first, int& count) {
-    if (g.table) {
-        first = g.seq_slot[seq];
-        count = g.seq_slot[seq + 1] - first;
-    } else {
-        first = seq * g.chunks_per_seq;
-        count = g.chunks_per_seq;
-    }
-}
-
-// Copies a [rows x D] tile of token-major input (row r = token t0 + r of head h)
-// into LDS with leading dimension ldl, zero-filling rows >= len.
-// src points at element (token 0, head 0, 0) and the token stride is H * D.
-template <typename T, int D, int NTHR>
-__device__ __forceinline__ void stage_tokens(T* dst, int ldl, const T* src, int t0, int len,
-                                             int rows, int H, int h) {
-    constexpr int V = 16 / sizeof(T);           // elements per 16-byte vector
-    constexpr int VPR = D / V;                  // vectors per row
-    static_assert(D % V == 0, "row must be a whole number of 16-byte vectors");
-    for (int i = threadIdx.x; i < rows * VPR; i += NTHR) {
-        const int r = i / VPR, c = (i - r * VPR) * V;
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if (r < len) {
-            const int64_t off = ((int64_t)(t0 + r) * H + h) * D + c;
-            val = *reinterpret_cast<const uint4*>(src + off);
-        }
-        *reinterpret_cast<uint4*>(dst + r * ldl + c) = val;
-    }
-}
-
-// Copies a dense [rows x D] tile (row stride ld_src elements) into LDS.
-template <typename T, int D, int NTHR>
-__device__ __forceinline__ void stage_dense(T* dst, int ldl, const T* src, int64_t ld_src, int rows) {
-    constexpr int V = 16 / sizeof(T);
-    constexpr int VPR = D / V;
-    static_assert(D % V == 0, "row must be a whole number of 16-byte vectors");
-    for (int i = threadIdx.x; i < rows * VPR; i += NTHR) {
-        const int r = i / VPR, c = (i - r * VPR) * V;
-        *reinterpret_cast<uint4*>(dst + r * ldl + c) =
-            *reinterpret_cast<const uint4*>(src + (int64_t)r * ld_src + c);
-    }
 }
 
 }  // namespace gdn
