@@ -118,7 +118,9 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
     const int64_t rs_k = (int64_t)H * DK * ES;
     const int stride = (int)gridDim.x * Cfg::WAVES;
 
-    // keys and gates of unit u into registers (rows past the chunk end read as 0)
+    // gates and keys of unit u into registers (rows past the chunk end read as
+    // 0); the gates first, so that their prefix sum is done by the time the
+    // keys have landed
     float la_n = 0.f, be_n = 0.f;
     ChunkInfo ci_n{};
     auto fetch = [&](Frag (*dst)[NKK], int u) __attribute__((always_inline)) {
@@ -127,6 +129,14 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
         const int len = ci_n.len;
         const int64_t row0 = (int64_t)ci_n.t0 * H + h;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + row0 * DK, len > 0 ? (len - 1) * rs_k + DK * ES : 0);
+        {
+            const int64_t gbytes = len > 0 ? ((int64_t)(len - 1) * H + 1) * 4 : 0;
+            const uint32_t goff = l < C ? (uint32_t)(l * H * 4) : kOutOfRange;
+            be_n = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(beta + row0, gbytes), goff, 0, 0));
+            la_n = log_alpha ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                   make_rsrc(log_alpha + row0, gbytes), goff, 0, 0))
+                             : 0.f;
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -134,12 +144,6 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
                 dst[b][kk] = __builtin_bit_cast(
                     Frag, __builtin_amdgcn_raw_buffer_load_b128(
                               rk, (uint32_t)((b * 16 + n) * rs_k) + kk * KS * ES + g * 16, 0, 0));
-        const int64_t gbytes = len > 0 ? ((int64_t)(len - 1) * H + 1) * 4 : 0;
-        const uint32_t goff = l < C ? (uint32_t)(l * H * 4) : kOutOfRange;
-        be_n = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(beta + row0, gbytes), goff, 0, 0));
-        la_n = log_alpha ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                               make_rsrc(log_alpha + row0, gbytes), goff, 0, 0))
-                         : 0.f;
     };
 
     // block (ti, q) of a unit's Tb at out: this lane's 16 bytes
