@@ -284,7 +284,8 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     const bool has_tokens = T > 0;
     if (has_tokens && (!q || !k || !v || !beta || !O)) return GDN_ERR_NULL;
     if (gdn_status s = check_sizes(B, T, H, Dk, Dv, C, varlen, n_seqs, dt)) return s;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(workspace))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(workspace) ||
+        !aligned16(S0) || !aligned16(S_T))
         return GDN_ERR_SHAPE;
     const Layout L = make_layout(B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt));
     if (L.total > 0 && !workspace) return GDN_ERR_NULL;

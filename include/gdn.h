@@ -77,6 +77,8 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
  *              NULL means alpha = 1 (DeltaNet).
  *  beta        [B][T][H] fp32, per-token write strength (not clamped).
  *  S0          [N][H][Dv][Dk] fp32 initial states; NULL means zero states.
+ *              S0 and S_T are read and written in 16-byte pieces and must be
+ *              16-byte aligned.
  *  cu_seqlens  NULL: the batch is N = B sequences of T tokens each.
  *              Otherwise a DEVICE int32 array [n_seqs + 1] of prefix offsets of
  *              n_seqs sequences packed along T (B must be 1, N = n_seqs):
@@ -91,7 +93,7 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
  *              may equal S0 (updated in place).
  *  C           chunk size (16 or 64, see the instantiation list).
  *  workspace   device buffer of at least gdn_chunk_fwd_workspace_bytes(...)
- *              bytes, 256-byte aligned; its contents on entry are ignored and on
+ *              bytes, 16-byte aligned; its contents on entry are ignored and on
  *              return hold intermediates (no stable layout).  Two calls that
  *              overlap in time must not share a workspace.
  *  stream      hipStream_t to enqueue on.
@@ -100,7 +102,7 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
  * Errors: GDN_ERR_NULL (q, k, v, beta, O or workspace NULL), GDN_ERR_SHAPE
  * (B, H < 1, T < 0, n_seqs < 1 or B != 1 with cu_seqlens, more than 2^31-1
  * elements in a tensor, C * H * max(Dk, Dv) * element size above 2^31-1 bytes,
- * q/k/v/O/workspace not 16-byte aligned),
+ * q/k/v/O/S0/S_T/workspace not 16-byte aligned),
  * GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP. */
 gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
                          const float *log_alpha, const float *beta, const float *S0,

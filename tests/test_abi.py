@@ -100,6 +100,8 @@ def test_chunk_fwd_argument_errors(lib):
     assert _fwd(lib, dt=5) == GDN_ERR_UNSUPPORTED
     assert _fwd(lib, wsb=16) == GDN_ERR_WORKSPACE
     assert _fwd(lib, q=ctypes.c_void_p((1 << 20) + 4)) == GDN_ERR_SHAPE      # misaligned
+    assert _fwd(lib, S0=ctypes.c_void_p((1 << 20) + 4)) == GDN_ERR_SHAPE
+    assert _fwd(lib, S_T=ctypes.c_void_p((1 << 20) + 8)) == GDN_ERR_SHAPE
     need = lib.gdn_chunk_fwd_workspace_bytes(1, 128, 1, 16, 16, 16, 0, F32)
     assert _fwd(lib, wsb=need - 1) == GDN_ERR_WORKSPACE
 
