@@ -7,6 +7,7 @@
 //   scan  (Dv slice, head, sequence)    O, S_T                 (serial over chunks)
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -78,19 +79,27 @@ Layout make_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int6
     return L;
 }
 
-// Compute units of the current device (queried once per device).
-int device_cu_count() {
-    static int cached[64] = {0};
+// Per-device caches of launch queries, safe for calls from several host
+// threads (a value is the same whichever thread stores it); devices past the
+// table are queried on every call.
+constexpr int kMaxCachedDevices = 64;
+int current_device() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    if (dev >= 64) dev = 63;
-    if (cached[dev] <= 0) {
-        int n = 0;
+    return dev;
+}
+
+// Compute units of the current device.
+int device_cu_count() {
+    static std::atomic<int> cached[kMaxCachedDevices] = {};
+    const int dev = current_device();
+    int n = dev < kMaxCachedDevices ? cached[dev].load(std::memory_order_relaxed) : 0;
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        if (dev < kMaxCachedDevices) cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // Raises the dynamic LDS limit of one kernel instantiation once (gfx950
@@ -109,19 +118,17 @@ void allow_smem(size_t bytes) {
 // once (occupancy query, cached per kernel and device; at least 1).
 template <auto Kernel>
 int resident_per_cu(int threads, size_t smem) {
-    static int cached[64] = {0};
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    int& c = cached[dev & 63];
-    if (c == 0) {
-        int nb = 0;
+    static std::atomic<int> cached[kMaxCachedDevices] = {};
+    const int dev = current_device();
+    int nb = dev < kMaxCachedDevices ? cached[dev].load(std::memory_order_relaxed) : 0;
+    if (nb <= 0) {
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(Kernel), threads, smem) !=
                 hipSuccess ||
             nb < 1)
             nb = 1;
-        c = nb;
+        if (dev < kMaxCachedDevices) cached[dev].store(nb, std::memory_order_relaxed);
     }
-    return c;
+    return nb;
 }
 
 // Optional per-kernel timing: events recorded on the launch stream around each
