@@ -137,6 +137,22 @@ def test_varlen_packed(dtype, Dk, Dv):
     check(inp, dtype, C=64, tag=f"varlen {lengths}")
 
 
+@pytest.mark.parametrize("dtype,D,C", [("f32", 16, 16), ("bf16", 128, 64)])
+def test_varlen_many_sequences(dtype, D, C):
+    # more sequences than the chunk table's workgroup covers in one pass (1024),
+    # so its running maximum, chunk-count prefix sum and slot search carry
+    # across passes; every third sequence is empty and most are shorter than
+    # a chunk
+    rng = np.random.default_rng(2500 + D)
+    lengths = [int(x) for x in rng.integers(1, 40, size=2500)]
+    for i in range(0, len(lengths), 3):
+        lengths[i] = 0
+    lengths[1], lengths[2047] = 300, 5 * C + 3   # several chunks with a ragged tail
+    inp = make_inputs(B=1, T=sum(lengths), H=2, Dk=D, Dv=D, dtype=dtype, gated=True, s0=True,
+                      seed=79, lengths=lengths)
+    check(inp, dtype, C=C, tag=f"varlen {len(lengths)} sequences")
+
+
 def test_varlen_equals_separate_calls():
     lengths = [100, 37, 256]
     inp = make_inputs(B=1, T=sum(lengths), H=4, Dk=128, Dv=128, dtype="bf16", gated=True,
