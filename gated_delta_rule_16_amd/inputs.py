@@ -68,7 +68,8 @@ _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 @dataclass
 class GdnInputs:
-    """CPU tensors of one call. Token-major layout [B, T, H, D]."""
+    """Tensors of one call (on the CPU unless drawn on a device). Token-major
+    layout [B, T, H, D]."""
     q: torch.Tensor
     k: torch.Tensor
     v: torch.Tensor
@@ -109,35 +110,48 @@ def _unit_norm(x: torch.Tensor) -> torch.Tensor:
 def make_inputs(B: int, T: int, H: int, Dk: int, Dv: int, *, dtype: str = "bf16",
                 gated: bool = True, s0: bool = True, seed: int = 0, C: int = 64,
                 lengths: Optional[list[int]] = None, normalize_qk: bool = True,
-                beta_fill: Optional[float] = None) -> GdnInputs:
+                beta_fill: Optional[float] = None, device: str = "cpu") -> GdnInputs:
     """Draw one call's inputs.
 
     With ``lengths`` the batch is packed: B must be 1, T must equal
     sum(lengths), and ``cu_seqlens`` holds the prefix offsets.
-    ``beta_fill`` replaces the drawn beta by a constant (special cases)."""
-    g = torch.Generator().manual_seed(seed)
+    ``beta_fill`` replaces the drawn beta by a constant (special cases).
+    ``device`` draws the tensors there, from that device's generator (same
+    distributions, other values than a CPU draw of the same seed): for inputs
+    too large to draw on the host in reasonable time."""
+    g = torch.Generator(device=device).manual_seed(seed)
     td = _TORCH_DTYPE[dtype]
     if lengths is not None:
         assert B == 1 and sum(lengths) == T
         cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
         cu[1:] = torch.tensor(lengths, dtype=torch.int64).cumsum(0).to(torch.int32)
+        cu = cu.to(device)
         N = len(lengths)
     else:
         cu, N = None, B
-    q = torch.randn(B, T, H, Dk, generator=g)
-    k = torch.randn(B, T, H, Dk, generator=g)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=device)
+
+    # q and k rounded as soon as they are drawn: on a device the fp32 draws of
+    # the largest inputs are the bulk of the memory
+    q = randn(B, T, H, Dk)
     if normalize_qk:
-        q, k = _unit_norm(q), _unit_norm(k)
-    v = torch.randn(B, T, H, Dv, generator=g)
-    beta = torch.sigmoid(torch.randn(B, T, H, generator=g))
+        q = _unit_norm(q)
+    q = q.to(td).contiguous()
+    k = randn(B, T, H, Dk)
+    if normalize_qk:
+        k = _unit_norm(k)
+    k = k.to(td).contiguous()
+    v = randn(B, T, H, Dv).to(td).contiguous()
+    beta = torch.sigmoid(randn(B, T, H))
     if beta_fill is not None:
         beta = torch.full_like(beta, beta_fill)
     log_alpha = None
     if gated:
-        log_alpha = -torch.nn.functional.softplus(torch.randn(B, T, H, generator=g) - 3.0)
-    S0 = torch.randn(N, H, Dv, Dk, generator=g) * 0.1 if s0 else None
-    return GdnInputs(q.to(td).contiguous(), k.to(td).contiguous(), v.to(td).contiguous(),
-                     beta.contiguous(), None if log_alpha is None else log_alpha.contiguous(),
+        log_alpha = -torch.nn.functional.softplus(randn(B, T, H) - 3.0)
+    S0 = randn(N, H, Dv, Dk) * 0.1 if s0 else None
+    return GdnInputs(q, k, v, beta.contiguous(), None if log_alpha is None else log_alpha.contiguous(),
                      S0, cu, C, {"dtype": dtype, "seed": seed})
 
 

@@ -104,6 +104,12 @@ def test_chunk_fwd_argument_errors(lib):
     assert _fwd(lib, S_T=ctypes.c_void_p((1 << 20) + 8)) == GDN_ERR_SHAPE
     need = lib.gdn_chunk_fwd_workspace_bytes(1, 128, 1, 16, 16, 16, 0, F32)
     assert _fwd(lib, wsb=need - 1) == GDN_ERR_WORKSPACE
+    # one past the size limits: a token tensor of 2^31 elements; a chunk of one
+    # tensor (C * H * Dv * element size) past 2^31 - 1 bytes
+    big = dict(B=1, T=1024, H=16384, Dk=128, Dv=128, C=64, dt=BF16)
+    assert _fwd(lib, **big) == GDN_ERR_SHAPE
+    assert lib.gdn_chunk_fwd_workspace_bytes(1, 1024, 16384, 128, 128, 64, 0, BF16) == 0
+    assert _fwd(lib, B=1, T=1, H=65535, Dk=128, Dv=256, C=64, dt=F32) == GDN_ERR_SHAPE
 
 
 def test_recurrent_step_argument_errors(lib):

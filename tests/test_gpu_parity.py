@@ -116,6 +116,30 @@ def test_ragged(dtype, Dk, Dv, C, T):
     check(inp, dtype, C=C, tag="ragged")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_largest_accepted_sizes(dtype):
+    # the largest token tensors gdn_chunk_fwd accepts (one token more passes
+    # 2^31 - 1 elements): byte offsets past 2^31 (bf16) and past 2^32 (fp32).
+    # Drawn on the device, checked by the oracle on the first, a middle and the
+    # last head
+    B, T, H, D = 1, 1023, 16384, 128
+    assert B * T * H * D <= 2**31 - 1 < B * (T + 1) * H * D
+    say(f"[gpu] largest sizes B={B} T={T} H={H} D={D} {dtype} C=64 seed=91")
+    d = make_inputs(B, T, H, D, D, dtype=dtype, seed=91, device=DEV)
+    O, S = gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, None, chunk_size=64)
+    torch.cuda.synchronize()
+    heads = [0, H // 2 - 1, H - 1]
+    sub = lambda t: t[:, :, heads].cpu()
+    Or, Sr = oracle.forward(sub(d.q), sub(d.k), sub(d.v), sub(d.log_alpha), sub(d.beta),
+                            d.S0[:, heads].cpu(), None)
+    eo = rel(O[:, :, heads].double().cpu().numpy(), Or)
+    es = rel(S[:, heads].double().cpu().numpy(), Sr)
+    say(f"      max rel err O {eo:.3e}  S_T {es:.3e}  (tol {TOL[dtype]:.0e})")
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+    del d, O, S
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
 def test_deltanet_alpha_one_with_state(dtype, D):
     inp = make_inputs(B=1, T=257, H=2, Dk=D, Dv=D, dtype=dtype, gated=False, s0=True, seed=5)
