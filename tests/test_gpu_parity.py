@@ -293,6 +293,31 @@ def test_recurrent_step(dtype, Dk, Dv, gated):
     assert rel(S.double().cpu().numpy(), Sr) <= 1e-5
 
 
+def test_recurrent_step_largest_state():
+    # the largest state gdn_recurrent_step accepts: N = 65535 sequences (the
+    # grid limit), H = 2, Dk = Dv = 128, just under 2^31 fp32 elements (byte
+    # offsets past 2^32). Drawn on the device, checked by the oracle on the
+    # first, a middle and the last sequence
+    N, H, D = 65535, 2, 128
+    assert N * H * D * D <= 2**31 - 1 < N * (H + 1) * D * D
+    say(f"[gpu] largest step state N={N} H={H} D={D} bf16 seed=93")
+    d = make_inputs(B=N, T=1, H=H, Dk=D, Dv=D, dtype="bf16", seed=93, device=DEV)
+    seqs = [0, N // 2, N - 1]
+    sub = lambda t: t[seqs].cpu()
+    Or, Sr = oracle.forward(sub(d.q), sub(d.k), sub(d.v), sub(d.log_alpha), sub(d.beta),
+                            d.S0[seqs].cpu(), None)
+    o = gdn.gdn_recurrent_step(d.q[:, 0].contiguous(), d.k[:, 0].contiguous(),
+                               d.v[:, 0].contiguous(), d.log_alpha[:, 0].contiguous(),
+                               d.beta[:, 0].contiguous(), d.S0)
+    torch.cuda.synchronize()
+    eo = rel(o[seqs].double().cpu().numpy(), Or[:, 0])
+    es = rel(d.S0[seqs].double().cpu().numpy(), Sr)
+    say(f"      max rel err o {eo:.3e}  S {es:.3e}")
+    assert eo <= TOL["bf16"] and es <= 1e-5, (eo, es)
+    del d, o
+    torch.cuda.empty_cache()
+
+
 def test_recurrent_step_decode_batch():
     """The decode batch that bench.py --recurrent 64 times: N = 64 sequences, H = 16,
     Dk = Dv = 128, bf16, every workgroup of the launch."""
