@@ -140,6 +140,24 @@ def test_largest_accepted_sizes(dtype):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("case", ["beta0", "beta1", "decay30", "resets"])
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_degenerate_gates(case, dtype, D):
+    # beta = 0: nothing is written, the state only decays; beta = 1: each
+    # write replaces the state's value along k; log alpha = -30 on every token:
+    # the state is forgotten from one token to the next and the in-chunk
+    # decays underflow; log alpha alternating 0 and -80: resets inside chunks,
+    # so that exp(g) underflows to zero part-way through a chunk
+    inp = make_inputs(B=2, T=200, H=2, Dk=D, Dv=D, dtype=dtype, gated=True, s0=True,
+                      seed=300 + D, beta_fill={"beta0": 0.0, "beta1": 1.0}.get(case))
+    if case == "decay30":
+        inp.log_alpha = torch.full_like(inp.log_alpha, -30.0)
+    elif case == "resets":
+        inp.log_alpha = torch.zeros_like(inp.log_alpha)
+        inp.log_alpha[:, 5::37] = -80.0
+    check(inp, dtype, C=64, tag=f"gates {case}")   # a NaN or inf anywhere fails the bound
+
+
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
 def test_deltanet_alpha_one_with_state(dtype, D):
     inp = make_inputs(B=1, T=257, H=2, Dk=D, Dv=D, dtype=dtype, gated=False, s0=True, seed=5)
