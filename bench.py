@@ -32,6 +32,8 @@ if ROOT not in sys.path:
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}   # dense flop/s
 METRIC = "tokens/sec gated-DeltaNet chunk fwd (H=16,T=4096,D=128,bf16); % roofline"
+BASELINE_NOTE = ("the pages that define the method quote no throughput and no hardware, "
+                 "so there is no published figure to compare with (vs_baseline null)")
 
 
 def per_kernel_work(B, T, H, Dk, Dv, C, s_in, n_seqs, has_s0, gated):
@@ -176,6 +178,7 @@ def bench_recurrent(args, w):
         "step_ms": {"median": round(statistics.median(step_ms), 5), "min": round(min(step_ms), 5),
                     "max": round(max(step_ms), 5)},
         "cpu_baseline": None,
+        "baseline_note": BASELINE_NOTE,
     }
     print(json.dumps(out), flush=True)
 
@@ -314,6 +317,7 @@ def main():
                     "max": round(max(step_ms), 4)},
         "wall_s_timed_loop": round(wall, 4),
         "cpu_baseline": cpu,
+        "baseline_note": BASELINE_NOTE,
     }
     print(json.dumps(out), flush=True)
 
