@@ -122,8 +122,9 @@ struct ColCfg {
         return 0;
     }
     static constexpr int NQB = (NW + 1) / 2;               // query blocks per helper, at most
-    // Q register sets without QLDS: three where a set takes at most 32 registers
-    static constexpr int NQS = NQB * NKK * 16 <= 128 ? 3 : 2;
+    // Q register sets without QLDS: three where a set takes at most 32 registers,
+    // two below 64, else one (fp32 with Dk = 128: two sets would spill)
+    static constexpr int NQS = NQB * NKK * 16 <= 128 ? 3 : NQB * NKK * 16 < 256 ? 2 : 1;
     static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && NVW <= 2, "tile counts");
     static_assert(DV % DVT == 0 && DVT % 16 == 0 && DK % KS == 0 && DK % 16 == 0, "tile shapes");
     static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && (VB % 4 == 0 || VB == 2) && DK % 32 == 0),
