@@ -6,10 +6,15 @@ bf16 q/k/v/O, fp32 gates and state, S0 = 0, seeded synthetic inputs already
 resident in HBM.  Prints ONE JSON line.
 
   value         tokens/s = B*T / (mean device time of one step)
-  roofline      dominant kernel: its algorithmic bytes (or flops) per launch over
-                its mean HIP-event duration, against MI355X's published peak
-  roofline_path the same for the whole call (all kernels)
-  cpu_baseline  the fp64 oracle on the host cores over the same inputs
+  roofline      the whole call (every kernel of one gdn_chunk_fwd): the method's
+                algorithmic bytes (or flops) per call over the mean HIP-event
+                duration of a call, against MI355X's published peak; traffic is
+                the sum of the call's kernels' measured HBM bytes
+  roofline_dominant  the same for the longest kernel alone (its own algorithmic
+                bytes over its mean duration, timed inside the library)
+  kernels       per-kernel mean duration and roofline fraction
+  cpu_baseline  the fp64 oracle on the host cores over a bounded sample of the
+                same inputs, threaded and single-threaded
 
 Options: --gpus (only 1), --steps, --warmup, --workload, --no-flush,
 --profile-steps, --cpu-sample (heads per batch row the oracle runs on, 0 = skip),
@@ -105,29 +110,50 @@ def roofline(name, bytes_, flops, seconds, dtype):
             "alg_bytes": int(bytes_), "alg_flops": int(flops), "ms": round(seconds * 1e3, 4)}
 
 
-def cpu_baseline(inp, heads_per_row: int):
+def usable_cores() -> int:
+    """Host cores this process may run on (its CPU affinity set)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, heads_per_row: int, single_heads: int = 2):
     """The fp64 oracle timed on the host cores over a bounded sample: every
-    batch row, the first ``heads_per_row`` heads, all tokens."""
-    import oracle
-    hs = list(range(min(heads_per_row, inp.q.shape[2])))
-    sl = lambda t: None if t is None else t[:, :, hs].contiguous()
-    q, k, v, la, be = (sl(t) for t in (inp.q, inp.k, inp.v, inp.log_alpha, inp.beta))
-    s0 = None if inp.S0 is None else inp.S0[:, hs].contiguous()
+    batch row, the first ``heads_per_row`` heads, all tokens (threaded over
+    (sequence, head) units), and again on one thread over the first
+    ``single_heads`` of those heads."""
     import numpy as np
-    q, k, v = (np.ascontiguousarray(t.double().numpy()) for t in (q, k, v))
-    la = None if la is None else np.ascontiguousarray(la.double().numpy())
-    be = np.ascontiguousarray(be.double().numpy())
-    t0 = time.perf_counter()
-    _, _, nt = oracle.forward(q, k, v, la, be, s0, inp.cu_seqlens, return_threads=True)
-    dt = time.perf_counter() - t0
-    tokens = inp.q.shape[0] * inp.q.shape[1]
-    # scale to the full workload's tokens/s: the sample holds len(hs) of H heads
+    import oracle
     H = inp.q.shape[2]
-    return {"value": round(tokens * len(hs) / H / dt, 1), "unit": "tokens/s", "cores": nt,
+    tokens = inp.q.shape[0] * inp.q.shape[1]
+
+    def run(nh, n_threads):
+        hs = list(range(min(nh, H)))
+        sl = lambda t: None if t is None else t[:, :, hs].contiguous()
+        q, k, v, la, be = (sl(t) for t in (inp.q, inp.k, inp.v, inp.log_alpha, inp.beta))
+        s0 = None if inp.S0 is None else inp.S0[:, hs].contiguous()
+        q, k, v = (np.ascontiguousarray(t.double().numpy()) for t in (q, k, v))
+        la = None if la is None else np.ascontiguousarray(la.double().numpy())
+        be = np.ascontiguousarray(be.double().numpy())
+        t0 = time.perf_counter()
+        _, _, nt = oracle.forward(q, k, v, la, be, s0, inp.cu_seqlens, n_threads=n_threads,
+                                  return_threads=True)
+        return len(hs), nt, time.perf_counter() - t0
+
+    nh, nt, dt = run(heads_per_row, 0)
+    nh1, _, dt1 = run(single_heads, 1)
+    # scale to the full workload's tokens/s: a sample of nh heads of H
+    return {"value": round(tokens * nh / H / dt, 1), "unit": "tokens/s", "cores": nt,
             "kind": "oracle",
             "sample": f"fp64 token recurrence over all {inp.q.shape[0]}x{inp.q.shape[1]} tokens "
-                      f"of heads 0..{len(hs) - 1} of {H} ({tokens * len(hs)} token-heads, "
-                      f"{dt:.2f} s wall on {nt} threads); tokens/s scaled by {len(hs)}/{H}"}
+                      f"of heads 0..{nh - 1} of {H} ({tokens * nh} token-heads, "
+                      f"{dt:.2f} s wall on {nt} threads); tokens/s scaled by {nh}/{H}",
+            "host_cores": usable_cores(),
+            "single_thread": {"value": round(tokens * nh1 / H / dt1, 1), "unit": "tokens/s",
+                              "seconds": round(dt1, 3),
+                              "sample": f"heads 0..{nh1 - 1} of {H}, all tokens, one thread; "
+                                        f"tokens/s scaled by {nh1}/{H}"}}
 
 
 def bench_recurrent(args, w):
@@ -280,9 +306,13 @@ def main():
     work = per_kernel_work(B, T, H, w.Dk, w.Dv, w.C, s_in, N, inp.S0 is not None,
                            inp.log_alpha is not None)
     dom = max(("prep", "scan"), key=lambda k_: kmean[k_])
-    rl = roofline(dom, *work[dom], kmean[dom] / 1e3, w.dtype)
-    rl["traffic"] = measured_traffic(args.workload, dom)
-    rl_path = roofline("path", *work["path"], ms / 1e3, w.dtype)
+    rl_dom = roofline(dom, *work[dom], kmean[dom] / 1e3, w.dtype)
+    rl_dom["traffic"] = measured_traffic(args.workload, dom)
+    # the metric is the call's % roofline: the whole call is the headline
+    rl = roofline("call (" + " + ".join(k_ for k_ in kms if kmean[k_] > 0) + ")", *work["path"],
+                  ms / 1e3, w.dtype)
+    parts = [measured_traffic(args.workload, k_) for k_ in kms if kmean[k_] > 0]
+    rl["traffic"] = None if any(p is None for p in parts) else sum(parts)
     kernels = {k_: {"ms": round(kmean[k_], 4),
                     **({"frac": roofline(k_, *work[k_], kmean[k_] / 1e3, w.dtype)["frac"]}
                        if k_ in work and kmean[k_] > 0 else {})}
@@ -312,7 +342,7 @@ def main():
         "config": {"workload": args.workload, "B": B, "T": T, "H": H, "Dk": w.Dk, "Dv": w.Dv,
                    "chunk": w.C, "state": "fp32", "S0": inp.S0 is not None,
                    "flush_l2_mall": flush is not None},
-        "roofline": rl, "roofline_path": rl_path, "kernels": kernels,
+        "roofline": rl, "roofline_dominant": rl_dom, "kernels": kernels,
         "step_ms": {"median": round(statistics.median(step_ms), 4), "min": round(min(step_ms), 4),
                     "max": round(max(step_ms), 4)},
         "wall_s_timed_loop": round(wall, 4),
