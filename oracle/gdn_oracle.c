@@ -7,24 +7,25 @@
  * never calls it.
  *
  * What it computes, for every independent unit u = (sequence, head), in IEEE
- * double precision and strictly token by token (no chunking, no blocking):
+ * double precision and strictly token by token (no chunking, no blocking).
+ * The definition is the per-token update of the Qiita article by Nyysyyan on
+ * the Linear Attention lineage, section "Gated-DeltaNet":
  *
- *     a_t   = exp(log_alpha_t)            (a_t = 1 when log_alpha is NULL: DeltaNet)
- *     S~    = a_t * S                      gate the old memory
- *     p_t   = S~ k_t                       what the gated memory predicts for key k_t
- *     S     = S~ + beta_t (v_t - p_t) k_t^T    delta-rule write of the prediction error
- *     o_t   = S q_t                        read the UPDATED memory with the query
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,    o_t = S_t q_t
  *
- * Sources:
- *  - Qiita article by Nyysyyan on the Linear Attention lineage, section
- *    "Gated-DeltaNet": S_i = alpha_i S_{i-1}(I - beta_i k_i k_i^T) + beta_i v_i k_i^T,
- *    h_i = S_i q_i.  Expanding alpha S (I - beta k k^T) = S~ - beta (S~ k) k^T gives
- *    exactly the gate / predict / delta / write order above.
- *  - kkkzoz blog post "linear-attention", sections "Gated DeltaNet" and
- *    "Workflow": the same four steps (gate_memory, batch_matvec, delta,
- *    batch_outer) followed by o_t = S_new q_t.
- *  - LinearAttention系列解读(六)：DeltaNet的Chunkwise Form推导, section 3
- *    (recursive form): DeltaNet is the alpha = 1 case.
+ * Multiplying out the first term, alpha S (I - beta k k^T) = S~ - beta (S~ k) k^T
+ * with S~ = alpha S, so one token is evaluated as
+ *
+ *     S~    = alpha_t S                         (alpha_t = exp(log_alpha_t); 1 when NULL)
+ *     e     = beta_t (v_t - S~ k_t)             one value per row of S
+ *     S     = S~ + e k_t^T
+ *     o_t   = S q_t                             the state AFTER token t's write
+ *
+ * which is the same expression with its products grouped per row; no term is
+ * dropped or reordered beyond that.  The post "linear-attention" on kkkzoz.top
+ * (section "Gated DeltaNet") states the same update, and
+ * LinearAttention系列解读(六)：DeltaNet的Chunkwise Form推导, section 3 (recursive
+ * form), is its alpha = 1 case (DeltaNet).
  *
  * State orientation: S is [Dv][Dk] row-major, o = S q (both pages read the
  * state as S q with S of shape [Dv, Dk]).
