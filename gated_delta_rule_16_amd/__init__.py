@@ -6,10 +6,11 @@ and supplies seeded synthetic inputs (``inputs``).  Importing the package does
 not load the library; the first call does, and fails loudly if it is missing.
 """
 from .binding import (GDN_BF16, GDN_F32, GdnError, LIB_PATH, gdn_chunk_fwd,
-                      gdn_chunk_fwd_profiled, gdn_chunk_fwd_supported,
+                      gdn_chunk_fwd_noalloc, gdn_chunk_fwd_profiled, gdn_chunk_fwd_supported,
                       gdn_chunk_fwd_workspace_bytes, gdn_recurrent_step, gdn_status_string,
                       load_library)
 
 __all__ = ["GDN_BF16", "GDN_F32", "GdnError", "LIB_PATH", "gdn_chunk_fwd",
-           "gdn_chunk_fwd_profiled", "gdn_chunk_fwd_supported", "gdn_chunk_fwd_workspace_bytes",
-           "gdn_recurrent_step", "gdn_status_string", "load_library"]
+           "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_profiled", "gdn_chunk_fwd_supported",
+           "gdn_chunk_fwd_workspace_bytes", "gdn_recurrent_step", "gdn_status_string",
+           "load_library"]

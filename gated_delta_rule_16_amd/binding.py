@@ -6,7 +6,7 @@ workspace) and the stream.  There is no fallback: if the library is not built,
 or a tensor is not on a ROCm device, the call raises.
 
 The Python functions carry the C names:
-  gdn_chunk_fwd, gdn_chunk_fwd_profiled, gdn_recurrent_step,
+  gdn_chunk_fwd, gdn_chunk_fwd_profiled, gdn_chunk_fwd_noalloc, gdn_recurrent_step,
   gdn_chunk_fwd_workspace_bytes, gdn_chunk_fwd_supported, gdn_status_string.
 """
 from __future__ import annotations
@@ -53,6 +53,8 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_chunk_fwd.restype = I
     lib.gdn_chunk_fwd_profiled.argtypes = lib.gdn_chunk_fwd.argtypes + [P]
     lib.gdn_chunk_fwd_profiled.restype = I
+    lib.gdn_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P]
+    lib.gdn_chunk_fwd_noalloc.restype = I
     lib.gdn_recurrent_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.gdn_recurrent_step.restype = I
     lib.gdn_status_string.argtypes = [I]
@@ -164,6 +166,41 @@ def gdn_chunk_fwd_profiled(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *
     kernel [table, prep, scan, output]; blocks until the call has finished."""
     return _chunk_fwd(True, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
                       output_final_state, workspace, stream)
+
+
+def gdn_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          log_alpha: Optional[torch.Tensor], beta: torch.Tensor,
+                          S0: Optional[torch.Tensor], cu_seqlens: Optional[torch.Tensor],
+                          O: torch.Tensor, S_T: Optional[torch.Tensor], *, chunk_size: int = 64,
+                          stream: Optional[torch.cuda.Stream] = None) -> None:
+    """gdn_chunk_fwd on the library's static scratch buffer (include/gdn.h,
+    gdn_chunk_fwd_noalloc): no workspace, and the caller passes the outputs
+    O [B,T,H,Dv] and S_T [N,H,Dv,Dk] (or None), so that nothing is allocated."""
+    lib = load_library()
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,T,H,Dk] and v [B,T,H,Dv]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    N = B if cu_seqlens is None else n_seqs
+    for name, t in (("beta", beta), ("log_alpha", log_alpha)):
+        if t is not None and t.shape != (B, T, H):
+            raise ValueError(f"{name} must be [B,T,H]")
+    if S0 is not None and S0.shape != (N, H, Dv, Dk):
+        raise ValueError("S0 must be [N,H,Dv,Dk]")
+    if O.shape != (B, T, H, Dv) or (S_T is not None and S_T.shape != (N, H, Dv, Dk)):
+        raise ValueError("O must be [B,T,H,Dv] and S_T [N,H,Dv,Dk]")
+    rc = lib.gdn_chunk_fwd_noalloc(
+        _ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt),
+        _ptr(log_alpha, "log_alpha", dev, torch.float32), _ptr(beta, "beta", dev, torch.float32),
+        _ptr(S0, "S0", dev, torch.float32), _ptr(cu_seqlens, "cu_seqlens", dev, torch.int32),
+        n_seqs, _ptr(O, "O", dev, dt), _ptr(S_T, "S_T", dev, torch.float32),
+        B, T, H, Dk, Dv, chunk_size, _DT[dt], _stream(dev, stream))
+    if rc != 0:
+        raise GdnError(rc, "gdn_chunk_fwd_noalloc")
 
 
 def gdn_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -280,21 +280,60 @@ extern "C" size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int
     return make_layout(B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt)).total;
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch buffer of gdn_chunk_fwd_noalloc: the per-chunk intermediates
+// of one call, in device memory the library owns (one copy per GPU, from the
+// library's load until the process ends), for callers that cannot allocate.
+// In host code `scratch` names a host-side stand-in, not a device address: its
+// device address is looked up once per device with hipGetSymbolAddress and
+// only that pointer is ever handed to a kernel.
+// ---------------------------------------------------------------------------
 namespace {
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static_assert(kScratchBytes == (size_t)GDN_NOALLOC_SCRATCH_BYTES, "header and library disagree");
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+// Device address of `scratch` on the current device (looked up on the first
+// call with that device current, then cached); NULL if the lookup fails.
+void* scratch_device_ptr() {
+    static std::atomic<void*> cached[kMaxCachedDevices] = {};
+    const int dev = current_device();
+    void* p = dev < kMaxCachedDevices ? cached[dev].load(std::memory_order_acquire) : nullptr;
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        if (dev < kMaxCachedDevices) cached[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+// use_scratch: run on the static scratch buffer instead of `workspace`
 gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* log_alpha,
                           const float* beta, const float* S0, const int32_t* cu_seqlens,
                           int n_seqs, void* O, float* S_T, int B, int T, int H, int Dk, int Dv,
                           int C, gdn_dtype dt, void* workspace, size_t workspace_bytes,
-                          void* stream, KernelTimer* tm) {
+                          bool use_scratch, void* stream, KernelTimer* tm) {
     const bool varlen = cu_seqlens != nullptr;
     // with no tokens the token tensors are never read (empty tensors may be NULL)
     const bool has_tokens = T > 0;
     if (has_tokens && (!q || !k || !v || !beta || !O)) return GDN_ERR_NULL;
     if (gdn_status s = check_sizes(B, T, H, Dk, Dv, C, varlen, n_seqs, dt)) return s;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(workspace) ||
-        !aligned16(S0) || !aligned16(S_T))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(S0) ||
+        !aligned16(S_T))
         return GDN_ERR_SHAPE;
     const Layout L = make_layout(B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt));
+    if (use_scratch) {
+        if (L.total > kScratchBytes) return GDN_ERR_SCRATCH_LIMIT;
+        workspace = scratch_device_ptr();
+        if (!workspace) return GDN_ERR_HIP;
+        workspace_bytes = kScratchBytes;
+    }
+    if (!aligned16(workspace)) return GDN_ERR_SHAPE;
     if (L.total > 0 && !workspace) return GDN_ERR_NULL;
     if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
     FwdArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, varlen ? n_seqs : B, O, S_T,
@@ -313,7 +352,21 @@ extern "C" gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
     try {
         KernelTimer off;
         return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O, S_T, B, T, H,
-                              Dk, Dv, C, dt, workspace, workspace_bytes, stream, &off);
+                              Dk, Dv, C, dt, workspace, workspace_bytes, false, stream, &off);
+    } catch (...) {
+        return GDN_ERR_INTERNAL;
+    }
+}
+
+extern "C" gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                            const float* log_alpha, const float* beta,
+                                            const float* S0, const int32_t* cu_seqlens,
+                                            int n_seqs, void* O, float* S_T, int B, int T, int H,
+                                            int Dk, int Dv, int C, gdn_dtype dt, void* stream) {
+    try {
+        KernelTimer off;
+        return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O, S_T, B, T, H,
+                              Dk, Dv, C, dt, nullptr, 0, true, stream, &off);
     } catch (...) {
         return GDN_ERR_INTERNAL;
     }
@@ -338,8 +391,8 @@ extern "C" gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const
             }
         }
         gdn_status s = chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O, S_T,
-                                      B, T, H, Dk, Dv, C, dt, workspace, workspace_bytes, stream,
-                                      &tm);
+                                      B, T, H, Dk, Dv, C, dt, workspace, workspace_bytes, false,
+                                      stream, &tm);
         if (s == GDN_OK && hipEventSynchronize(tm.ev[tm.n - 1]) != hipSuccess) s = GDN_ERR_HIP;
         if (s == GDN_OK) {
             // pairs of marks: [table], [prep], scan (prep absent when there are no chunks)
@@ -430,6 +483,8 @@ extern "C" const char* gdn_status_string(gdn_status s) {
         case GDN_ERR_WORKSPACE: return "workspace is smaller than required";
         case GDN_ERR_HIP: return "a HIP launch or runtime call failed";
         case GDN_ERR_INTERNAL: return "internal error";
+        case GDN_ERR_SCRATCH_LIMIT:
+            return "these sizes need more than the library's static scratch buffer holds";
     }
     return "unknown status";
 }

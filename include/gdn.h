@@ -48,7 +48,8 @@ typedef enum {
     GDN_ERR_UNSUPPORTED = 3,   /* (Dk, Dv, C, dtype) has no compiled kernel */
     GDN_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than required */
     GDN_ERR_HIP = 5,           /* a HIP launch or runtime call failed */
-    GDN_ERR_INTERNAL = 6
+    GDN_ERR_INTERNAL = 6,
+    GDN_ERR_SCRATCH_LIMIT = 7  /* gdn_chunk_fwd_noalloc: the sizes need more than its static buffer */
 } gdn_status;
 
 typedef enum {
@@ -110,6 +111,34 @@ gdn_status gdn_chunk_fwd(const void *q, const void *k, const void *v,
                          void *O, float *S_T,
                          int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Allocation-free variant of gdn_chunk_fwd, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments (minus the
+ * workspace), same kernels and bitwise the same results as gdn_chunk_fwd; the
+ * per-chunk intermediates go to a buffer of GDN_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that the library holds in device memory, one copy per GPU, from its load
+ * until the process ends.  The call itself allocates and frees nothing.
+ *  - Limit: the call is refused with GDN_ERR_SCRATCH_LIMIT, before anything is
+ *    enqueued, when gdn_chunk_fwd_workspace_bytes(...) for the same sizes
+ *    exceeds GDN_NOALLOC_SCRATCH_BYTES (e.g. bf16, Dk = Dv = 128, C = 64 needs
+ *    6912 bytes per chunk of 64 tokens and head: about 9700 chunk-heads).
+ *  - Sharing: every call on one GPU uses that GPU's one buffer, which keeps the
+ *    last call's contents; nothing in it needs to start at any value.  Calls
+ *    ordered on one stream are safe; calls that overlap in time on one GPU (two
+ *    streams, two host threads without ordering) race on the buffer and give
+ *    undefined results.
+ *  - The first call on each device looks up the buffer's device address
+ *    (GDN_ERR_HIP if that fails).
+ * Errors: as gdn_chunk_fwd (without GDN_ERR_WORKSPACE), plus
+ * GDN_ERR_SCRATCH_LIMIT. */
+#define GDN_NOALLOC_SCRATCH_BYTES (64ull << 20)
+gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                 const float *log_alpha, const float *beta, const float *S0,
+                                 const int32_t *cu_seqlens, int n_seqs,
+                                 void *O, float *S_T,
+                                 int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
+                                 void *stream);
 
 /* Measurement variant of gdn_chunk_fwd: same arguments and result, plus
  * kernel_ms, a HOST array of 4 floats that receives the device time in

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         s = lib.gdn_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.gdn_status_string(99).decode() == "unknown status"
@@ -110,6 +110,30 @@ def test_chunk_fwd_argument_errors(lib):
     assert _fwd(lib, **big) == GDN_ERR_SHAPE
     assert lib.gdn_chunk_fwd_workspace_bytes(1, 1024, 16384, 128, 128, 64, 0, BF16) == 0
     assert _fwd(lib, B=1, T=1, H=65535, Dk=128, Dv=256, C=64, dt=F32) == GDN_ERR_SHAPE
+
+
+def test_noalloc_argument_errors(lib):
+    """gdn_chunk_fwd_noalloc checks its arguments, and its scratch limit, on the
+    host before any HIP call (fake, never dereferenced pointers)."""
+    GDN_ERR_SCRATCH_LIMIT = 7
+    p = ctypes.c_void_p(1 << 20)
+
+    def call(**kw):
+        a = dict(q=p, k=p, v=p, la=None, beta=p, S0=None, cu=None, n=0, O=p, S_T=None,
+                 B=1, T=128, H=1, Dk=16, Dv=16, C=16, dt=F32, st=None)
+        a.update(kw)
+        return lib.gdn_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["la"], a["beta"], a["S0"],
+                                         a["cu"], a["n"], a["O"], a["S_T"], a["B"], a["T"],
+                                         a["H"], a["Dk"], a["Dv"], a["C"], a["dt"], a["st"])
+    assert call(q=None) == GDN_ERR_NULL
+    assert call(B=0) == GDN_ERR_SHAPE
+    assert call(Dk=32, Dv=32) == GDN_ERR_UNSUPPORTED
+    assert call(O=ctypes.c_void_p((1 << 20) + 4)) == GDN_ERR_SHAPE
+    # the long-context shape needs about 113 MB of intermediates: above the 64 MiB buffer
+    long = dict(B=1, T=32768, H=32, Dk=128, Dv=128, C=64, dt=BF16)
+    assert lib.gdn_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 0, BF16) > 64 << 20
+    assert call(**long) == GDN_ERR_SCRATCH_LIMIT
+    assert "scratch" in lib.gdn_status_string(GDN_ERR_SCRATCH_LIMIT).decode()
 
 
 def test_recurrent_step_argument_errors(lib):
