@@ -18,6 +18,8 @@ resident in HBM.  Prints ONE JSON line.
 
 Options: --gpus (only 1), --steps, --warmup, --workload, --no-flush,
 --profile-steps, --cpu-sample (heads per batch row the oracle runs on, 0 = skip),
+--rule (delta: gdn_chunk_fwd, the default; mamba2: gdn_mamba2_chunk_fwd, the
+scalar-gated rule without the erase term, on the same workload),
 --recurrent N (instead: the single-token step, gdn_recurrent_step, over a decode
 batch of N sequences with the workload's H, Dk, Dv and dtype; its own JSON line).
 """
@@ -41,7 +43,7 @@ BASELINE_NOTE = ("the pages that define the method quote no throughput and no ha
                  "so there is no published figure to compare with (vs_baseline null)")
 
 
-def per_kernel_work(B, T, H, Dk, Dv, C, s_in, n_seqs, has_s0, gated):
+def per_kernel_work(B, T, H, Dk, Dv, C, s_in, n_seqs, has_s0, gated, rule="delta"):
     """Algorithmic bytes and flops of each kernel and of the whole call.
 
     Bytes count only the operation's own inputs and outputs that a kernel
@@ -49,7 +51,11 @@ def per_kernel_work(B, T, H, Dk, Dv, C, s_in, n_seqs, has_s0, gated):
     T diag(beta), written by prep and read by scan) are implementation traffic
     and are not counted.  Flops count dense 16x16 tiles of every product.
     The path's flops are the method's count per token-head,
-    6 Dk Dv + 2C (3 Dk + 2 Dv) + C^2 / 3 (K K^T, W, Q K^T; U, P V'; inverse)."""
+    6 Dk Dv + 2C (3 Dk + 2 Dv) + C^2 / 3 (K K^T, W, Q K^T; U, P V'; inverse).
+    The no-erase rule (mamba2) has no prediction and no inverse: its path is
+    4 Dk Dv + 2C (Dk + Dv) per token-head (Q S^T, the state update, Q K^T, P V),
+    and its per-chunk kernel ("prep" here: the gates kernel) reads only the
+    gates."""
     th = B * T * H                      # token-heads
     gate_b = 4 + (4 if gated else 0)    # beta (+ log alpha), fp32
     state_b = n_seqs * H * Dv * Dk * 4 * (2 if has_s0 else 1)
@@ -59,6 +65,10 @@ def per_kernel_work(B, T, H, Dk, Dv, C, s_in, n_seqs, has_s0, gated):
     prep_f = th * (2 * C * Dk + C * C / 3)
     scan_f = th * (6 * Dk * Dv + 2 * C * (Dk + 2 * Dv))
     path_f = th * (6 * Dk * Dv + 2 * C * (3 * Dk + 2 * Dv) + C * C / 3)
+    if rule == "mamba2":
+        prep_b, prep_f = th * gate_b, th * 8
+        scan_f = th * (4 * Dk * Dv + 2 * C * (Dk + Dv))
+        path_f = scan_f + prep_f
     return {"prep": (prep_b, prep_f), "scan": (scan_b, scan_f), "path": (path_b, path_f)}
 
 
@@ -118,7 +128,7 @@ def usable_cores() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline(inp, heads_per_row: int, single_heads: int = 2):
+def cpu_baseline(inp, heads_per_row: int, single_heads: int = 2, no_erase: bool = False):
     """The fp64 oracle timed on the host cores over a bounded sample: every
     batch row, the first ``heads_per_row`` heads, all tokens (threaded over
     (sequence, head) units), and again on one thread over the first
@@ -138,7 +148,7 @@ def cpu_baseline(inp, heads_per_row: int, single_heads: int = 2):
         be = np.ascontiguousarray(be.double().numpy())
         t0 = time.perf_counter()
         _, _, nt = oracle.forward(q, k, v, la, be, s0, inp.cu_seqlens, n_threads=n_threads,
-                                  return_threads=True)
+                                  return_threads=True, no_erase=no_erase)
         return len(hs), nt, time.perf_counter() - t0
 
     nh, nt, dt = run(heads_per_row, 0)
@@ -223,6 +233,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="after timing, copy an MB-megabyte buffer a few times (a plain copy "
                          "kernel of known traffic, the scale for hardware byte counters)")
+    ap.add_argument("--rule", choices=["delta", "mamba2"], default="delta",
+                    help="update rule: delta (gdn_chunk_fwd) or mamba2 (gdn_mamba2_chunk_fwd)")
     ap.add_argument("--recurrent", type=int, default=0, metavar="N",
                     help="time gdn_recurrent_step over N sequences instead (one token each)")
     args = ap.parse_args()
@@ -249,8 +261,10 @@ def main():
     tdt = inp.q.dtype
     O = torch.empty(B, T, H, w.Dv, device=dev, dtype=tdt)
     S_T = torch.empty(N, H, w.Dv, w.Dk, device=dev, dtype=torch.float32)
-    n_ws = gdn.gdn_chunk_fwd_workspace_bytes(B, T, H, w.Dk, w.Dv, w.C,
-                                             0 if inp.cu_seqlens is None else N, tdt)
+    rule = {"delta": gdn.GDN_RULE_DELTA, "mamba2": gdn.GDN_RULE_MAMBA2}[args.rule]
+    fwd = gdn.gdn_chunk_fwd if args.rule == "delta" else gdn.gdn_mamba2_chunk_fwd
+    n_ws = gdn.gdn_rule_workspace_bytes(rule, B, T, H, w.Dk, w.Dv, w.C,
+                                        0 if inp.cu_seqlens is None else N, tdt)
     ws = torch.empty(n_ws, device=dev, dtype=torch.uint8)
     # Cache eviction between steps: one pass reading 512 MB (twice the MALL)
     # leaves L2 and MALL holding clean lines of this buffer, so every step reads
@@ -266,8 +280,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, d.cu_seqlens, chunk_size=w.C,
-                          O=O, S_T=S_T, workspace=ws, stream=stream)
+        fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, d.cu_seqlens, chunk_size=w.C,
+            O=O, S_T=S_T, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         evict()
@@ -294,9 +308,9 @@ def main():
     kms = {"table": [], "prep": [], "scan": [], "unused": []}
     for _ in range(args.profile_steps):
         evict()
-        _, _, t = gdn.gdn_chunk_fwd_profiled(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0,
-                                             d.cu_seqlens, chunk_size=w.C, O=O, S_T=S_T,
-                                             workspace=ws, stream=stream)
+        _, _, t = gdn.gdn_rule_chunk_fwd_profiled(rule, d.q, d.k, d.v, d.log_alpha, d.beta,
+                                                  d.S0, d.cu_seqlens, chunk_size=w.C, O=O,
+                                                  S_T=S_T, workspace=ws, stream=stream)
         for key, x in zip(kms, t):
             kms[key].append(x)
     kms.pop("unused")
@@ -304,14 +318,15 @@ def main():
 
     s_in = 2 if w.dtype == "bf16" else 4
     work = per_kernel_work(B, T, H, w.Dk, w.Dv, w.C, s_in, N, inp.S0 is not None,
-                           inp.log_alpha is not None)
+                           inp.log_alpha is not None, args.rule)
     dom = max(("prep", "scan"), key=lambda k_: kmean[k_])
     rl_dom = roofline(dom, *work[dom], kmean[dom] / 1e3, w.dtype)
-    rl_dom["traffic"] = measured_traffic(args.workload, dom)
+    tkey = args.workload if args.rule == "delta" else f"{args.rule}_{args.workload}"
+    rl_dom["traffic"] = measured_traffic(tkey, dom)
     # the metric is the call's % roofline: the whole call is the headline
     rl = roofline("call (" + " + ".join(k_ for k_ in kms if kmean[k_] > 0) + ")", *work["path"],
                   ms / 1e3, w.dtype)
-    parts = [measured_traffic(args.workload, k_) for k_ in kms if kmean[k_] > 0]
+    parts = [measured_traffic(tkey, k_) for k_ in kms if kmean[k_] > 0]
     rl["traffic"] = None if any(p is None for p in parts) else sum(parts)
     kernels = {k_: {"ms": round(kmean[k_], 4),
                     **({"frac": roofline(k_, *work[k_], kmean[k_] / 1e3, w.dtype)["frac"]}
@@ -330,16 +345,20 @@ def main():
 
     cpu = None
     if args.cpu_sample > 0:
-        cpu = cpu_baseline(inp, args.cpu_sample)
+        cpu = cpu_baseline(inp, args.cpu_sample, no_erase=args.rule == "mamba2")
 
-    headline = args.workload == ap.get_default("workload")
+    headline = args.workload == ap.get_default("workload") and args.rule == "delta"
+    metric = METRIC if headline else f"tokens/sec gated-DeltaNet chunk fwd ({args.workload})"
+    if args.rule == "mamba2":
+        metric = f"tokens/sec Mamba2 (scalar gate, no erase) chunk fwd ({args.workload})"
     out = {
-        "metric": METRIC if headline else f"tokens/sec gated-DeltaNet chunk fwd ({args.workload})",
+        "metric": metric,
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "Dk": w.Dk, "Dv": w.Dv,
+        "config": {"workload": args.workload, "rule": args.rule, "B": B, "T": T, "H": H,
+                   "Dk": w.Dk, "Dv": w.Dv,
                    "chunk": w.C, "state": "fp32", "S0": inp.S0 is not None,
                    "flush_l2_mall": flush is not None},
         "roofline": rl, "roofline_dominant": rl_dom, "kernels": kernels,

@@ -7,7 +7,9 @@ or a tensor is not on a ROCm device, the call raises.
 
 The Python functions carry the C names:
   gdn_chunk_fwd, gdn_chunk_fwd_profiled, gdn_chunk_fwd_noalloc, gdn_recurrent_step,
-  gdn_chunk_fwd_workspace_bytes, gdn_chunk_fwd_supported, gdn_status_string.
+  gdn_chunk_fwd_workspace_bytes, gdn_chunk_fwd_supported, gdn_status_string,
+  gdn_mamba2_chunk_fwd, gdn_rule_chunk_fwd_profiled, gdn_rule_workspace_bytes,
+  gdn_rule_supported.
 """
 from __future__ import annotations
 
@@ -22,6 +24,8 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_RULE_DELTA = 0
+GDN_RULE_MAMBA2 = 1
 _DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
 
 _lib = None
@@ -55,6 +59,14 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_chunk_fwd_profiled.restype = I
     lib.gdn_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, P]
     lib.gdn_chunk_fwd_noalloc.restype = I
+    lib.gdn_mamba2_chunk_fwd.argtypes = lib.gdn_chunk_fwd.argtypes
+    lib.gdn_mamba2_chunk_fwd.restype = I
+    lib.gdn_rule_chunk_fwd_profiled.argtypes = [I] + lib.gdn_chunk_fwd.argtypes + [P]
+    lib.gdn_rule_chunk_fwd_profiled.restype = I
+    lib.gdn_rule_supported.argtypes = [I, I, I, I, I]
+    lib.gdn_rule_supported.restype = I
+    lib.gdn_rule_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I]
+    lib.gdn_rule_workspace_bytes.restype = SZ
     lib.gdn_recurrent_step.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P]
     lib.gdn_recurrent_step.restype = I
     lib.gdn_status_string.argtypes = [I]
@@ -77,6 +89,16 @@ def gdn_chunk_fwd_workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, C: i
                                                             _DT[dtype]))
 
 
+def gdn_rule_supported(rule: int, Dk: int, Dv: int, C: int, dtype: torch.dtype) -> bool:
+    return bool(load_library().gdn_rule_supported(rule, Dk, Dv, C, _DT[dtype]))
+
+
+def gdn_rule_workspace_bytes(rule: int, B: int, T: int, H: int, Dk: int, Dv: int, C: int,
+                             n_seqs: int, dtype: torch.dtype) -> int:
+    return int(load_library().gdn_rule_workspace_bytes(rule, B, T, H, Dk, Dv, C, n_seqs,
+                                                       _DT[dtype]))
+
+
 def _ptr(t: Optional[torch.Tensor], name: str, device=None, dtype=None):
     if t is None:
         return None
@@ -97,7 +119,7 @@ def _stream(device, stream) -> ctypes.c_void_p:
 
 
 def _chunk_fwd(profiled: bool, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
-               output_final_state, workspace, stream):
+               output_final_state, workspace, stream, rule=GDN_RULE_DELTA):
     lib = load_library()
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,T,H,Dk] and v [B,T,H,Dv]")
@@ -117,7 +139,7 @@ def _chunk_fwd(profiled: bool, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_s
         O = torch.empty(B, T, H, Dv, device=dev, dtype=dt)
     if S_T is None and output_final_state:
         S_T = torch.empty(N, H, Dv, Dk, device=dev, dtype=torch.float32)
-    need = lib.gdn_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, chunk_size, n_seqs, _DT[dt])
+    need = lib.gdn_rule_workspace_bytes(rule, B, T, H, Dk, Dv, chunk_size, n_seqs, _DT[dt])
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), device=dev, dtype=torch.uint8)
     args = [
@@ -130,13 +152,15 @@ def _chunk_fwd(profiled: bool, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_s
         _stream(dev, stream)]
     if profiled:
         ms = (ctypes.c_float * 4)()
-        rc = lib.gdn_chunk_fwd_profiled(*args, ms)
+        rc = lib.gdn_rule_chunk_fwd_profiled(rule, *args, ms)
         if rc != 0:
-            raise GdnError(rc, "gdn_chunk_fwd_profiled")
+            raise GdnError(rc, "gdn_rule_chunk_fwd_profiled")
         return O, S_T, [float(x) for x in ms]
-    rc = lib.gdn_chunk_fwd(*args)
+    fn, name = {GDN_RULE_DELTA: (lib.gdn_chunk_fwd, "gdn_chunk_fwd"),
+                GDN_RULE_MAMBA2: (lib.gdn_mamba2_chunk_fwd, "gdn_mamba2_chunk_fwd")}[rule]
+    rc = fn(*args)
     if rc != 0:
-        raise GdnError(rc, "gdn_chunk_fwd")
+        raise GdnError(rc, name)
     return O, S_T
 
 
@@ -166,6 +190,31 @@ def gdn_chunk_fwd_profiled(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *
     kernel [table, prep, scan, output]; blocks until the call has finished."""
     return _chunk_fwd(True, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
                       output_final_state, workspace, stream)
+
+
+def gdn_mamba2_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         log_alpha: Optional[torch.Tensor], beta: Optional[torch.Tensor],
+                         S0: Optional[torch.Tensor] = None,
+                         cu_seqlens: Optional[torch.Tensor] = None, *, chunk_size: int = 64,
+                         O: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+                         output_final_state: bool = True,
+                         workspace: Optional[torch.Tensor] = None,
+                         stream: Optional[torch.cuda.Stream] = None
+                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked forward of S_t = alpha_t S_{t-1} + beta_t v_t k_t^T, o_t = S_t q_t
+    (include/gdn.h, gdn_mamba2_chunk_fwd).  Arguments as gdn_chunk_fwd; beta may
+    be None (beta = 1), and log_alpha None (alpha = 1) gives linear attention."""
+    return _chunk_fwd(False, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
+                      output_final_state, workspace, stream, rule=GDN_RULE_MAMBA2)
+
+
+def gdn_rule_chunk_fwd_profiled(rule: int, q, k, v, log_alpha, beta, S0=None, cu_seqlens=None,
+                                *, chunk_size: int = 64, O=None, S_T=None,
+                                output_final_state=True, workspace=None, stream=None):
+    """The forward of ``rule`` (GDN_RULE_DELTA or GDN_RULE_MAMBA2), also returning
+    each kernel's device milliseconds [table, prep or gates, scan, unused]."""
+    return _chunk_fwd(True, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
+                      output_final_state, workspace, stream, rule=rule)
 
 
 def gdn_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

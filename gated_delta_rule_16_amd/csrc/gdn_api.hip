@@ -5,9 +5,12 @@
 //   [packed batches only] chunk table  <- cu_seqlens
 //   prep  (chunk slot, head)            g, Tb = T diag(beta)   (independent chunks)
 //   scan  (Dv slice, head, sequence)    O, S_T                 (serial over chunks)
+// gdn_mamba2_chunk_fwd (the no-erase rule) replaces prep by the gates kernel
+// (g and beta per chunk) and runs the same scan without the prediction step.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <iterator>
 #include <cstdlib>
 #include <cstring>
 
@@ -59,7 +62,7 @@ struct Layout {
     size_t g, Tb, bounds, seq_slot, table, total;
 };
 
-Layout make_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C,
+Layout make_layout(int rule, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C,
                    bool varlen, int64_t n_seqs, size_t es) {
     Layout L{};
     const int64_t cps = (T + C - 1) / C;
@@ -68,8 +71,10 @@ Layout make_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int6
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
     const size_t u = (size_t)(L.slots * H);
-    L.g = take(u * 3 * C * sizeof(float));   // g, exp(g), exp(g_n - g) per chunk
-    L.Tb = take(u * (size_t)tb_blocks((int)C, es == 2) * 1024);   // Tb blocks per chunk
+    // g, exp(g), exp(g_n - g) (and beta for kNoErase) per chunk
+    L.g = take(u * gate_rows(rule) * C * sizeof(float));
+    // Tb blocks per chunk (delta rule only)
+    L.Tb = take(rule == kDelta ? u * (size_t)tb_blocks((int)C, es == 2) * 1024 : 0);
     if (varlen) {
         L.bounds = take((size_t)(n_seqs + 1) * sizeof(int));
         L.seq_slot = take((size_t)(n_seqs + 1) * sizeof(int));
@@ -142,10 +147,10 @@ struct KernelTimer {
     }
 };
 
-template <typename T, int DK, int DV, int C>
+template <typename T, int DK, int DV, int C, int RULE>
 gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     const bool varlen = a.cu != nullptr;
-    const Layout L = make_layout(a.B, a.T, a.H, DK, DV, C, varlen, a.n_seqs, sizeof(T));
+    const Layout L = make_layout(RULE, a.B, a.T, a.H, DK, DV, C, varlen, a.n_seqs, sizeof(T));
     float* g_ws = reinterpret_cast<float*>(a.ws + L.g);
     T* Tb_ws = reinterpret_cast<T*>(a.ws + L.Tb);
 
@@ -170,7 +175,16 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     const T* k = static_cast<const T*>(a.k);
     const T* v = static_cast<const T*>(a.v);
 
-    if (L.slots > 0) {
+    if (RULE == kNoErase && L.slots > 0) {
+        constexpr int WPB = kThreads / 64;
+        const int64_t units = L.slots * a.H;
+        tm->mark(a.stream);
+        hipLaunchKernelGGL(gdn_gates_kernel<C>, dim3((unsigned)((units + WPB - 1) / WPB)), dim3(kThreads), 0,
+                           a.stream, a.log_alpha, a.beta, geom, a.H, (int)units, g_ws);
+        if (gdn_status s = check_launch(a.stream)) return s;
+        tm->mark(a.stream);
+    }
+    if (RULE == kDelta && L.slots > 0) {
         using P = PrepCfg<T, DK, C>;
         constexpr auto kp = gdn_prep_kernel<T, DK, C>;
         allow_smem<kp>(P::SMEM);
@@ -189,15 +203,15 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     {
         // the column-wave scan, with 32 state columns per workgroup where that
         // fits in LDS and still gives every CU a workgroup, else 16
-        using C32 = ColCfg<T, DK, DV, C, (DV >= 32 ? 32 : 16)>;
-        using C16 = ColCfg<T, DK, DV, C, 16>;
+        using C32 = ColCfg<T, DK, DV, C, (DV >= 32 ? 32 : 16), RULE>;
+        using C16 = ColCfg<T, DK, DV, C, 16, RULE>;
         constexpr bool fit32 = DV >= 32 && C32::FITS, fit16 = C16::FITS;
         const int64_t units = (int64_t)a.H * L.N;
         auto launch_cols = [&](auto cfg_tag) -> gdn_status {
             using CC = decltype(cfg_tag);
             if constexpr (CC::FITS) {
                 constexpr int DVT = CC::NVW * 16;
-                constexpr auto ks = gdn_scan_cols_kernel<T, DK, DV, C, DVT>;
+                constexpr auto ks = gdn_scan_cols_kernel<T, DK, DV, C, DVT, RULE>;
                 allow_smem<ks>(CC::SMEM);
                 tm->mark(a.stream);
                 hipLaunchKernelGGL(ks, dim3(DV / DVT, a.H, (unsigned)L.N), dim3(CC::NTHR), CC::SMEM,
@@ -224,19 +238,33 @@ struct Variant {
     FwdFn fn;
 };
 
+// compiled instantiations of each rule
 const Variant kVariants[] = {
-    {16, 16, 16, GDN_F32, launch_fwd<float, 16, 16, 16>},
-    {64, 64, 16, GDN_F32, launch_fwd<float, 64, 64, 16>},
-    {64, 64, 64, GDN_F32, launch_fwd<float, 64, 64, 64>},
-    {128, 128, 64, GDN_F32, launch_fwd<float, 128, 128, 64>},
-    {128, 256, 64, GDN_F32, launch_fwd<float, 128, 256, 64>},
-    {128, 128, 64, GDN_BF16, launch_fwd<bf16, 128, 128, 64>},
-    {128, 256, 64, GDN_BF16, launch_fwd<bf16, 128, 256, 64>},
+    {16, 16, 16, GDN_F32, launch_fwd<float, 16, 16, 16, kDelta>},
+    {64, 64, 16, GDN_F32, launch_fwd<float, 64, 64, 16, kDelta>},
+    {64, 64, 64, GDN_F32, launch_fwd<float, 64, 64, 64, kDelta>},
+    {128, 128, 64, GDN_F32, launch_fwd<float, 128, 128, 64, kDelta>},
+    {128, 256, 64, GDN_F32, launch_fwd<float, 128, 256, 64, kDelta>},
+    {128, 128, 64, GDN_BF16, launch_fwd<bf16, 128, 128, 64, kDelta>},
+    {128, 256, 64, GDN_BF16, launch_fwd<bf16, 128, 256, 64, kDelta>},
+};
+const Variant kVariantsNoErase[] = {
+    {16, 16, 16, GDN_F32, launch_fwd<float, 16, 16, 16, kNoErase>},
+    {64, 64, 64, GDN_F32, launch_fwd<float, 64, 64, 64, kNoErase>},
+    {128, 128, 64, GDN_BF16, launch_fwd<bf16, 128, 128, 64, kNoErase>},
+    {128, 256, 64, GDN_BF16, launch_fwd<bf16, 128, 256, 64, kNoErase>},
 };
 
-const Variant* find_variant(int dk, int dv, int c, gdn_dtype dt) {
-    for (const Variant& v : kVariants)
-        if (v.dk == dk && v.dv == dv && v.c == c && v.dt == dt) return &v;
+bool valid_rule(int rule) { return rule == GDN_RULE_DELTA || rule == GDN_RULE_MAMBA2; }
+
+const Variant* find_variant(int rule, int dk, int dv, int c, gdn_dtype dt) {
+    auto scan = [&](const Variant* b, const Variant* e) -> const Variant* {
+        for (const Variant* v = b; v != e; ++v)
+            if (v->dk == dk && v->dv == dv && v->c == c && v->dt == dt) return v;
+        return nullptr;
+    };
+    if (rule == GDN_RULE_DELTA) return scan(std::begin(kVariants), std::end(kVariants));
+    if (rule == GDN_RULE_MAMBA2) return scan(std::begin(kVariantsNoErase), std::end(kVariantsNoErase));
     return nullptr;
 }
 
@@ -247,9 +275,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kMaxElems = 0x7fffffffLL;
 
 // Host-side checks shared by the size query and the forward call.
-gdn_status check_sizes(int B, int T, int H, int Dk, int Dv, int C, bool varlen, int n_seqs,
-                       gdn_dtype dt) {
+gdn_status check_sizes(int rule, int B, int T, int H, int Dk, int Dv, int C, bool varlen,
+                       int n_seqs, gdn_dtype dt) {
     if (dt != GDN_F32 && dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!valid_rule(rule)) return GDN_ERR_UNSUPPORTED;
     if (B < 1 || T < 0 || H < 1 || H > 65535 || Dk < 1 || Dv < 1 || C < 1) return GDN_ERR_SHAPE;
     if (varlen && (B != 1 || n_seqs < 1 || n_seqs > 65535)) return GDN_ERR_SHAPE;
     if (!varlen && B > 65535) return GDN_ERR_SHAPE;
@@ -260,7 +289,7 @@ gdn_status check_sizes(int B, int T, int H, int Dk, int Dv, int C, bool varlen, 
     if (N * H * (int64_t)Dv * Dk > kMaxElems) return GDN_ERR_SHAPE;
     // the scan addresses one chunk of one token tensor with 31-bit byte offsets
     if ((int64_t)C * H * dmax * elem_size(dt) > kMaxElems) return GDN_ERR_SHAPE;
-    if (!find_variant(Dk, Dv, C, dt)) return GDN_ERR_UNSUPPORTED;
+    if (!find_variant(rule, Dk, Dv, C, dt)) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
@@ -269,15 +298,24 @@ gdn_status check_sizes(int B, int T, int H, int Dk, int Dv, int C, bool varlen, 
 
 using namespace gdn;
 
+extern "C" int gdn_rule_supported(gdn_rule rule, int Dk, int Dv, int C, gdn_dtype dt) {
+    return find_variant(rule, Dk, Dv, C, dt) ? 1 : 0;
+}
+
 extern "C" int gdn_chunk_fwd_supported(int Dk, int Dv, int C, gdn_dtype dt) {
-    return find_variant(Dk, Dv, C, dt) ? 1 : 0;
+    return gdn_rule_supported(GDN_RULE_DELTA, Dk, Dv, C, dt);
+}
+
+extern "C" size_t gdn_rule_workspace_bytes(gdn_rule rule, int B, int T, int H, int Dk, int Dv,
+                                           int C, int n_seqs, gdn_dtype dt) {
+    const bool varlen = n_seqs > 0;
+    if (check_sizes(rule, B, T, H, Dk, Dv, C, varlen, n_seqs, dt) != GDN_OK) return 0;
+    return make_layout(rule, B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt)).total;
 }
 
 extern "C" size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
                                                 int n_seqs, gdn_dtype dt) {
-    const bool varlen = n_seqs > 0;
-    if (check_sizes(B, T, H, Dk, Dv, C, varlen, n_seqs, dt) != GDN_OK) return 0;
-    return make_layout(B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt)).total;
+    return gdn_rule_workspace_bytes(GDN_RULE_DELTA, B, T, H, Dk, Dv, C, n_seqs, dt);
 }
 
 // ---------------------------------------------------------------------------
@@ -312,23 +350,27 @@ void* scratch_device_ptr() {
     return p;
 }
 
-// use_scratch: run on the static scratch buffer instead of `workspace`
-gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* log_alpha,
-                          const float* beta, const float* S0, const int32_t* cu_seqlens,
-                          int n_seqs, void* O, float* S_T, int B, int T, int H, int Dk, int Dv,
-                          int C, gdn_dtype dt, void* workspace, size_t workspace_bytes,
-                          bool use_scratch, void* stream, KernelTimer* tm) {
+// use_scratch: run on the static scratch buffer instead of `workspace`;
+// tm == NULL: only the host-side argument checks (no HIP call is made)
+gdn_status chunk_fwd_impl(int rule, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* beta, const float* S0,
+                          const int32_t* cu_seqlens, int n_seqs, void* O, float* S_T, int B,
+                          int T, int H, int Dk, int Dv, int C, gdn_dtype dt, void* workspace,
+                          size_t workspace_bytes, bool use_scratch, void* stream,
+                          KernelTimer* tm) {
     const bool varlen = cu_seqlens != nullptr;
-    // with no tokens the token tensors are never read (empty tensors may be NULL)
+    // with no tokens the token tensors are never read (empty tensors may be
+    // NULL); beta may be NULL (beta = 1) for the no-erase rule only
     const bool has_tokens = T > 0;
-    if (has_tokens && (!q || !k || !v || !beta || !O)) return GDN_ERR_NULL;
-    if (gdn_status s = check_sizes(B, T, H, Dk, Dv, C, varlen, n_seqs, dt)) return s;
+    if (has_tokens && (!q || !k || !v || (!beta && rule == GDN_RULE_DELTA) || !O)) return GDN_ERR_NULL;
+    if (gdn_status s = check_sizes(rule, B, T, H, Dk, Dv, C, varlen, n_seqs, dt)) return s;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(S0) ||
         !aligned16(S_T))
         return GDN_ERR_SHAPE;
-    const Layout L = make_layout(B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt));
+    const Layout L = make_layout(rule, B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt));
     if (use_scratch) {
         if (L.total > kScratchBytes) return GDN_ERR_SCRATCH_LIMIT;
+        if (!tm) return GDN_OK;
         workspace = scratch_device_ptr();
         if (!workspace) return GDN_ERR_HIP;
         workspace_bytes = kScratchBytes;
@@ -336,11 +378,12 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     if (!aligned16(workspace)) return GDN_ERR_SHAPE;
     if (L.total > 0 && !workspace) return GDN_ERR_NULL;
     if (workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+    if (!tm) return GDN_OK;
     FwdArgs a{q, k, v, log_alpha, beta, S0, cu_seqlens, varlen ? n_seqs : B, O, S_T,
               B, T, H, Dk, Dv, C, dt, static_cast<unsigned char*>(workspace),
               static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();   // report only errors raised by this call's launches
-    return find_variant(Dk, Dv, C, dt)->fn(a, tm);
+    return find_variant(rule, Dk, Dv, C, dt)->fn(a, tm);
 }
 }  // namespace
 
@@ -351,8 +394,9 @@ extern "C" gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                                     void* workspace, size_t workspace_bytes, void* stream) {
     try {
         KernelTimer off;
-        return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O, S_T, B, T, H,
-                              Dk, Dv, C, dt, workspace, workspace_bytes, false, stream, &off);
+        return chunk_fwd_impl(GDN_RULE_DELTA, q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs,
+                              O, S_T, B, T, H, Dk, Dv, C, dt, workspace, workspace_bytes, false,
+                              stream, &off);
     } catch (...) {
         return GDN_ERR_INTERNAL;
     }
@@ -365,23 +409,45 @@ extern "C" gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const 
                                             int Dk, int Dv, int C, gdn_dtype dt, void* stream) {
     try {
         KernelTimer off;
-        return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O, S_T, B, T, H,
-                              Dk, Dv, C, dt, nullptr, 0, true, stream, &off);
+        return chunk_fwd_impl(GDN_RULE_DELTA, q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs,
+                              O, S_T, B, T, H, Dk, Dv, C, dt, nullptr, 0, true, stream, &off);
     } catch (...) {
         return GDN_ERR_INTERNAL;
     }
 }
 
-extern "C" gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v,
-                                             const float* log_alpha, const float* beta,
-                                             const float* S0, const int32_t* cu_seqlens,
-                                             int n_seqs, void* O, float* S_T, int B, int T,
-                                             int H, int Dk, int Dv, int C, gdn_dtype dt,
-                                             void* workspace, size_t workspace_bytes,
-                                             void* stream, float* kernel_ms) {
+extern "C" gdn_status gdn_mamba2_chunk_fwd(const void* q, const void* k, const void* v,
+                                           const float* log_alpha, const float* beta,
+                                           const float* S0, const int32_t* cu_seqlens,
+                                           int n_seqs, void* O, float* S_T, int B, int T, int H,
+                                           int Dk, int Dv, int C, gdn_dtype dt, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+    try {
+        KernelTimer off;
+        return chunk_fwd_impl(GDN_RULE_MAMBA2, q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs,
+                              O, S_T, B, T, H, Dk, Dv, C, dt, workspace, workspace_bytes, false,
+                              stream, &off);
+    } catch (...) {
+        return GDN_ERR_INTERNAL;
+    }
+}
+
+extern "C" gdn_status gdn_rule_chunk_fwd_profiled(gdn_rule rule, const void* q, const void* k,
+                                                  const void* v, const float* log_alpha,
+                                                  const float* beta, const float* S0,
+                                                  const int32_t* cu_seqlens, int n_seqs, void* O,
+                                                  float* S_T, int B, int T, int H, int Dk, int Dv,
+                                                  int C, gdn_dtype dt, void* workspace,
+                                                  size_t workspace_bytes, void* stream,
+                                                  float* kernel_ms) {
     if (!kernel_ms) return GDN_ERR_NULL;
     for (int i = 0; i < 4; ++i) kernel_ms[i] = 0.f;
     try {
+        // argument errors before any HIP call
+        if (gdn_status s = chunk_fwd_impl(rule, q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs,
+                                          O, S_T, B, T, H, Dk, Dv, C, dt, workspace,
+                                          workspace_bytes, false, stream, nullptr))
+            return s;
         KernelTimer tm;
         tm.on = true;
         for (int i = 0; i < 8; ++i) {
@@ -390,12 +456,13 @@ extern "C" gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const
                 return GDN_ERR_HIP;
             }
         }
-        gdn_status s = chunk_fwd_impl(q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O, S_T,
-                                      B, T, H, Dk, Dv, C, dt, workspace, workspace_bytes, false,
-                                      stream, &tm);
+        gdn_status s = chunk_fwd_impl(rule, q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O,
+                                      S_T, B, T, H, Dk, Dv, C, dt, workspace, workspace_bytes,
+                                      false, stream, &tm);
         if (s == GDN_OK && hipEventSynchronize(tm.ev[tm.n - 1]) != hipSuccess) s = GDN_ERR_HIP;
         if (s == GDN_OK) {
-            // pairs of marks: [table], [prep], scan (prep absent when there are no chunks)
+            // pairs of marks: [table], [prep or gates], scan (prep absent when
+            // there are no chunks)
             const bool varlen = cu_seqlens != nullptr;
             const bool has_chunks = tm.n >= (varlen ? 6 : 4);
             int slot[4] = {-1, -1, -1, -1};
@@ -416,6 +483,18 @@ extern "C" gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const
     } catch (...) {
         return GDN_ERR_INTERNAL;
     }
+}
+
+extern "C" gdn_status gdn_chunk_fwd_profiled(const void* q, const void* k, const void* v,
+                                             const float* log_alpha, const float* beta,
+                                             const float* S0, const int32_t* cu_seqlens,
+                                             int n_seqs, void* O, float* S_T, int B, int T,
+                                             int H, int Dk, int Dv, int C, gdn_dtype dt,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream, float* kernel_ms) {
+    return gdn_rule_chunk_fwd_profiled(GDN_RULE_DELTA, q, k, v, log_alpha, beta, S0, cu_seqlens,
+                                       n_seqs, O, S_T, B, T, H, Dk, Dv, C, dt, workspace,
+                                       workspace_bytes, stream, kernel_ms);
 }
 
 namespace gdn {

@@ -26,6 +26,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16 raw byte
 
 constexpr int kThreads = 256;   // 4 waves per workgroup (prep)
 
+// Update rules the chunk kernels evaluate (the C ABI's gdn_rule values):
+//  kDelta    S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+//  kNoErase  S_t = alpha_t S_{t-1} + beta_t v_t k_t^T   (Mamba2 with a write strength)
+enum : int { kDelta = 0, kNoErase = 1 };
+// fp32 rows per chunk of the gate values handed to the scan: g, exp(g),
+// exp(g_n - g), and for kNoErase beta as a fourth row
+constexpr int gate_rows(int rule) { return rule == kDelta ? 3 : 4; }
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // wave index, known to the compiler to be uniform across the wave
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

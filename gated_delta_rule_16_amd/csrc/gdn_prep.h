@@ -342,4 +342,40 @@ __global__ __launch_bounds__(kThreads, (PrepCfg<T, DK, C>::MIN_WAVES_SIMD)) void
     for (int u = blockIdx.x * Cfg::WAVES + w; u < units; u += stride) process(u, kf);
 }
 
+// Per-chunk gates of the no-erase rule, the only per-chunk preparation it
+// needs (the chunk form of the Qiita article's "Chunk Computation" section,
+// Mamba2 case, uses the in-chunk decays only): for every (chunk slot, head)
+// unit, g_i = sum_{t<=i} log alpha_t, exp(g_i), exp(g_n - g_i) and beta_i, as
+// four fp32 rows of C.  One wave per unit, lane = token; beta NULL means
+// beta = 1; rows past the chunk end act as tokens with log alpha = 0, beta = 0.
+template <int C>
+__global__ __launch_bounds__(kThreads) void gdn_gates_kernel(const float* __restrict__ log_alpha,
+                                                             const float* __restrict__ beta, SeqGeom geom,
+                                                             int H, int units, float* __restrict__ g_ws) {
+    static_assert(C <= 64, "one lane per token");
+    const int l = lane_id();
+    const int u = (int)blockIdx.x * (kThreads / 64) + wave_id();
+    if (u >= units) return;
+    const int slot = u / H, h = u - slot * H;
+    const ChunkInfo ci = chunk_info(geom, slot);
+    if (ci.len <= 0) return;   // unused packed-batch slot
+    const bool in = l < ci.len;
+    const int64_t x = ((int64_t)ci.t0 + (in ? l : 0)) * H + h;
+    float g = in && log_alpha ? log_alpha[x] : 0.f;
+    const float be = in ? (beta ? beta[x] : 1.f) : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(g, off, 64);
+        if (l >= off) g += y;
+    }
+    const float glast = __shfl(g, C - 1, 64);
+    if (l < C) {
+        float* out = g_ws + (int64_t)u * gate_rows(kNoErase) * C;
+        out[l] = g;
+        out[C + l] = __expf(g);
+        out[2 * C + l] = __expf(glast - g);
+        out[3 * C + l] = be;
+    }
+}
+
 }  // namespace gdn

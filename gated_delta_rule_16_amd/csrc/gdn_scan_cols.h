@@ -9,6 +9,11 @@
 // (Qiita, the Linear Attention lineage, section "Gated-DeltaNet" and "Chunk
 // Computation"; LinearAttention系列解读(六), sections 4.4 and 4.5).
 //
+// Rule kNoErase (the same article's "Mamba2" update with a write strength,
+// S_t = alpha_t S_{t-1} + beta_t v_t k_t^T, in the chunk form of its "Chunk
+// Computation" section): there is no prediction to remove, so Y and Tb drop
+// out and V' = diag(beta) V; the output and the state update are unchanged.
+//
 // Work split.  A workgroup owns a DVT-column slice of one (sequence, head):
 //  - column waves (DVT / 16): wave vb holds all Dk rows of columns vb*16 ..
 //    vb*16 + 15 of S^T in MFMA accumulators and runs the recurrence alone --
@@ -41,9 +46,11 @@
 
 namespace gdn {
 
-template <typename T, int DK, int DV, int C, int DVT>
+template <typename T, int DK, int DV, int C, int DVT, int RULE = kDelta>
 struct ColCfg {
     static constexpr bool BF = sizeof(T) == 2;
+    static constexpr bool ERASE = RULE == kDelta;          // delta rule: Y, X and Tb
+    static constexpr int NGR = gate_rows(RULE);            // fp32 gate rows per chunk
     static constexpr int ES = sizeof(T);
     static constexpr int NW = C / 16;                      // 16-token blocks of a chunk
     static constexpr int NVW = DVT / 16;                   // column waves
@@ -70,7 +77,7 @@ struct ColCfg {
     static constexpr int blocks(int bytes) { return (bytes + 1023) / 1024; }
     static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
     static constexpr int NIK = blocks(C * LDK * ES), NIV = blocks(C * LDV * ES);
-    static constexpr int NIT = tb_blocks(C, BF), NIG = blocks(3 * C * 4);
+    static constexpr int NIT = ERASE ? tb_blocks(C, BF) : 0, NIG = blocks(NGR * C * 4);
     static constexpr int BT = NIK, BV = BT + NIT, BG = BV + NIV, NI = BG + NIG;
     static constexpr int NL = cdiv(NI, NLD);               // loads per loading lane per chunk
     // loads loading wave f issues per chunk
@@ -168,7 +175,7 @@ __device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_
         case 3: off = region((i - Cfg::BV) * 64 + l, Cfg::VP, Cfg::VB, Cfg::VSW, rs_v); break;
         case 4: {
             const int s = (i - Cfg::BG) * 64 + l;
-            off = s < 3 * C / 4 ? (int64_t)s * 16 : -1;
+            off = s < Cfg::NGR * C / 4 ? (int64_t)s * 16 : -1;
             break;
         }
         default: break;
@@ -195,13 +202,13 @@ __device__ __forceinline__ typename K16<T>::op kT_tile(const T* sK, int kb, int 
     }
 }
 
-template <typename T, int DK, int DV, int C, int DVT>
+template <typename T, int DK, int DV, int C, int DVT, int RULE>
 __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* S0, SeqGeom geom, int H,
     const float* __restrict__ g_ws, const T* __restrict__ Tb_ws,
     T* __restrict__ O, float* S_T) {   // S_T may alias S0
-    using Cfg = ColCfg<T, DK, DV, C, DVT>;
+    using Cfg = ColCfg<T, DK, DV, C, DVT, RULE>;
     static_assert(Cfg::FITS, "scan workgroup exceeds the LDS of one CU");
     using St16 = Step<T>;
     using Frag = typename St16::frag;
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
     };
     struct Staged {
         const T *K, *V, *Tb;
-        const float *g, *gam, *dec;
+        const float *g, *gam, *dec, *beta;
     };
     auto staged = [&](int cc) __attribute__((always_inline)) {
         const unsigned char* sb = smem + (cc % Cfg::NSTG) * Cfg::SZ_STAGE;
@@ -268,6 +275,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         st.g = reinterpret_cast<const float*>(sb + Cfg::OFF_G);
         st.gam = st.g + C;
         st.dec = st.g + 2 * C;
+        st.beta = st.g + 3 * C;   // kNoErase only
         return st;
     };
     // staged Q of chunk cd
@@ -308,74 +316,87 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         constexpr int KPF = NKK * NW * (int)sizeof(Frag) <= 256 ? NKK : 256 / (NW * (int)sizeof(Frag));
         auto step = [&](const int cc) __attribute__((always_inline)) {
             const Staged st = staged(cc);
-            Frag fk[KPF][NW];
+            float4 dec4[NW];
+            f32x4 vv[NW], Vp[NW];
+            Op kt[NDB][NW];   // K^T operands of the state update
+            const float gamma_n = st.gam[C - 1];
+            if constexpr (Cfg::ERASE) {
+                Frag fk[KPF][NW];
 #pragma unroll
-            for (int kk = 0; kk < KPF; ++kk)
+                for (int kk = 0; kk < KPF; ++kk)
 #pragma unroll
-                for (int tb = 0; tb < NW; ++tb) fk[kk][tb] = kfrag_rows<Cfg>(st.K, tb * 16, kk * KS);
-            float4 gam4[NW], dec4[NW];
-            float gamma_n;
-            f32x4 vv[NW];
-            typedef typename std::conditional<Cfg::BF, bf16x8, f32x4>::type TFrag;
-            constexpr int NTP = Cfg::BF ? NP : NW;
-            TFrag ta[NW][NTP];
-#pragma unroll
-            for (int tb = 0; tb < NW; ++tb) {
-                gam4[tb] = *reinterpret_cast<const float4*>(st.gam + tb * 16 + g4);
-                dec4[tb] = *reinterpret_cast<const float4*>(st.dec + tb * 16 + g4);
-                vv[tb] = vcol4<Cfg>(st.V, tb, vb);
-            }
-            gamma_n = st.gam[C - 1];
-#pragma unroll
-            for (int ib = 0; ib < NW; ++ib)
-#pragma unroll
-                for (int p = 0; p < NTP; ++p)
-                    if ((Cfg::BF ? 2 * p : p) <= ib)
-                        ta[ib][p] = *reinterpret_cast<const TFrag*>(reinterpret_cast<const unsigned char*>(st.Tb) +
-                                                                    tb_block(ib, p, Cfg::BF) * 1024 + l * 16);
-            // Y = K S^T (A: K rows; B: the state tiles) for every token block
-            f32x4 Y[NW];
-#pragma unroll
-            for (int tb = 0; tb < NW; ++tb) Y[tb] = zero4();
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
+                    for (int tb = 0; tb < NW; ++tb) fk[kk][tb] = kfrag_rows<Cfg>(st.K, tb * 16, kk * KS);
+                float4 gam4[NW];
+                typedef typename std::conditional<Cfg::BF, bf16x8, f32x4>::type TFrag;
+                constexpr int NTP = Cfg::BF ? NP : NW;
+                TFrag ta[NW][NTP];
 #pragma unroll
                 for (int tb = 0; tb < NW; ++tb) {
-                    if constexpr (Cfg::BF) Y[tb] = KO::mma2p(fk[kk % KPF][tb], Sb[2 * kk], Sb[2 * kk + 1], Y[tb]);
-                    else Y[tb] = St16::mma(fk[kk % KPF][tb], Sb[kk], Y[tb]);
+                    gam4[tb] = *reinterpret_cast<const float4*>(st.gam + tb * 16 + g4);
+                    dec4[tb] = *reinterpret_cast<const float4*>(st.dec + tb * 16 + g4);
+                    vv[tb] = vcol4<Cfg>(st.V, tb, vb);
                 }
-                if (kk + KPF < NKK) {
 #pragma unroll
-                    for (int tb = 0; tb < NW; ++tb) fk[kk % KPF][tb] = kfrag_rows<Cfg>(st.K, tb * 16, (kk + KPF) * KS);
+                for (int ib = 0; ib < NW; ++ib)
+#pragma unroll
+                    for (int p = 0; p < NTP; ++p)
+                        if ((Cfg::BF ? 2 * p : p) <= ib)
+                            ta[ib][p] = *reinterpret_cast<const TFrag*>(reinterpret_cast<const unsigned char*>(st.Tb) +
+                                                                        tb_block(ib, p, Cfg::BF) * 1024 + l * 16);
+                // Y = K S^T (A: K rows; B: the state tiles) for every token block
+                f32x4 Y[NW];
+#pragma unroll
+                for (int tb = 0; tb < NW; ++tb) Y[tb] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+                    for (int tb = 0; tb < NW; ++tb) {
+                        if constexpr (Cfg::BF) Y[tb] = KO::mma2p(fk[kk % KPF][tb], Sb[2 * kk], Sb[2 * kk + 1], Y[tb]);
+                        else Y[tb] = St16::mma(fk[kk % KPF][tb], Sb[kk], Y[tb]);
+                    }
+                    if (kk + KPF < NKK) {
+#pragma unroll
+                        for (int tb = 0; tb < NW; ++tb) fk[kk % KPF][tb] = kfrag_rows<Cfg>(st.K, tb * 16, (kk + KPF) * KS);
+                    }
                 }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // K^T operands of the state update
-            Op kt[NDB][NW];
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < NDB; ++i)
+                for (int i = 0; i < NDB; ++i)
 #pragma unroll
-                for (int kb = 0; kb < NW; ++kb) kt[i][kb] = kT_tile<Cfg>(st.K, kb, i);
-            // X = V - diag(gamma) Y, as the B operand of V' = Tb X
-            Op Xo[NW];
+                    for (int kb = 0; kb < NW; ++kb) kt[i][kb] = kT_tile<Cfg>(st.K, kb, i);
+                // X = V - diag(gamma) Y, as the B operand of V' = Tb X
+                Op Xo[NW];
 #pragma unroll
-            for (int tb = 0; tb < NW; ++tb)
-                Xo[tb] = KO::tile(f32x4{vv[tb][0] - gam4[tb].x * Y[tb][0], vv[tb][1] - gam4[tb].y * Y[tb][1],
-                                        vv[tb][2] - gam4[tb].z * Y[tb][2], vv[tb][3] - gam4[tb].w * Y[tb][3]});
-            // V' = Tb X (A: Tb rows, token pairs as X)
-            f32x4 Vp[NW];
+                for (int tb = 0; tb < NW; ++tb)
+                    Xo[tb] = KO::tile(f32x4{vv[tb][0] - gam4[tb].x * Y[tb][0], vv[tb][1] - gam4[tb].y * Y[tb][1],
+                                            vv[tb][2] - gam4[tb].z * Y[tb][2], vv[tb][3] - gam4[tb].w * Y[tb][3]});
+                // V' = Tb X (A: Tb rows, token pairs as X)
 #pragma unroll
-            for (int ib = 0; ib < NW; ++ib) {
-                f32x4 acc = zero4();
-                if constexpr (Cfg::BF) {
+                for (int ib = 0; ib < NW; ++ib) {
+                    f32x4 acc = zero4();
+                    if constexpr (Cfg::BF) {
 #pragma unroll
-                    for (int p = 0; p < NP; ++p)
-                        if (2 * p <= ib) acc = KO::mma2p(ta[ib][p], Xo[2 * p], Xo[2 * p + 1], acc);
-                } else {
+                        for (int p = 0; p < NP; ++p)
+                            if (2 * p <= ib) acc = KO::mma2p(ta[ib][p], Xo[2 * p], Xo[2 * p + 1], acc);
+                    } else {
 #pragma unroll
-                    for (int jb = 0; jb <= ib; ++jb) acc = KO::mma1(ta[ib][jb], Xo[jb], acc);
+                        for (int jb = 0; jb <= ib; ++jb) acc = KO::mma1(ta[ib][jb], Xo[jb], acc);
+                    }
+                    Vp[ib] = acc;
                 }
-                Vp[ib] = acc;
+            } else {
+                // no prediction to remove: V' = diag(beta) V
+#pragma unroll
+                for (int i = 0; i < NDB; ++i)
+#pragma unroll
+                    for (int kb = 0; kb < NW; ++kb) kt[i][kb] = kT_tile<Cfg>(st.K, kb, i);
+#pragma unroll
+                for (int tb = 0; tb < NW; ++tb) {
+                    dec4[tb] = *reinterpret_cast<const float4*>(st.dec + tb * 16 + g4);
+                    const float4 b4 = *reinterpret_cast<const float4*>(st.beta + tb * 16 + g4);
+                    vv[tb] = vcol4<Cfg>(st.V, tb, vb);
+                    Vp[tb] = f32x4{vv[tb][0] * b4.x, vv[tb][1] * b4.y, vv[tb][2] * b4.z, vv[tb][3] * b4.w};
+                }
             }
             // gamma_n S^T while V' completes
 #pragma unroll
@@ -631,7 +652,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             const T* kb = k + ((int64_t)t0 * H + h) * DK;
             const T* vb_ = v + ((int64_t)t0 * H + h) * DV + v0;
             const T* tb = Tb_ws + unit * (Cfg::NIT * 1024 / ES);
-            const float* gb = g_ws + unit * 3 * C;
+            const float* gb = g_ws + unit * Cfg::NGR * C;
             const int nk = (int)((len - 1) * rs_k + DK * ES), nv = (int)((len - 1) * rs_v + DVT * ES);
             unsigned char* dst = smem + (cd % Cfg::NSTG) * Cfg::SZ_STAGE + f * 1024;
 #pragma unroll
@@ -640,7 +661,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 if (r == 5) continue;
                 const void* base = r == 0 ? (const void*)kb : r == 2 ? (const void*)tb : r == 3 ? (const void*)vb_
                                  : (const void*)gb;
-                const int nrec = r == 0 ? nk : r == 2 ? Cfg::NIT * 1024 : r == 3 ? nv : 3 * C * 4;
+                const int nrec = r == 0 ? nk : r == 2 ? Cfg::NIT * 1024 : r == 3 ? nv : Cfg::NGR * C * 4;
                 lds_load16(make_rsrc(base, nrec), dst + j * Cfg::NLD * 1024, soff[j]);
             }
         };
@@ -688,7 +709,9 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         // and writes Q once it is in, each into the buffer whose readers passed
         // the previous barrier; before its closing barrier it waits for all but
         // the newest DIST - 1 chunks of staging loads, i.e. for everything chunk
-        // cc + 1 needs (loads complete in issue order), and for its LDS writes
+        // cc + 1 needs (loads complete in issue order), and for its LDS writes.
+        // (Requesting Q a step earlier, so that its loads had a whole step to
+        // land, measured slower: 94 against 86 us on the headline.)
         static_assert(ND * (Cfg::DIST - 1) < 64, "vmcnt range");
         if (LOADER && count > 0) {
             if constexpr (Cfg::QLDS) {

@@ -57,11 +57,26 @@ typedef enum {
     GDN_BF16 = 1               /* q, k, v, O in bf16; fp32 accumulation and state */
 } gdn_dtype;
 
+/* The per-token update rule a chunked forward evaluates (see each entry point). */
+typedef enum {
+    GDN_RULE_DELTA = 0,        /* gdn_chunk_fwd:        S = a S (I - b k k^T) + b v k^T */
+    GDN_RULE_MAMBA2 = 1        /* gdn_mamba2_chunk_fwd: S = a S + b v k^T */
+} gdn_rule;
+
 /* Compiled (Dk, Dv, C, dtype) instantiations:
  *   (16, 16, 16, F32)  (64, 64, 16, F32)  (64, 64, 64, F32)
  *   (128, 128, 64, BF16) (128, 256, 64, BF16) (128, 128, 64, F32) (128, 256, 64, F32)
  * Returns 1 when the combination is compiled, 0 otherwise. */
 int gdn_chunk_fwd_supported(int Dk, int Dv, int C, gdn_dtype dt);
+
+/* As gdn_chunk_fwd_supported, for the entry point of `rule`.  Compiled for
+ * GDN_RULE_MAMBA2: (16, 16, 16, F32) (64, 64, 64, F32) (128, 128, 64, BF16)
+ * (128, 256, 64, BF16).  0 for an unknown rule. */
+int gdn_rule_supported(gdn_rule rule, int Dk, int Dv, int C, gdn_dtype dt);
+
+/* As gdn_chunk_fwd_workspace_bytes, for the entry point of `rule`. */
+size_t gdn_rule_workspace_bytes(gdn_rule rule, int B, int T, int H, int Dk, int Dv, int C,
+                                int n_seqs, gdn_dtype dt);
 
 /* Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 on bad
  * sizes).  n_seqs is only read when cu_seqlens will be passed (B must then be
@@ -155,6 +170,40 @@ gdn_status gdn_chunk_fwd_profiled(const void *q, const void *k, const void *v,
                                   int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
                                   void *workspace, size_t workspace_bytes, void *stream,
                                   float *kernel_ms);
+
+/* Chunked forward of the scalar-gated linear recurrence without the delta
+ * rule's erase term (Mamba2 with a write strength beta):
+ *     S_t = alpha_t S_{t-1} + beta_t v_t k_t^T,   o_t = S_t q_t
+ * Definition: the Qiita article by Nyysyyan on the Linear Attention lineage,
+ * section "Mamba2" (update of S_i, read h_i = S_i q_i; its closed form
+ * H = S_0 Q D_gamma + V (Gamma o K^T Q)), here with V D_beta in place of V;
+ * chunked as in that article's section "Chunk Computation" (Mamba2 case: the
+ * chunk output from the chunk-start state and the in-chunk decays, then the
+ * state handed to the next chunk).  It is the "GLA (scalar gate)" row of the
+ * form table in LinearAttention系列解读(六)'s summary; with log_alpha NULL it is
+ * plain linear attention (the Qiita article's section "Linear attention").
+ * Arguments, layouts, ownership, asynchrony and errors as gdn_chunk_fwd, except:
+ *  beta   [B][T][H] fp32, or NULL for beta = 1;
+ *  workspace  at least gdn_rule_workspace_bytes(GDN_RULE_MAMBA2, ...) bytes;
+ *  supported sizes: gdn_rule_supported(GDN_RULE_MAMBA2, ...). */
+gdn_status gdn_mamba2_chunk_fwd(const void *q, const void *k, const void *v,
+                                const float *log_alpha, const float *beta, const float *S0,
+                                const int32_t *cu_seqlens, int n_seqs,
+                                void *O, float *S_T,
+                                int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* gdn_chunk_fwd_profiled for the entry point of `rule` (same arguments as
+ * that entry point, then kernel_ms; kernel_ms[1] is the per-chunk preparation
+ * of that rule: prep for GDN_RULE_DELTA, the gates kernel for
+ * GDN_RULE_MAMBA2).  Blocks until the call's work has finished. */
+gdn_status gdn_rule_chunk_fwd_profiled(gdn_rule rule, const void *q, const void *k, const void *v,
+                                       const float *log_alpha, const float *beta, const float *S0,
+                                       const int32_t *cu_seqlens, int n_seqs,
+                                       void *O, float *S_T,
+                                       int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
+                                       void *workspace, size_t workspace_bytes, void *stream,
+                                       float *kernel_ms);
 
 /* One token per sequence (decoding).  Updates the state in place and reads it:
  *     S <- alpha S (I - beta k k^T) + beta v k^T,   o = S q     (same section).

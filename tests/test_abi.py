@@ -56,6 +56,45 @@ def test_supported_instantiations(lib):
         assert lib.gdn_chunk_fwd_supported(*a) == 0, a
 
 
+def test_rule_queries(lib):
+    RULE_DELTA, RULE_MAMBA2 = 0, 1
+    for a in [(128, 128, 64, BF16), (128, 256, 64, BF16), (64, 64, 64, F32), (16, 16, 16, F32)]:
+        assert lib.gdn_rule_supported(RULE_MAMBA2, *a) == 1, a
+        assert lib.gdn_rule_supported(RULE_DELTA, *a) == lib.gdn_chunk_fwd_supported(*a)
+    assert lib.gdn_rule_supported(RULE_MAMBA2, 64, 64, 16, F32) == 0
+    assert lib.gdn_rule_supported(9, 128, 128, 64, BF16) == 0
+    f = lib.gdn_rule_workspace_bytes
+    assert f(RULE_DELTA, 4, 4096, 16, 128, 128, 64, 0, BF16) == \
+        lib.gdn_chunk_fwd_workspace_bytes(4, 4096, 16, 128, 128, 64, 0, BF16)
+    # no-erase: four fp32 gate rows per chunk and no Tb
+    slots, H, C = 4 * 64, 16, 64
+    assert f(RULE_MAMBA2, 4, 4096, 16, 128, 128, 64, 0, BF16) == slots * H * 4 * C * 4
+    assert f(9, 4, 4096, 16, 128, 128, 64, 0, BF16) == 0
+
+
+def test_mamba2_argument_errors(lib):
+    p = ctypes.c_void_p(1 << 20)
+
+    def call(**kw):
+        a = dict(q=p, k=p, v=p, la=None, beta=p, S0=None, cu=None, n=0, O=p, S_T=None,
+                 B=1, T=128, H=1, Dk=16, Dv=16, C=16, dt=F32, ws=p, wsb=0, st=None)
+        a.update(kw)
+        return lib.gdn_mamba2_chunk_fwd(a["q"], a["k"], a["v"], a["la"], a["beta"], a["S0"],
+                                        a["cu"], a["n"], a["O"], a["S_T"], a["B"], a["T"],
+                                        a["H"], a["Dk"], a["Dv"], a["C"], a["dt"], a["ws"],
+                                        a["wsb"], a["st"])
+    assert call(q=None) == GDN_ERR_NULL
+    assert call(ws=None, wsb=1 << 30) == GDN_ERR_NULL
+    assert call(wsb=16) == GDN_ERR_WORKSPACE          # beta NULL is allowed, the size is not
+    assert call(beta=None, wsb=16) == GDN_ERR_WORKSPACE
+    assert call(Dk=64, Dv=64, C=16) == GDN_ERR_UNSUPPORTED
+    assert call(B=0) == GDN_ERR_SHAPE
+    ms = (ctypes.c_float * 4)()
+    args = [p, p, p, None, p, None, None, 0, p, None, 1, 128, 1, 16, 16, 16, F32, p, 16, None]
+    assert lib.gdn_rule_chunk_fwd_profiled(7, *args, ms) == GDN_ERR_UNSUPPORTED
+    assert lib.gdn_rule_chunk_fwd_profiled(1, *args, None) == GDN_ERR_NULL
+
+
 def test_workspace_bytes(lib):
     f = lib.gdn_chunk_fwd_workspace_bytes
     a = f(4, 4096, 16, 128, 128, 64, 0, BF16)

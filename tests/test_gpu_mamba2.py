@@ -1,0 +1,111 @@
+"""Parity of gdn_mamba2_chunk_fwd (scalar gate, no erase term) with the fp64
+oracle's no-erase mode, on the GPU, through the C ABI.
+
+The recurrence is S_t = alpha_t S_{t-1} + beta_t v_t k_t^T, o_t = S_t q_t: the
+Qiita article's "Mamba2" update with a write strength.  The oracle's no-erase
+mode is pinned against that section's closed form (tests/oracle_pins.py,
+pin_mamba2_no_erase).  Tolerances as for the delta rule: max relative error
+1e-4 (fp32) and 2e-2 (bf16 inputs, fp32 accumulation), O and S_T separately.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import oracle  # noqa: E402
+import gated_delta_rule_16_amd as gdn  # noqa: E402
+from gated_delta_rule_16_amd.inputs import make_inputs, workload_inputs  # noqa: E402
+from test_gpu_parity import TOL, rel, rel_elem, say  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load_library()
+
+
+def check(inp, dtype, C=64, beta_none=False, tag=""):
+    say(f"[gpu] mamba2 {tag} q={tuple(inp.q.shape)} v={tuple(inp.v.shape)} {dtype} C={C} "
+        f"seed={inp.meta.get('seed')} beta={'1' if beta_none else 'drawn'}")
+    d = inp.to(DEV)
+    O, S = gdn.gdn_mamba2_chunk_fwd(d.q, d.k, d.v, d.log_alpha, None if beta_none else d.beta,
+                                    d.S0, d.cu_seqlens, chunk_size=C)
+    torch.cuda.synchronize()
+    O, S = O.double().cpu().numpy(), S.double().cpu().numpy()
+    be = torch.ones_like(inp.beta) if beta_none else inp.beta
+    Or, Sr = oracle.forward(inp.q, inp.k, inp.v, inp.log_alpha, be, inp.S0, inp.cu_seqlens,
+                            no_erase=True)
+    eo, es = rel(O, Or), rel(S, Sr)
+    say(f"      max rel err O {eo:.3e}  S_T {es:.3e}  (tol {TOL[dtype]:.0e}); element-wise "
+        f"O {rel_elem(O, Or):.3e}  S_T {rel_elem(S, Sr):.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+
+
+def test_mamba2_f32_b2_h4_t1024_d64():
+    w = workload_inputs("gdn_f32_b2_h4_t1024_d64")
+    check(w, "f32", tag="fp32 B2 H4 T1024 D64")
+
+
+def test_mamba2_bf16_b4_h16_t4096_d128():
+    check(workload_inputs("gdn_bf16_b4_h16_t4096_d128"), "bf16", tag="bf16 B4 H16 T4096 D128")
+
+
+def test_mamba2_bf16_varlen_dv256():
+    check(workload_inputs("gdn_bf16_varlen_65536_h16_dk128_dv256"), "bf16",
+          tag="packed 65536 tokens Dv256")
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv,C", [("f32", 16, 16, 16), ("f32", 64, 64, 64),
+                                           ("bf16", 128, 128, 64), ("bf16", 128, 256, 64)])
+@pytest.mark.parametrize("T", [1, 5, 64, 300])
+def test_mamba2_ragged(dtype, Dk, Dv, C, T):
+    inp = make_inputs(B=2, T=T, H=3, Dk=Dk, Dv=Dv, dtype=dtype, gated=True, s0=True,
+                      seed=1500 + T + Dv)
+    check(inp, dtype, C=C, tag="ragged")
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_mamba2_beta_one_and_linear_attention(dtype, D):
+    # beta NULL (= 1): the pages' Mamba2 update as printed; with log_alpha NULL
+    # as well it is plain linear attention
+    inp = make_inputs(B=2, T=200, H=2, Dk=D, Dv=D, dtype=dtype, gated=True, s0=True, seed=610)
+    check(inp, dtype, beta_none=True, tag="beta=1")
+    inp = make_inputs(B=2, T=200, H=2, Dk=D, Dv=D, dtype=dtype, gated=False, s0=False, seed=611)
+    check(inp, dtype, beta_none=True, tag="linear attention")
+
+
+@pytest.mark.parametrize("case", ["decay30", "resets"])
+def test_mamba2_degenerate_gates(case):
+    inp = make_inputs(B=2, T=200, H=2, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True, seed=620)
+    if case == "decay30":
+        inp.log_alpha = torch.full_like(inp.log_alpha, -30.0)
+    else:
+        inp.log_alpha = torch.zeros_like(inp.log_alpha)
+        inp.log_alpha[:, 5::37] = -80.0
+    check(inp, "bf16", tag=f"gates {case}")
+
+
+def test_mamba2_varlen_short_and_empty():
+    lengths = [0, 1, 63, 64, 65, 200, 0, 7, 130]
+    inp = make_inputs(B=1, T=sum(lengths), H=2, Dk=128, Dv=256, dtype="bf16", gated=True,
+                      s0=True, seed=630, lengths=lengths)
+    check(inp, "bf16", tag=f"varlen {lengths}")
+
+
+def test_mamba2_profiled_matches_plain_call():
+    inp = make_inputs(B=2, T=300, H=4, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True, seed=640)
+    d = inp.to(DEV)
+    O1, S1 = gdn.gdn_mamba2_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0)
+    O2, S2, ms = gdn.gdn_rule_chunk_fwd_profiled(gdn.GDN_RULE_MAMBA2, d.q, d.k, d.v, d.log_alpha,
+                                                 d.beta, d.S0)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(S1, S2)
+    assert ms[1] > 0 and ms[2] > 0
