@@ -7,7 +7,9 @@ arithmetic of the method), and the product path never imports it.
 
 Contents
   forward(...)      token-by-token recurrence in C (``gdn_oracle.c``), threaded
-                    over independent (sequence, head) units.
+                    over independent (sequence, head) units: the gated delta
+                    rule, its no-erase (Mamba2) form, each with a scalar or a
+                    per-channel (vector) gate.
   wy_vectors(...)   the w recursion of the WY representation (numpy, tiny sizes).
   u_vectors(...)    the gated u recursion (numpy, tiny sizes).
 
@@ -45,7 +47,7 @@ def _bind(path: str):
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     lib.gdn_oracle_forward.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64,
-                                       P, P, ctypes.c_int, ctypes.c_int]
+                                       P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.gdn_oracle_forward.restype = ctypes.c_int
     return lib
 
@@ -92,13 +94,16 @@ def forward(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
     """Run the gated delta rule token by token in fp64.
 
     Follows the Qiita Linear-Attention article, section "Gated-DeltaNet"
-    (S_i = a_i S_{i-1}(I - b_i k_i k_i^T) + b_i v_i k_i^T, h_i = S_i q_i) in the
-    gate / predict / delta / write order of the kkkzoz "linear-attention"
-    post, section "Workflow".
+    (S_i = a_i S_{i-1}(I - b_i k_i k_i^T) + b_i v_i k_i^T, h_i = S_i q_i),
+    token by token.  ``no_erase`` drops the prediction term (the same
+    article's "Mamba2" update with a write strength).  A per-channel gate is
+    selected by the shape of log_alpha, [B,T,H,Dk]: S~ = S diag(alpha_t) on
+    the key side (the vector-gated GLA that LinearAttention系列解读(六),
+    section 1, names), with or without the erase term.
 
-    Shapes: q, k [B,T,H,Dk]; v [B,T,H,Dv]; log_alpha, beta [B,T,H]
-    (log_alpha None -> alpha = 1); S0 [N,H,Dv,Dk] or None;
-    cu_seqlens [N+1] or None (then N = B).
+    Shapes: q, k [B,T,H,Dk]; v [B,T,H,Dv]; log_alpha [B,T,H] (scalar gate)
+    or [B,T,H,Dk] (per-channel gate) or None (alpha = 1); beta [B,T,H];
+    S0 [N,H,Dv,Dk] or None; cu_seqlens [N+1] or None (then N = B).
     Returns (O [B,T,H,Dv], S_T [N,H,Dv,Dk]) as fp64 numpy arrays
     (and the thread count when ``return_threads``).
     ``lib`` substitutes another build of the same C source (the mutation
@@ -109,7 +114,8 @@ def forward(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     assert k.shape == (B, T, H, Dk) and v.shape == (B, T, H, Dv)
-    assert be.shape == (B, T, H) and (la is None or la.shape == (B, T, H))
+    gate_vec = la is not None and la.ndim == 4
+    assert be.shape == (B, T, H) and (la is None or la.shape in ((B, T, H), (B, T, H, Dk)))
     cu = None
     if cu_seqlens is not None:
         cu = np.ascontiguousarray(np.asarray(
@@ -126,7 +132,7 @@ def forward(q, k, v, log_alpha, beta, S0=None, cu_seqlens=None, *,
         n_threads = default_threads()
     rc = (lib or _load()).gdn_oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be), _ptr(s0),
                                     _ptr(cu), N, B, T, H, Dk, Dv, _ptr(O), _ptr(S_T),
-                                    int(n_threads), 1 if no_erase else 0)
+                                    int(n_threads), 1 if no_erase else 0, 1 if gate_vec else 0)
     if rc < 1:
         raise RuntimeError(f"gdn_oracle_forward failed with code {rc}")
     return (O, S_T, rc) if return_threads else (O, S_T)

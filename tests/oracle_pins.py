@@ -14,7 +14,7 @@ Sources (cited by page title and section):
   [Q]  Qiita article by Nyysyyan on the Linear Attention lineage
        (sections "Linear attention", "Mamba2", "Gated-DeltaNet").
   [K]  kkkzoz blog post "linear-attention" (sections "Gated DeltaNet", "Workflow").
-  [M]  LinearAttention系列解读(六)：DeltaNet的Chunkwise Form推导 (section 3 and 4).
+  [M]  LinearAttention系列解读(六)：DeltaNet的Chunkwise Form推导 (sections 1, 3 and 4).
 """
 from __future__ import annotations
 
@@ -313,6 +313,120 @@ def pin_structure(forward, rng=None, **_):
     assert np.array_equal(Sp[1], s0p[1]), "empty sequence must return its S0"
 
 
+# ----------------------------------------------------------------------------
+# Per-channel (vector) gate: the gate of token t is D_t = diag(alpha_t) on the
+# key side of the state, S~ = S D_t ([M] section 1: the vector-gated GLA's
+# transition is a diagonal matrix that scales each state element on its own).
+# log_alpha of shape [B,T,H,Dk] selects it.
+# ----------------------------------------------------------------------------
+def _run_vec(forward, q, k, v, la, be, s0=None, **kw):
+    L = q.shape[0]
+    O, S = forward(q.reshape(1, L, 1, -1), k.reshape(1, L, 1, -1), v.reshape(1, L, 1, -1),
+                   la.reshape(1, L, 1, -1), be.reshape(1, L, 1),
+                   None if s0 is None else s0.reshape(1, 1, *s0.shape), **kw)
+    return O[0, :, 0, :], S[0, 0]
+
+
+def pin_vector_gate_golden(forward, **_):
+    """Hand-worked 3-token example with per-channel gates, with and without the
+    erase term (tests/golden/gla_vector_gate_2x2_worked.txt); exact dyadic values."""
+    g = load_golden("gla_vector_gate_2x2_worked.txt")
+    L, D = 3, 2
+    q, k, v = g["q"].reshape(L, D), g["k"].reshape(L, D), g["v"].reshape(L, D)
+    la, be, s0 = np.log(g["alpha"]).reshape(L, D), g["beta"], g["S0"].reshape(D, D)
+    for mode, no_erase in (("no_erase", True), ("erase", False)):
+        O, S = _run_vec(forward, q, k, v, la, be, s0, no_erase=no_erase)
+        _close(O, g[f"O_{mode}"].reshape(L, D), 1e-15, f"vector-gate golden O ({mode})")
+        _close(S, g[f"S_T_{mode}"].reshape(D, D), 1e-15, f"vector-gate golden S_T ({mode})")
+
+
+def pin_vector_gate_scalar_reduction(forward, rng=None, **_):
+    """Every channel of alpha_t equal: the per-channel gate is the scalar gate,
+    to the last bit (the same doubles multiply the same entries), in both modes."""
+    rng = rng or np.random.default_rng(21)
+    B, T, H, Dk, Dv = 2, 17, 2, 5, 3
+    q, k, v = rng.standard_normal((B, T, H, Dk)), rng.standard_normal((B, T, H, Dk)), rng.standard_normal((B, T, H, Dv))
+    be, la = rng.uniform(0.1, 0.9, (B, T, H)), -rng.uniform(0.01, 0.5, (B, T, H))
+    s0 = rng.standard_normal((B, H, Dv, Dk))
+    lav = np.repeat(la[..., None], Dk, axis=-1)
+    for no_erase in (False, True):
+        Os, Ss = forward(q, k, v, la, be, s0, no_erase=no_erase)
+        Ov, Sv = forward(q, k, v, lav, be, s0, no_erase=no_erase)
+        assert np.array_equal(Os, Ov) and np.array_equal(Ss, Sv), \
+            f"equal channels differ from the scalar gate (no_erase={no_erase})"
+
+
+def gla_closed_form(q, k, v, la, be, s0):
+    """Unrolled no-erase recurrence with a per-channel gate (row form, one unit):
+    with b_i = sum_{t<=i} log alpha_t (a vector over key channels),
+        S_i = S0 diag(e^{b_i}) + sum_{s<=i} beta_s v_s (k_s o e^{b_i - b_s})^T,
+        o_i = S0 (q_i o e^{b_i}) + sum_{s<=i} beta_s v_s sum_d q_id k_sd e^{b_id - b_sd}.
+    Evaluated densely with numpy (the exponent of every (i, s, d) formed
+    explicitly, masked to s <= i)."""
+    L = q.shape[0]
+    b = np.cumsum(la, axis=0)                               # [L, Dk]
+    E = np.exp(b[:, None, :] - b[None, :, :])               # [i, s, d]
+    mask = np.tril(np.ones((L, L)))[:, :, None]
+    P = np.einsum("id,sd,isd->is", q, k, E * mask)          # [i, s]
+    O = (q * np.exp(b)) @ s0.T + P @ (be[:, None] * v)
+    S = s0 * np.exp(b[-1])[None, :] + (be[:, None] * v).T @ (k * np.exp(b[-1] - b))
+    return O, S
+
+
+def pin_gla_closed_form(forward, rng=None, **_):
+    """The no-erase mode with a per-channel gate equals its unrolled closed
+    form (the diagonal transitions commute, so the decay between tokens s and
+    i of channel d is e^{b_id - b_sd})."""
+    rng = rng or np.random.default_rng(22)
+    L, Dk, Dv = 24, 6, 4
+    q, k, v = rng.standard_normal((L, Dk)), rng.standard_normal((L, Dk)), rng.standard_normal((L, Dv))
+    be, la = rng.uniform(0.1, 0.9, L), -rng.uniform(0.01, 0.6, (L, Dk))
+    s0 = rng.standard_normal((Dv, Dk))
+    O, S = _run_vec(forward, q, k, v, la, be, s0, no_erase=True)
+    Ow, Sw = gla_closed_form(q, k, v, la, be, s0)
+    _close(O, Ow, TIGHT, "GLA closed form O")
+    _close(S, Sw, TIGHT, "GLA closed form S_T")
+
+
+def pin_vector_gate_coordinate_retrieval(forward, rng=None, **_):
+    """Erase mode, keys = distinct coordinate vectors e_{c_i}, beta = 1, any S0:
+    token i overwrites column c_i with v_i, later tokens (other columns) only
+    scale it by their gate of channel c_i, so S_T e_{c_i} = (prod_{t>i}
+    alpha_t[c_i]) v_i.  (A diagonal gate keeps coordinate keys orthogonal.)"""
+    rng = rng or np.random.default_rng(23)
+    L, Dk, Dv = 6, 9, 4
+    cols = rng.permutation(Dk)[:L]
+    k = np.zeros((L, Dk))
+    k[np.arange(L), cols] = 1.0
+    q, v = rng.standard_normal((L, Dk)), rng.standard_normal((L, Dv))
+    la = -rng.uniform(0.01, 0.7, (L, Dk))
+    s0 = rng.standard_normal((Dv, Dk))
+    _, S = _run_vec(forward, q, k, v, la, np.ones(L), s0)
+    for i in range(L):
+        tail = np.exp(la[i + 1:, cols[i]].sum())
+        _close(S[:, cols[i]], tail * v[i], TIGHT, f"coordinate retrieval token {i}")
+
+
+def pin_vector_gate_key_permutation(forward, rng=None, **_):
+    """Renaming the key channels (the same permutation applied to q, k, the
+    per-channel gate and the columns of S0) leaves O unchanged and permutes the
+    columns of S_T, in both modes: each channel's gate travels with it."""
+    rng = rng or np.random.default_rng(24)
+    L, Dk, Dv = 15, 7, 3
+    q, k, v = rng.standard_normal((L, Dk)), 0.5 * rng.standard_normal((L, Dk)), rng.standard_normal((L, Dv))
+    be, la = rng.uniform(0.1, 0.9, L), -rng.uniform(0.01, 0.6, (L, Dk))
+    s0 = rng.standard_normal((Dv, Dk))
+    perm = rng.permutation(Dk)
+    for no_erase in (False, True):
+        O, S = _run_vec(forward, q, k, v, la, be, s0, no_erase=no_erase)
+        Op, Sp = _run_vec(forward, q[:, perm], k[:, perm], v, la[:, perm], be, s0[:, perm],
+                          no_erase=no_erase)
+        _close(Op, O, TIGHT, f"key permutation O (no_erase={no_erase})")
+        _close(Sp, S[:, perm], TIGHT, f"key permutation S_T (no_erase={no_erase})")
+
+
 ALL_PINS = [pin_golden, pin_identity_step, pin_retrieval_identity, pin_mamba2_no_erase,
             pin_mamba2_orthogonal_keys, pin_exact_retrieval, pin_wy_identity,
-            pin_product_form, pin_parallel_form, pin_linear_attention, pin_structure]
+            pin_product_form, pin_parallel_form, pin_linear_attention, pin_structure,
+            pin_vector_gate_golden, pin_vector_gate_scalar_reduction, pin_gla_closed_form,
+            pin_vector_gate_coordinate_retrieval, pin_vector_gate_key_permutation]

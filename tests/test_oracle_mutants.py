@@ -19,9 +19,9 @@ import oracle_pins as P  # noqa: E402
 MUTANTS = {
     "delta_sign": [("be * (vt[r] - p)", "be * (vt[r] + p)")],
     "beta_dropped": [(": be * (vt[r] - p)", ": (vt[r] - p)")],
-    "gate_after_predict": [("row[c] *= a; p += row[c] * kt[c];", "p += row[c] * kt[c]; row[c] *= a;")],
-    "gate_after_write": [("row[c] *= a; p += row[c] * kt[c];", "p += row[c] * kt[c];"),
-                         ("row[c] += e * kt[c];", "row[c] = a * (row[c] + e * kt[c]);")],
+    "gate_after_predict": [("row[c] *= ga[c]; p += row[c] * kt[c];", "p += row[c] * kt[c]; row[c] *= ga[c];")],
+    "gate_after_write": [("row[c] *= ga[c]; p += row[c] * kt[c];", "p += row[c] * kt[c];"),
+                         ("row[c] += e * kt[c];", "row[c] = ga[c] * (row[c] + e * kt[c]);")],
     "gate_ignored": [("exp(j->log_alpha[x])", "1.0")],
     "gate_squared": [("exp(j->log_alpha[x])", "exp(2.0 * j->log_alpha[x])")],
     "write_dropped": [("const double e = j->no_erase", "const double e = 0.0 * (j->no_erase"),
@@ -31,6 +31,11 @@ MUTANTS = {
     "read_transposed_state": [("o += row[c] * qt[c];", "o += S[(c % Dv) * Dk + (r % Dk)] * qt[c];")],
     "initial_state_ignored": [("if (j->S0) memcpy", "if (0) memcpy")],
     "sequence_end_off_by_one": [("t1 = j->cu[n + 1]; }", "t1 = j->cu[n + 1] - (j->cu[n + 1] > j->cu[n]); }")],
+    # per-channel gate
+    "vector_gate_ignored": [("ga[c] = exp(j->log_alpha[x * Dk + c]);", "ga[c] = 1.0;")],
+    "vector_gate_channels_reversed": [("exp(j->log_alpha[x * Dk + c])", "exp(j->log_alpha[x * Dk + (Dk - 1 - c)])")],
+    "vector_gate_on_value_side": [("row[c] *= ga[c];", "row[c] *= ga[r % Dk];")],
+    "vector_gate_first_channel_only": [("exp(j->log_alpha[x * Dk + c])", "exp(j->log_alpha[x * Dk])")],
 }
 
 
