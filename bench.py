@@ -19,7 +19,9 @@ resident in HBM.  Prints ONE JSON line.
 Options: --gpus (only 1), --steps, --warmup, --workload, --no-flush,
 --profile-steps, --cpu-sample (heads per batch row the oracle runs on, 0 = skip),
 --rule (delta: gdn_chunk_fwd, the default; mamba2: gdn_mamba2_chunk_fwd, the
-scalar-gated rule without the erase term, on the same workload),
+scalar-gated rule without the erase term; gla: gdn_gla_chunk_fwd, one gate per
+key channel and no erase term, the gate drawn per channel; each on the same
+workload shape),
 --recurrent N (instead: the single-token step, gdn_recurrent_step, over a decode
 batch of N sequences with the workload's H, Dk, Dv and dtype; its own JSON line).
 """
@@ -55,7 +57,9 @@ def per_kernel_work(B, T, H, Dk, Dv, C, s_in, n_seqs, has_s0, gated, rule="delta
     The no-erase rule (mamba2) has no prediction and no inverse: its path is
     4 Dk Dv + 2C (Dk + Dv) per token-head (Q S^T, the state update, Q K^T, P V),
     and its per-chunk kernel ("prep" here: the gates kernel) reads only the
-    gates."""
+    gates.  The per-channel rule (gla) has the same flops; its gate is Dk fp32
+    values per token-head, and its per-chunk kernel (the GLA prep) reads q, k
+    and the gates and forms Q K^T."""
     th = B * T * H                      # token-heads
     gate_b = 4 + (4 if gated else 0)    # beta (+ log alpha), fp32
     state_b = n_seqs * H * Dv * Dk * 4 * (2 if has_s0 else 1)
@@ -68,6 +72,13 @@ def per_kernel_work(B, T, H, Dk, Dv, C, s_in, n_seqs, has_s0, gated, rule="delta
     if rule == "mamba2":
         prep_b, prep_f = th * gate_b, th * 8
         scan_f = th * (4 * Dk * Dv + 2 * C * (Dk + Dv))
+        path_f = scan_f + prep_f
+    elif rule == "gla":
+        gate_b = 4 + (4 * Dk if gated else 0)
+        path_b = th * ((2 * Dk + 2 * Dv) * s_in + gate_b) + state_b
+        prep_b = th * (2 * Dk * s_in + gate_b)
+        prep_f = th * (2 * C * Dk + 4 * Dk)
+        scan_f = th * (4 * Dk * Dv + 2 * C * Dv)
         path_f = scan_f + prep_f
     return {"prep": (prep_b, prep_f), "scan": (scan_b, scan_f), "path": (path_b, path_f)}
 
@@ -233,8 +244,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="after timing, copy an MB-megabyte buffer a few times (a plain copy "
                          "kernel of known traffic, the scale for hardware byte counters)")
-    ap.add_argument("--rule", choices=["delta", "mamba2"], default="delta",
-                    help="update rule: delta (gdn_chunk_fwd) or mamba2 (gdn_mamba2_chunk_fwd)")
+    ap.add_argument("--rule", choices=["delta", "mamba2", "gla"], default="delta",
+                    help="update rule: delta (gdn_chunk_fwd), mamba2 (gdn_mamba2_chunk_fwd) "
+                         "or gla (gdn_gla_chunk_fwd)")
     ap.add_argument("--recurrent", type=int, default=0, metavar="N",
                     help="time gdn_recurrent_step over N sequences instead (one token each)")
     args = ap.parse_args()
@@ -253,7 +265,7 @@ def main():
     if args.recurrent > 0:
         bench_recurrent(args, w)
         return
-    inp = workload_inputs(args.workload)
+    inp = workload_inputs(args.workload, gate_channels=args.rule == "gla")
     dev = torch.device("cuda:0")
     d = inp.to(dev)
     B, T, H = inp.q.shape[:3]
@@ -261,8 +273,10 @@ def main():
     tdt = inp.q.dtype
     O = torch.empty(B, T, H, w.Dv, device=dev, dtype=tdt)
     S_T = torch.empty(N, H, w.Dv, w.Dk, device=dev, dtype=torch.float32)
-    rule = {"delta": gdn.GDN_RULE_DELTA, "mamba2": gdn.GDN_RULE_MAMBA2}[args.rule]
-    fwd = gdn.gdn_chunk_fwd if args.rule == "delta" else gdn.gdn_mamba2_chunk_fwd
+    rule = {"delta": gdn.GDN_RULE_DELTA, "mamba2": gdn.GDN_RULE_MAMBA2,
+            "gla": gdn.GDN_RULE_GLA}[args.rule]
+    fwd = {"delta": gdn.gdn_chunk_fwd, "mamba2": gdn.gdn_mamba2_chunk_fwd,
+           "gla": gdn.gdn_gla_chunk_fwd}[args.rule]
     n_ws = gdn.gdn_rule_workspace_bytes(rule, B, T, H, w.Dk, w.Dv, w.C,
                                         0 if inp.cu_seqlens is None else N, tdt)
     ws = torch.empty(n_ws, device=dev, dtype=torch.uint8)
@@ -345,12 +359,14 @@ def main():
 
     cpu = None
     if args.cpu_sample > 0:
-        cpu = cpu_baseline(inp, args.cpu_sample, no_erase=args.rule == "mamba2")
+        cpu = cpu_baseline(inp, args.cpu_sample, no_erase=args.rule != "delta")
 
     headline = args.workload == ap.get_default("workload") and args.rule == "delta"
     metric = METRIC if headline else f"tokens/sec gated-DeltaNet chunk fwd ({args.workload})"
     if args.rule == "mamba2":
         metric = f"tokens/sec Mamba2 (scalar gate, no erase) chunk fwd ({args.workload})"
+    elif args.rule == "gla":
+        metric = f"tokens/sec GLA (per-channel gate, no erase) chunk fwd ({args.workload})"
     out = {
         "metric": metric,
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

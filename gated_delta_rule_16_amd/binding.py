@@ -8,8 +8,8 @@ or a tensor is not on a ROCm device, the call raises.
 The Python functions carry the C names:
   gdn_chunk_fwd, gdn_chunk_fwd_profiled, gdn_chunk_fwd_noalloc, gdn_recurrent_step,
   gdn_chunk_fwd_workspace_bytes, gdn_chunk_fwd_supported, gdn_status_string,
-  gdn_mamba2_chunk_fwd, gdn_rule_chunk_fwd_profiled, gdn_rule_workspace_bytes,
-  gdn_rule_supported.
+  gdn_mamba2_chunk_fwd, gdn_gla_chunk_fwd, gdn_rule_chunk_fwd_profiled,
+  gdn_rule_workspace_bytes, gdn_rule_supported.
 """
 from __future__ import annotations
 
@@ -26,6 +26,7 @@ GDN_F32 = 0
 GDN_BF16 = 1
 GDN_RULE_DELTA = 0
 GDN_RULE_MAMBA2 = 1
+GDN_RULE_GLA = 2
 _DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
 
 _lib = None
@@ -61,6 +62,8 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_chunk_fwd_noalloc.restype = I
     lib.gdn_mamba2_chunk_fwd.argtypes = lib.gdn_chunk_fwd.argtypes
     lib.gdn_mamba2_chunk_fwd.restype = I
+    lib.gdn_gla_chunk_fwd.argtypes = lib.gdn_chunk_fwd.argtypes
+    lib.gdn_gla_chunk_fwd.restype = I
     lib.gdn_rule_chunk_fwd_profiled.argtypes = [I] + lib.gdn_chunk_fwd.argtypes + [P]
     lib.gdn_rule_chunk_fwd_profiled.restype = I
     lib.gdn_rule_supported.argtypes = [I, I, I, I, I]
@@ -130,9 +133,11 @@ def _chunk_fwd(profiled: bool, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_s
         raise ValueError(f"unsupported dtype {dt}")
     n_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     N = B if cu_seqlens is None else n_seqs
-    for name, t in (("beta", beta), ("log_alpha", log_alpha)):
-        if t is not None and t.shape != (B, T, H):
-            raise ValueError(f"{name} must be [B,T,H]")
+    if beta is not None and beta.shape != (B, T, H):
+        raise ValueError("beta must be [B,T,H]")
+    la_shape = (B, T, H, Dk) if rule == GDN_RULE_GLA else (B, T, H)
+    if log_alpha is not None and log_alpha.shape != la_shape:
+        raise ValueError(f"log_alpha must be {list(la_shape)}")
     if S0 is not None and S0.shape != (N, H, Dv, Dk):
         raise ValueError("S0 must be [N,H,Dv,Dk]")
     if O is None:
@@ -157,7 +162,8 @@ def _chunk_fwd(profiled: bool, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_s
             raise GdnError(rc, "gdn_rule_chunk_fwd_profiled")
         return O, S_T, [float(x) for x in ms]
     fn, name = {GDN_RULE_DELTA: (lib.gdn_chunk_fwd, "gdn_chunk_fwd"),
-                GDN_RULE_MAMBA2: (lib.gdn_mamba2_chunk_fwd, "gdn_mamba2_chunk_fwd")}[rule]
+                GDN_RULE_MAMBA2: (lib.gdn_mamba2_chunk_fwd, "gdn_mamba2_chunk_fwd"),
+                GDN_RULE_GLA: (lib.gdn_gla_chunk_fwd, "gdn_gla_chunk_fwd")}[rule]
     rc = fn(*args)
     if rc != 0:
         raise GdnError(rc, name)
@@ -208,11 +214,29 @@ def gdn_mamba2_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                       output_final_state, workspace, stream, rule=GDN_RULE_MAMBA2)
 
 
+def gdn_gla_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      log_alpha: Optional[torch.Tensor], beta: Optional[torch.Tensor],
+                      S0: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None, *, chunk_size: int = 64,
+                      O: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+                      output_final_state: bool = True,
+                      workspace: Optional[torch.Tensor] = None,
+                      stream: Optional[torch.cuda.Stream] = None
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked forward of S_t = S_{t-1} diag(alpha_t) + beta_t v_t k_t^T,
+    o_t = S_t q_t with one gate per key channel (include/gdn.h,
+    gdn_gla_chunk_fwd).  log_alpha [B,T,H,Dk] (each <= 0) or None; beta
+    [B,T,H] or None (beta = 1); the rest as gdn_chunk_fwd."""
+    return _chunk_fwd(False, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
+                      output_final_state, workspace, stream, rule=GDN_RULE_GLA)
+
+
 def gdn_rule_chunk_fwd_profiled(rule: int, q, k, v, log_alpha, beta, S0=None, cu_seqlens=None,
                                 *, chunk_size: int = 64, O=None, S_T=None,
                                 output_final_state=True, workspace=None, stream=None):
-    """The forward of ``rule`` (GDN_RULE_DELTA or GDN_RULE_MAMBA2), also returning
-    each kernel's device milliseconds [table, prep or gates, scan, unused]."""
+    """The forward of ``rule`` (GDN_RULE_DELTA, GDN_RULE_MAMBA2 or GDN_RULE_GLA),
+    also returning each kernel's device milliseconds [table, per-chunk
+    preparation, scan, unused]."""
     return _chunk_fwd(True, q, k, v, log_alpha, beta, S0, cu_seqlens, chunk_size, O, S_T,
                       output_final_state, workspace, stream, rule=rule)
 

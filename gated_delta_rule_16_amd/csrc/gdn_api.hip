@@ -7,6 +7,8 @@
 //   scan  (Dv slice, head, sequence)    O, S_T                 (serial over chunks)
 // gdn_mamba2_chunk_fwd (the no-erase rule) replaces prep by the gates kernel
 // (g and beta per chunk) and runs the same scan without the prediction step.
+// gdn_gla_chunk_fwd (per-channel gate) replaces it by the GLA prep kernel
+// (Q~, K^, P~ and the chunk decay per chunk) and runs the scan on those.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -16,6 +18,7 @@
 
 #include "../../include/gdn.h"
 #include "gdn_device.h"
+#include "gdn_gla_prep.h"
 #include "gdn_prep.h"
 #include "gdn_scan_cols.h"
 #include "gdn_step.h"
@@ -59,7 +62,7 @@ struct FwdArgs {
 // Workspace regions, in order; every region starts on a 256-byte boundary.
 struct Layout {
     int64_t slots, N;
-    size_t g, Tb, bounds, seq_slot, table, total;
+    size_t g, Tb, qt, kh, bounds, seq_slot, table, total;
 };
 
 Layout make_layout(int rule, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C,
@@ -71,10 +74,14 @@ Layout make_layout(int rule, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
     const size_t u = (size_t)(L.slots * H);
-    // g, exp(g), exp(g_n - g) (and beta for kNoErase) per chunk
-    L.g = take(u * gate_rows(rule) * C * sizeof(float));
-    // Tb blocks per chunk (delta rule only)
-    L.Tb = take(rule == kDelta ? u * (size_t)tb_blocks((int)C, es == 2) * 1024 : 0);
+    // g, exp(g), exp(g_n - g) (and beta for kNoErase) per chunk; kGla: e^{b_n}
+    L.g = take(u * gate_floats(rule, (int)C, (int)Dk) * sizeof(float));
+    // Tb (delta rule) or P~ (kGla) blocks per chunk
+    L.Tb = take(rule != kNoErase ? u * (size_t)tb_blocks((int)C, es == 2) * 1024 : 0);
+    // kGla: Q~ and K^, token-major like q and k
+    const size_t tok = (size_t)(varlen ? T : B * T) * H * Dk * es;
+    L.qt = take(rule == kGla ? tok : 0);
+    L.kh = take(rule == kGla ? tok : 0);
     if (varlen) {
         L.bounds = take((size_t)(n_seqs + 1) * sizeof(int));
         L.seq_slot = take((size_t)(n_seqs + 1) * sizeof(int));
@@ -174,17 +181,41 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     const T* q = static_cast<const T*>(a.q);
     const T* k = static_cast<const T*>(a.k);
     const T* v = static_cast<const T*>(a.v);
+    if constexpr (RULE == kGla) {
+        using P = GlaPrepCfg<T, DK, C>;
+        constexpr auto kp = gdn_gla_prep_kernel<T, DK, C>;
+        allow_smem<kp>(P::SMEM);
+        const int64_t units = L.slots * a.H;
+        T* qt = reinterpret_cast<T*>(a.ws + L.qt);
+        T* kh = reinterpret_cast<T*>(a.ws + L.kh);
+        // persistent: as many workgroups as are resident at once, each walking
+        // units with a stride of the grid
+        const int64_t resident = (int64_t)device_cu_count() * resident_per_cu<kp>(P::THREADS, P::SMEM);
+        const unsigned grid = (unsigned)(units < resident ? units : resident);
+        tm->mark(a.stream);
+        if (units > 0) {
+            hipLaunchKernelGGL(kp, dim3(grid), dim3(P::THREADS), P::SMEM, a.stream, q, k,
+                               a.log_alpha, a.beta, geom, a.H, (int)units, g_ws, Tb_ws, qt, kh);
+            if (gdn_status s = check_launch(a.stream)) return s;
+        }
+        tm->mark(a.stream);
+        // the scan runs on the decayed operands
+        q = qt;
+        k = kh;
+    }
 
-    if (RULE == kNoErase && L.slots > 0) {
+    if constexpr (RULE == kNoErase) {
         constexpr int WPB = kThreads / 64;
         const int64_t units = L.slots * a.H;
         tm->mark(a.stream);
-        hipLaunchKernelGGL(gdn_gates_kernel<C>, dim3((unsigned)((units + WPB - 1) / WPB)), dim3(kThreads), 0,
-                           a.stream, a.log_alpha, a.beta, geom, a.H, (int)units, g_ws);
-        if (gdn_status s = check_launch(a.stream)) return s;
+        if (units > 0) {
+            hipLaunchKernelGGL(gdn_gates_kernel<C>, dim3((unsigned)((units + WPB - 1) / WPB)), dim3(kThreads), 0,
+                               a.stream, a.log_alpha, a.beta, geom, a.H, (int)units, g_ws);
+            if (gdn_status s = check_launch(a.stream)) return s;
+        }
         tm->mark(a.stream);
     }
-    if (RULE == kDelta && L.slots > 0) {
+    if constexpr (RULE == kDelta) if (L.slots > 0) {
         using P = PrepCfg<T, DK, C>;
         constexpr auto kp = gdn_prep_kernel<T, DK, C>;
         allow_smem<kp>(P::SMEM);
@@ -254,8 +285,18 @@ const Variant kVariantsNoErase[] = {
     {128, 128, 64, GDN_BF16, launch_fwd<bf16, 128, 128, 64, kNoErase>},
     {128, 256, 64, GDN_BF16, launch_fwd<bf16, 128, 256, 64, kNoErase>},
 };
+const Variant kVariantsGla[] = {
+    {16, 16, 16, GDN_F32, launch_fwd<float, 16, 16, 16, kGla>},
+    {64, 64, 64, GDN_F32, launch_fwd<float, 64, 64, 64, kGla>},
+    {128, 128, 64, GDN_BF16, launch_fwd<bf16, 128, 128, 64, kGla>},
+    {128, 256, 64, GDN_BF16, launch_fwd<bf16, 128, 256, 64, kGla>},
+};
+static_assert(GDN_RULE_DELTA == kDelta && GDN_RULE_MAMBA2 == kNoErase && GDN_RULE_GLA == kGla,
+              "rule numbering");
 
-bool valid_rule(int rule) { return rule == GDN_RULE_DELTA || rule == GDN_RULE_MAMBA2; }
+bool valid_rule(int rule) {
+    return rule == GDN_RULE_DELTA || rule == GDN_RULE_MAMBA2 || rule == GDN_RULE_GLA;
+}
 
 const Variant* find_variant(int rule, int dk, int dv, int c, gdn_dtype dt) {
     auto scan = [&](const Variant* b, const Variant* e) -> const Variant* {
@@ -265,6 +306,7 @@ const Variant* find_variant(int rule, int dk, int dv, int c, gdn_dtype dt) {
     };
     if (rule == GDN_RULE_DELTA) return scan(std::begin(kVariants), std::end(kVariants));
     if (rule == GDN_RULE_MAMBA2) return scan(std::begin(kVariantsNoErase), std::end(kVariantsNoErase));
+    if (rule == GDN_RULE_GLA) return scan(std::begin(kVariantsGla), std::end(kVariantsGla));
     return nullptr;
 }
 
@@ -289,6 +331,8 @@ gdn_status check_sizes(int rule, int B, int T, int H, int Dk, int Dv, int C, boo
     if (N * H * (int64_t)Dv * Dk > kMaxElems) return GDN_ERR_SHAPE;
     // the scan addresses one chunk of one token tensor with 31-bit byte offsets
     if ((int64_t)C * H * dmax * elem_size(dt) > kMaxElems) return GDN_ERR_SHAPE;
+    // ... and the GLA prep one chunk of the per-channel gate (fp32, Dk per token)
+    if (rule == GDN_RULE_GLA && (int64_t)C * H * Dk * 4 > kMaxElems) return GDN_ERR_SHAPE;
     if (!find_variant(rule, Dk, Dv, C, dt)) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
@@ -360,7 +404,7 @@ gdn_status chunk_fwd_impl(int rule, const void* q, const void* k, const void* v,
                           KernelTimer* tm) {
     const bool varlen = cu_seqlens != nullptr;
     // with no tokens the token tensors are never read (empty tensors may be
-    // NULL); beta may be NULL (beta = 1) for the no-erase rule only
+    // NULL); beta may be NULL (beta = 1) for the no-erase rules only
     const bool has_tokens = T > 0;
     if (has_tokens && (!q || !k || !v || (!beta && rule == GDN_RULE_DELTA) || !O)) return GDN_ERR_NULL;
     if (gdn_status s = check_sizes(rule, B, T, H, Dk, Dv, C, varlen, n_seqs, dt)) return s;
@@ -426,6 +470,21 @@ extern "C" gdn_status gdn_mamba2_chunk_fwd(const void* q, const void* k, const v
         KernelTimer off;
         return chunk_fwd_impl(GDN_RULE_MAMBA2, q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs,
                               O, S_T, B, T, H, Dk, Dv, C, dt, workspace, workspace_bytes, false,
+                              stream, &off);
+    } catch (...) {
+        return GDN_ERR_INTERNAL;
+    }
+}
+
+extern "C" gdn_status gdn_gla_chunk_fwd(const void* q, const void* k, const void* v,
+                                        const float* log_alpha, const float* beta, const float* S0,
+                                        const int32_t* cu_seqlens, int n_seqs, void* O, float* S_T,
+                                        int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        KernelTimer off;
+        return chunk_fwd_impl(GDN_RULE_GLA, q, k, v, log_alpha, beta, S0, cu_seqlens, n_seqs, O,
+                              S_T, B, T, H, Dk, Dv, C, dt, workspace, workspace_bytes, false,
                               stream, &off);
     } catch (...) {
         return GDN_ERR_INTERNAL;

@@ -29,10 +29,14 @@ constexpr int kThreads = 256;   // 4 waves per workgroup (prep)
 // Update rules the chunk kernels evaluate (the C ABI's gdn_rule values):
 //  kDelta    S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
 //  kNoErase  S_t = alpha_t S_{t-1} + beta_t v_t k_t^T   (Mamba2 with a write strength)
-enum : int { kDelta = 0, kNoErase = 1 };
+//  kGla      S_t = S_{t-1} diag(alpha_t) + beta_t v_t k_t^T   (per-channel gate)
+enum : int { kDelta = 0, kNoErase = 1, kGla = 2 };
 // fp32 rows per chunk of the gate values handed to the scan: g, exp(g),
 // exp(g_n - g), and for kNoErase beta as a fourth row
 constexpr int gate_rows(int rule) { return rule == kDelta ? 3 : 4; }
+// fp32 gate values per chunk handed to the scan: the rows above, or for kGla
+// the decay of the whole chunk per key channel, exp(b_n) (Dk values)
+constexpr int gate_floats(int rule, int C, int DK) { return rule == kGla ? DK : gate_rows(rule) * C; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // wave index, known to the compiler to be uniform across the wave

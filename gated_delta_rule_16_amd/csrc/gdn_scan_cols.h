@@ -14,6 +14,18 @@
 // Computation" section): there is no prediction to remove, so Y and Tb drop
 // out and V' = diag(beta) V; the output and the state update are unchanged.
 //
+// Rule kGla (per-channel gate, S_t = S_{t-1} diag(alpha_t) + beta_t v_t k_t^T;
+// LinearAttention系列解读(六), section 1: the diagonal transition is split onto
+// both sides of the mask): the GLA prep kernel hands over the chunk with its
+// decays folded in, and the same pipeline runs on those operands:
+//   Q -> Q~ = Q o e^b,  K -> K^ = diag(beta) K o e^(b_n - b),
+//   Tb slot -> P~ = ((Q o e^b)(K o e^-b)^T o M) diag(beta)  (formed there with
+//              bounded exponents), gates -> e^(b_n) per key channel,
+// with b_i the in-chunk cumulative log-gate of each channel, so that
+//   O^T = S Q~^T + V^T P~^T,   S^T <- diag(e^(b_n)) S^T + K^^T V.
+// The column waves scale each state row by its channel's decay and take
+// V' = V; the output helpers read P~ instead of forming P.
+//
 // Work split.  A workgroup owns a DVT-column slice of one (sequence, head):
 //  - column waves (DVT / 16): wave vb holds all Dk rows of columns vb*16 ..
 //    vb*16 + 15 of S^T in MFMA accumulators and runs the recurrence alone --
@@ -50,7 +62,9 @@ template <typename T, int DK, int DV, int C, int DVT, int RULE = kDelta>
 struct ColCfg {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr bool ERASE = RULE == kDelta;          // delta rule: Y, X and Tb
-    static constexpr int NGR = gate_rows(RULE);            // fp32 gate rows per chunk
+    static constexpr bool GLA = RULE == kGla;              // per-channel gate: P~ handed in
+    static constexpr bool HAS_TB = RULE != kNoErase;       // Tb (delta) or P~ (GLA) staged
+    static constexpr int GF = gate_floats(RULE, C, DK);    // fp32 gate values per chunk
     static constexpr int ES = sizeof(T);
     static constexpr int NW = C / 16;                      // 16-token blocks of a chunk
     static constexpr int NVW = DVT / 16;                   // column waves
@@ -77,7 +91,7 @@ struct ColCfg {
     static constexpr int blocks(int bytes) { return (bytes + 1023) / 1024; }
     static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
     static constexpr int NIK = blocks(C * LDK * ES), NIV = blocks(C * LDV * ES);
-    static constexpr int NIT = ERASE ? tb_blocks(C, BF) : 0, NIG = blocks(NGR * C * 4);
+    static constexpr int NIT = HAS_TB ? tb_blocks(C, BF) : 0, NIG = blocks(GF * 4);
     static constexpr int BT = NIK, BV = BT + NIT, BG = BV + NIV, NI = BG + NIG;
     static constexpr int NL = cdiv(NI, NLD);               // loads per loading lane per chunk
     // loads loading wave f issues per chunk
@@ -175,7 +189,7 @@ __device__ __forceinline__ uint32_t col_stage_offset(int j, int f, int l, int64_
         case 3: off = region((i - Cfg::BV) * 64 + l, Cfg::VP, Cfg::VB, Cfg::VSW, rs_v); break;
         case 4: {
             const int s = (i - Cfg::BG) * 64 + l;
-            off = s < Cfg::NGR * C / 4 ? (int64_t)s * 16 : -1;
+            off = s < Cfg::GF / 4 ? (int64_t)s * 16 : -1;
             break;
         }
         default: break;
@@ -319,7 +333,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             float4 dec4[NW];
             f32x4 vv[NW], Vp[NW];
             Op kt[NDB][NW];   // K^T operands of the state update
-            const float gamma_n = st.gam[C - 1];
+            const float gamma_n = Cfg::GLA ? 1.f : st.gam[C - 1];
             if constexpr (Cfg::ERASE) {
                 Frag fk[KPF][NW];
 #pragma unroll
@@ -384,6 +398,18 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                     }
                     Vp[ib] = acc;
                 }
+            } else if constexpr (Cfg::GLA) {
+                // the decays and beta are in K^: V' = V
+#pragma unroll
+                for (int i = 0; i < NDB; ++i)
+#pragma unroll
+                    for (int kb = 0; kb < NW; ++kb) kt[i][kb] = kT_tile<Cfg>(st.K, kb, i);
+#pragma unroll
+                for (int tb = 0; tb < NW; ++tb) {
+                    dec4[tb] = float4{1.f, 1.f, 1.f, 1.f};
+                    vv[tb] = vcol4<Cfg>(st.V, tb, vb);
+                    Vp[tb] = vv[tb];
+                }
             } else {
                 // no prediction to remove: V' = diag(beta) V
 #pragma unroll
@@ -398,9 +424,17 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                     Vp[tb] = f32x4{vv[tb][0] * b4.x, vv[tb][1] * b4.y, vv[tb][2] * b4.z, vv[tb][3] * b4.w};
                 }
             }
-            // gamma_n S^T while V' completes
+            // gamma_n S^T while V' completes (kGla: e^(b_n) of each row's key channel)
+            if constexpr (Cfg::GLA) {
 #pragma unroll
-            for (int i = 0; i < NDB; ++i) St[i] *= gamma_n;
+                for (int i = 0; i < NDB; ++i) {
+                    const float4 e4 = *reinterpret_cast<const float4*>(st.g + drow<Cfg>(i, g4));
+                    St[i] = f32x4{St[i][0] * e4.x, St[i][1] * e4.y, St[i][2] * e4.z, St[i][3] * e4.w};
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NDB; ++i) St[i] *= gamma_n;
+            }
             // S^T <- gamma_n S^T + K^T diag(gamma_n / gamma) V'
             Op Vd[NW];
 #pragma unroll
@@ -497,8 +531,10 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             Frag kf[2][NW], qf[2][Cfg::NQB];
             Op sbk[2][NVW][2];
             auto fetch = [&](int kk, int s) __attribute__((always_inline)) {
+                if constexpr (!Cfg::GLA) {   // kGla: P~ arrives formed
 #pragma unroll
-                for (int jb = 0; jb <= QMAX; ++jb) kf[s][jb] = kfrag_rows<Cfg>(st.K, jb * 16, kk * KS);
+                    for (int jb = 0; jb <= QMAX; ++jb) kf[s][jb] = kfrag_rows<Cfg>(st.K, jb * 16, kk * KS);
+                }
 #pragma unroll
                 for (int j = 0; j < NM; ++j)
                     qf[s][j] = Cfg::QLDS ? kfrag_rows<Cfg>(sQ, Cfg::mine(hw, j) * 16, kk * KS) : qcur[j][kk];
@@ -521,8 +557,8 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             float gq[Cfg::NQB], gamq[Cfg::NQB];
 #pragma unroll
             for (int j = 0; j < NM; ++j) {
-                gq[j] = st.g[Cfg::mine(hw, j) * 16 + n];
-                gamq[j] = st.gam[Cfg::mine(hw, j) * 16 + n];
+                gq[j] = Cfg::GLA ? 0.f : st.g[Cfg::mine(hw, j) * 16 + n];
+                gamq[j] = Cfg::GLA ? 1.f : st.gam[Cfg::mine(hw, j) * 16 + n];
             }
             // decay factors of the P^T tiles of key block jb (zero above the
             // diagonal), formed between the instructions of a contraction step
@@ -556,8 +592,10 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
 #pragma unroll
                 for (int j = 0; j < NM; ++j) {
                     const int qb = Cfg::mine(hw, j);
+                    if constexpr (!Cfg::GLA) {
 #pragma unroll
-                    for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] = St16::mma(kf[s][jb], qf[s][j], Pt[j][jb]);
+                        for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] = St16::mma(kf[s][jb], qf[s][j], Pt[j][jb]);
+                    }
 #pragma unroll
                     for (int vb = 0; vb < NVW; ++vb) {
                         if constexpr (Cfg::BF) {
@@ -569,11 +607,13 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                         }
                     }
                 }
+                if constexpr (!Cfg::GLA) {
 #pragma unroll
-                for (int jb = kk; jb < NW; jb += NKK) decay(jb);
-                if (kk == NKK - 1) {
+                    for (int jb = kk; jb < NW; jb += NKK) decay(jb);
+                    if (kk == NKK - 1) {
 #pragma unroll
-                    for (int jb = NKK; jb < NW; ++jb) decay(jb);
+                        for (int jb = NKK; jb < NW; ++jb) decay(jb);
+                    }
                 }
                 if (kk == 0 && cc > 0) out(cc - 1, vo);
                 __builtin_amdgcn_sched_barrier(0);
@@ -584,18 +624,27 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 const int qb = Cfg::mine(hw, j);
 #pragma unroll
                 for (int vb = 0; vb < NVW; ++vb) zp[j][vb] = Zt[j][vb] * gamq[j];
+                if constexpr (Cfg::GLA) {
+                    // P~ of this query block from the staged operand blocks
+                    const unsigned char* pb = reinterpret_cast<const unsigned char*>(st.Tb) + l * 16;
 #pragma unroll
-                for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] *= dfac[j][jb];
-                if constexpr (Cfg::BF) {
-#pragma unroll
-                    for (int p = 0; p < NP; ++p)
-                        if (2 * p <= qb)
-                            pp[j][p] = __builtin_shufflevector(KO::tile(Pt[j][2 * p]),
-                                                               KO::tile(2 * p + 1 < NW ? Pt[j][2 * p + 1] : zero4()),
-                                                               0, 1, 2, 3, 4, 5, 6, 7);
+                    for (int p = 0; p < NPQ; ++p)
+                        if ((Cfg::BF ? 2 * p : p) <= qb)
+                            pp[j][p] = *reinterpret_cast<const PFrag*>(pb + tb_block(qb, p, Cfg::BF) * 1024);
                 } else {
 #pragma unroll
-                    for (int jb = 0; jb <= qb; ++jb) pp[j][jb] = Pt[j][jb];
+                    for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] *= dfac[j][jb];
+                    if constexpr (Cfg::BF) {
+#pragma unroll
+                        for (int p = 0; p < NP; ++p)
+                            if (2 * p <= qb)
+                                pp[j][p] = __builtin_shufflevector(KO::tile(Pt[j][2 * p]),
+                                                                   KO::tile(2 * p + 1 < NW ? Pt[j][2 * p + 1] : zero4()),
+                                                                   0, 1, 2, 3, 4, 5, 6, 7);
+                    } else {
+#pragma unroll
+                        for (int jb = 0; jb <= qb; ++jb) pp[j][jb] = Pt[j][jb];
+                    }
                 }
             }
             if constexpr (!Cfg::QLDS) q_load(qcur, min(cc + Cfg::NQS, count - 1));   // refill the set just used
@@ -652,7 +701,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             const T* kb = k + ((int64_t)t0 * H + h) * DK;
             const T* vb_ = v + ((int64_t)t0 * H + h) * DV + v0;
             const T* tb = Tb_ws + unit * (Cfg::NIT * 1024 / ES);
-            const float* gb = g_ws + unit * Cfg::NGR * C;
+            const float* gb = g_ws + unit * Cfg::GF;
             const int nk = (int)((len - 1) * rs_k + DK * ES), nv = (int)((len - 1) * rs_v + DVT * ES);
             unsigned char* dst = smem + (cd % Cfg::NSTG) * Cfg::SZ_STAGE + f * 1024;
 #pragma unroll
@@ -661,7 +710,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 if (r == 5) continue;
                 const void* base = r == 0 ? (const void*)kb : r == 2 ? (const void*)tb : r == 3 ? (const void*)vb_
                                  : (const void*)gb;
-                const int nrec = r == 0 ? nk : r == 2 ? Cfg::NIT * 1024 : r == 3 ? nv : Cfg::NGR * C * 4;
+                const int nrec = r == 0 ? nk : r == 2 ? Cfg::NIT * 1024 : r == 3 ? nv : Cfg::GF * 4;
                 lds_load16(make_rsrc(base, nrec), dst + j * Cfg::NLD * 1024, soff[j]);
             }
         };

@@ -10,7 +10,8 @@ Value distributions follow the workloads the library is measured on:
   * v ~ N(0, 1), rounded to the storage dtype;
   * beta = sigmoid(N(0, 1)) in fp32, per (token, head);
   * log_alpha = -softplus(N(-3, 1)) in fp32, per (token, head); absent for
-    DeltaNet (alpha = 1);
+    DeltaNet (alpha = 1); with ``gate_channels`` one such value per key
+    channel, [B, T, H, Dk] (the per-channel gate), drawn in the same place;
   * S0 ~ N(0, 0.1^2) in fp32, shape [N, H, Dv, Dk], or absent (zero state).
 Draw order is fixed: [sequence lengths], q, k, v, beta logits, alpha logits,
 S0.  All draws use a CPU ``torch.Generator`` so that a seed gives the same
@@ -74,7 +75,7 @@ class GdnInputs:
     k: torch.Tensor
     v: torch.Tensor
     beta: torch.Tensor                      # [B, T, H] fp32
-    log_alpha: Optional[torch.Tensor]       # [B, T, H] fp32 or None
+    log_alpha: Optional[torch.Tensor]       # [B, T, H] (or [B, T, H, Dk]) fp32, or None
     S0: Optional[torch.Tensor]              # [N, H, Dv, Dk] fp32 or None
     cu_seqlens: Optional[torch.Tensor]      # [N+1] int32 or None
     C: int = 64
@@ -110,12 +111,14 @@ def _unit_norm(x: torch.Tensor) -> torch.Tensor:
 def make_inputs(B: int, T: int, H: int, Dk: int, Dv: int, *, dtype: str = "bf16",
                 gated: bool = True, s0: bool = True, seed: int = 0, C: int = 64,
                 lengths: Optional[list[int]] = None, normalize_qk: bool = True,
-                beta_fill: Optional[float] = None, device: str = "cpu") -> GdnInputs:
+                beta_fill: Optional[float] = None, gate_channels: bool = False,
+                device: str = "cpu") -> GdnInputs:
     """Draw one call's inputs.
 
     With ``lengths`` the batch is packed: B must be 1, T must equal
     sum(lengths), and ``cu_seqlens`` holds the prefix offsets.
     ``beta_fill`` replaces the drawn beta by a constant (special cases).
+    ``gate_channels`` draws log_alpha per key channel, [B, T, H, Dk].
     ``device`` draws the tensors there, from that device's generator (same
     distributions, other values than a CPU draw of the same seed): for inputs
     too large to draw on the host in reasonable time."""
@@ -149,14 +152,17 @@ def make_inputs(B: int, T: int, H: int, Dk: int, Dv: int, *, dtype: str = "bf16"
         beta = torch.full_like(beta, beta_fill)
     log_alpha = None
     if gated:
-        log_alpha = -torch.nn.functional.softplus(randn(B, T, H) - 3.0)
+        la_shape = (B, T, H, Dk) if gate_channels else (B, T, H)
+        log_alpha = -torch.nn.functional.softplus(randn(*la_shape) - 3.0)
     S0 = randn(N, H, Dv, Dk) * 0.1 if s0 else None
     return GdnInputs(q, k, v, beta.contiguous(), None if log_alpha is None else log_alpha.contiguous(),
                      S0, cu, C, {"dtype": dtype, "seed": seed})
 
 
-def workload_inputs(name: str, seed: Optional[int] = None) -> GdnInputs:
-    """Inputs of a named workload; ``seed`` overrides its default seed."""
+def workload_inputs(name: str, seed: Optional[int] = None, gate_channels: bool = False) -> GdnInputs:
+    """Inputs of a named workload; ``seed`` overrides its default seed;
+    ``gate_channels`` draws its gate per key channel instead (same shapes and
+    distributions otherwise)."""
     w = WORKLOADS[name]
     s = w.seed if seed is None else seed
     lengths = None
@@ -164,6 +170,6 @@ def workload_inputs(name: str, seed: Optional[int] = None) -> GdnInputs:
         lengths = draw_lengths(w.lengths_total, w.len_lo, w.len_hi,
                                torch.Generator().manual_seed(s))
     inp = make_inputs(w.B, w.T, w.H, w.Dk, w.Dv, dtype=w.dtype, gated=w.gated, s0=w.s0,
-                      seed=s, C=w.C, lengths=lengths)
+                      seed=s, C=w.C, lengths=lengths, gate_channels=gate_channels)
     inp.meta["workload"] = name
     return inp

@@ -60,7 +60,8 @@ typedef enum {
 /* The per-token update rule a chunked forward evaluates (see each entry point). */
 typedef enum {
     GDN_RULE_DELTA = 0,        /* gdn_chunk_fwd:        S = a S (I - b k k^T) + b v k^T */
-    GDN_RULE_MAMBA2 = 1        /* gdn_mamba2_chunk_fwd: S = a S + b v k^T */
+    GDN_RULE_MAMBA2 = 1,       /* gdn_mamba2_chunk_fwd: S = a S + b v k^T */
+    GDN_RULE_GLA = 2           /* gdn_gla_chunk_fwd:    S = S diag(a) + b v k^T, a per key channel */
 } gdn_rule;
 
 /* Compiled (Dk, Dv, C, dtype) instantiations:
@@ -70,8 +71,8 @@ typedef enum {
 int gdn_chunk_fwd_supported(int Dk, int Dv, int C, gdn_dtype dt);
 
 /* As gdn_chunk_fwd_supported, for the entry point of `rule`.  Compiled for
- * GDN_RULE_MAMBA2: (16, 16, 16, F32) (64, 64, 64, F32) (128, 128, 64, BF16)
- * (128, 256, 64, BF16).  0 for an unknown rule. */
+ * GDN_RULE_MAMBA2 and GDN_RULE_GLA: (16, 16, 16, F32) (64, 64, 64, F32)
+ * (128, 128, 64, BF16) (128, 256, 64, BF16).  0 for an unknown rule. */
 int gdn_rule_supported(gdn_rule rule, int Dk, int Dv, int C, gdn_dtype dt);
 
 /* As gdn_chunk_fwd_workspace_bytes, for the entry point of `rule`. */
@@ -193,10 +194,42 @@ gdn_status gdn_mamba2_chunk_fwd(const void *q, const void *k, const void *v,
                                 int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Chunked forward of the linear recurrence with a per-channel (vector) gate,
+ * without the erase term (vector-gated GLA with a write strength beta):
+ *     S_t = S_{t-1} diag(alpha_t) + beta_t v_t k_t^T,   o_t = S_t q_t
+ * where alpha_t = exp(log_alpha_t) holds one gate per key channel and scales
+ * column c of S = [Dv][Dk] (the channel of k and q it multiplies).
+ * Definition: LinearAttention系列解读(六)：DeltaNet的Chunkwise Form推导, section 1
+ * (引言): the vector-gated GLA's state transition is a diagonal matrix that
+ * scales each state element on its own, by an amount fixed by the gate, so in
+ * the chunk form that scaling is split onto both sides of the causal mask.
+ * The chunk form (derived from unrolling the update; the per-channel version
+ * of the Qiita article's "Chunk Computation", Mamba2 case): with b_i the
+ * in-chunk cumulative log-gate per channel,
+ *     O = (Q o e^b) S^T + P diag(beta) V,   P_is = sum_d q_id k_sd e^{b_id - b_sd} (s <= i)
+ *     S <- S diag(e^{b_n}) + V^T diag(beta) (K o e^{b_n - b}).
+ * Arguments, layouts, ownership, asynchrony and errors as gdn_chunk_fwd, except:
+ *  log_alpha  [B][T][H][Dk] fp32, one gate per key channel, each <= 0
+ *             (alpha in (0, 1]); NULL means alpha = 1;
+ *  beta       [B][T][H] fp32, or NULL for beta = 1;
+ *  workspace  at least gdn_rule_workspace_bytes(GDN_RULE_GLA, ...) bytes (it
+ *             holds decayed copies of q and k besides the per-chunk data);
+ *  supported sizes: gdn_rule_supported(GDN_RULE_GLA, ...); GDN_ERR_SHAPE also
+ *             when one chunk of log_alpha, C * H * Dk * 4 bytes, passes 2^31-1.
+ * Any gate in range is handled exactly (a chunk whose decay across 16 tokens
+ * passes e^64 on some channel takes a slower exact path for that block). */
+gdn_status gdn_gla_chunk_fwd(const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta, const float *S0,
+                             const int32_t *cu_seqlens, int n_seqs,
+                             void *O, float *S_T,
+                             int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 /* gdn_chunk_fwd_profiled for the entry point of `rule` (same arguments as
  * that entry point, then kernel_ms; kernel_ms[1] is the per-chunk preparation
  * of that rule: prep for GDN_RULE_DELTA, the gates kernel for
- * GDN_RULE_MAMBA2).  Blocks until the call's work has finished. */
+ * GDN_RULE_MAMBA2, the GLA prep kernel for GDN_RULE_GLA).  Blocks until the
+ * call's work has finished. */
 gdn_status gdn_rule_chunk_fwd_profiled(gdn_rule rule, const void *q, const void *k, const void *v,
                                        const float *log_alpha, const float *beta, const float *S0,
                                        const int32_t *cu_seqlens, int n_seqs,

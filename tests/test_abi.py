@@ -62,6 +62,12 @@ def test_rule_queries(lib):
         assert lib.gdn_rule_supported(RULE_MAMBA2, *a) == 1, a
         assert lib.gdn_rule_supported(RULE_DELTA, *a) == lib.gdn_chunk_fwd_supported(*a)
     assert lib.gdn_rule_supported(RULE_MAMBA2, 64, 64, 16, F32) == 0
+    RULE_GLA = 2
+    for a in [(128, 128, 64, BF16), (128, 256, 64, BF16), (64, 64, 64, F32), (16, 16, 16, F32)]:
+        assert lib.gdn_rule_supported(RULE_GLA, *a) == 1, a
+    # GLA: e^{b_n} per key channel, P~ blocks, and decayed copies of q and k
+    g = lib.gdn_rule_workspace_bytes(RULE_GLA, 4, 4096, 16, 128, 128, 64, 0, BF16)
+    assert g >= 4 * 64 * 16 * (128 * 4 + 6 * 1024) + 2 * 4 * 4096 * 16 * 128 * 2
     assert lib.gdn_rule_supported(9, 128, 128, 64, BF16) == 0
     f = lib.gdn_rule_workspace_bytes
     assert f(RULE_DELTA, 4, 4096, 16, 128, 128, 64, 0, BF16) == \
