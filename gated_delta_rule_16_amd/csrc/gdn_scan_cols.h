@@ -715,27 +715,37 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             }
         };
         // chunk cd's Q into the Q buffer of its parity (the K blocks' offsets and
-        // swizzle), through registers: q_issue loads, q_commit writes LDS once the
-        // loads are in.  (Measured 3 to 5 us faster over the headline than
-        // direct-to-LDS loads for Q.)  The LDS writes are inline assembly so that
-        // the compiler, which cannot tell them from the pending direct-to-LDS
-        // staging loads, inserts no wait for those before them.
-        u32x4 qreg[Cfg::NL];
-        auto q_issue = [&](int cd) __attribute__((always_inline)) {
+        // swizzle, as the loader lays out K), through registers: q_issue loads
+        // into one of two register sets, q_commit writes LDS once the loads are
+        // in.  The writing wave does it: step cc writes Q of chunk cc + 1, which
+        // it requested two steps before, and requests Q of chunk cc + 3 into the
+        // set just written from -- the loads have two steps to land, as the
+        // staging loads do (with one step they did not: the wait for them set
+        // the chunk step).  The loader then issues only its direct-to-LDS
+        // staging loads.  (Through registers measured 3 to 5 us faster over the
+        // headline than direct-to-LDS loads for Q, one chunk ahead.)  The LDS
+        // writes are inline assembly so that the compiler inserts no wait for
+        // unrelated memory operations before them.
+        constexpr bool QW = !LOADER && Cfg::QLDS;
+        u32x4 qreg[2][Cfg::NL];
+        uint32_t qoff[Cfg::NL];
+#pragma unroll
+        for (int j = 0; j < Cfg::NL; ++j) qoff[j] = QW ? col_stage_offset<Cfg>(j, 0, l, rs_k, rs_v) : 0u;
+        auto q_issue = [&](u32x4* qr, int cd) __attribute__((always_inline)) {
             const int t0 = ts + cd * C, len = min(C, te - t0);
             const __amdgpu_buffer_rsrc_t rq =
                 make_rsrc(q + ((int64_t)t0 * H + h) * DK, (int)((len - 1) * rs_k + DK * ES));
 #pragma unroll
             for (int j = 0; j < Cfg::NL; ++j)
-                if (col_region<Cfg>(j, f) == 0) qreg[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, soff[j], 0, 0);
+                if (col_region<Cfg>(j, 0) == 0) qr[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff[j], 0, 0);
         };
-        auto q_commit = [&](int cd) __attribute__((always_inline)) {
+        auto q_commit = [&](const u32x4* qr, int cd) __attribute__((always_inline)) {
             typedef __attribute__((address_space(3))) unsigned char lds_u8;
-            const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)(qbuf(cd) + f * 1024) + l * 16;
+            const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)(qbuf(cd)) + l * 16;
 #pragma unroll
             for (int j = 0; j < Cfg::NL; ++j)
-                if (col_region<Cfg>(j, f) == 0)
-                    asm volatile("ds_write_b128 %0, %1" ::"v"(base + j * Cfg::NLD * 1024), "v"(qreg[j]) : "memory");
+                if (col_region<Cfg>(j, 0) == 0)
+                    asm volatile("ds_write_b128 %0, %1" ::"v"(base + j * Cfg::NLD * 1024), "v"(qr[j]) : "memory");
         };
         // chunk cd's output slice from LDS to memory, 16 bytes per lane, rows
         // past the chunk end dropped by the buffer range; streamed past the caches
@@ -754,35 +764,52 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 }
             }
         };
-        // Step cc requests Q of chunk cc + 1, stages K .. gates of chunk cc + DIST
-        // and writes Q once it is in, each into the buffer whose readers passed
-        // the previous barrier; before its closing barrier it waits for all but
-        // the newest DIST - 1 chunks of staging loads, i.e. for everything chunk
-        // cc + 1 needs (loads complete in issue order), and for its LDS writes.
-        // (Requesting Q a step earlier, so that its loads had a whole step to
-        // land, measured slower: 94 against 86 us on the headline.)
+        // Loader: step cc stages K .. gates of chunk cc + DIST into the buffer
+        // whose readers passed the previous barrier; before its closing barrier
+        // it waits for all but the newest DIST - 1 chunks of staging loads, i.e.
+        // for everything chunk cc + 1 needs (loads complete in issue order).
+        // Writer: step cc writes Q of chunk cc + 1 (register set (cc + 1) & 1),
+        // requests Q of chunk cc + 3 into that set and writes out the output
+        // slice of chunk cc - 2; before the barrier it waits for its LDS writes.
+        // (Q requested before the stores: the wait for Q's loads, which count in
+        // vmcnt with the stores, leaves the newer stores in flight.)  Past the
+        // end the last chunk is re-read (the same values).
         static_assert(ND * (Cfg::DIST - 1) < 64, "vmcnt range");
-        if (LOADER && count > 0) {
-            if constexpr (Cfg::QLDS) {
-                q_issue(0);
-                q_commit(0);
-            }
-#pragma unroll
-            for (int d = 0; d < Cfg::DIST; ++d) stage(min(d, count - 1));
-            wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
-        }
-        __syncthreads();
-        for (int cc = 0; cc < count; ++cc) {
+        if (count > 0) {
             if constexpr (LOADER) {
-                if constexpr (Cfg::QLDS) q_issue(min(cc + 1, count - 1));   // past the end: re-read, unused
-                stage(min(cc + Cfg::DIST, count - 1));
-                if constexpr (Cfg::QLDS) q_commit(min(cc + 1, count - 1));
+#pragma unroll
+                for (int d = 0; d < Cfg::DIST; ++d) stage(min(d, count - 1));
                 wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
-            } else {
-                if (cc >= 2) write_out(cc - 2);                  // formed by the output helpers last step
+            } else if constexpr (QW) {
+                q_issue(qreg[0], 0);
+                q_commit(qreg[0], 0);
+                q_issue(qreg[1], min(1, count - 1));
+                q_issue(qreg[0], min(2, count - 1));
                 wait_vm_lgkm0<63>();
             }
+        }
+        __syncthreads();
+        auto writer_step = [&](int cc, u32x4* qr) __attribute__((always_inline)) {
+            if constexpr (QW) {
+                q_commit(qr, min(cc + 1, count - 1));
+                q_issue(qr, min(cc + 3, count - 1));
+            }
+            if (cc >= 2) write_out(cc - 2);                  // formed by the output helpers last step
+            wait_vm_lgkm0<63>();
             barrier();
+        };
+        if constexpr (LOADER) {
+            for (int cc = 0; cc < count; ++cc) {
+                stage(min(cc + Cfg::DIST, count - 1));
+                wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
+                barrier();
+            }
+        } else {
+            // two steps per iteration, so that each register set is a fixed one
+            for (int cc = 0; cc < count; cc += 2) {
+                writer_step(cc, qreg[1]);
+                if (cc + 1 < count) writer_step(cc + 1, qreg[0]);
+            }
         }
         wait_vm_lgkm0<0>();   // no load still writing LDS when the workgroup ends
         __syncthreads();      // the output helpers have formed the last output slice
