@@ -22,6 +22,10 @@ Options: --gpus (only 1), --steps, --warmup, --workload, --no-flush,
 scalar-gated rule without the erase term; gla: gdn_gla_chunk_fwd, one gate per
 key channel and no erase term, the gate drawn per channel; each on the same
 workload shape),
+--split L (delta rule, fixed-length workloads: gdn_chunk_fwd_split with spans of
+L chunks instead of gdn_chunk_fwd; its kernels are prep, the span-map scan,
+the span chaining and the output scan), --heads H (override the workload's head
+count, e.g. to measure the split where there are few units),
 --recurrent N (instead: the single-token step, gdn_recurrent_step, over a decode
 batch of N sequences with the workload's H, Dk, Dv and dtype; its own JSON line).
 """
@@ -247,6 +251,9 @@ def main():
     ap.add_argument("--rule", choices=["delta", "mamba2", "gla"], default="delta",
                     help="update rule: delta (gdn_chunk_fwd), mamba2 (gdn_mamba2_chunk_fwd) "
                          "or gla (gdn_gla_chunk_fwd)")
+    ap.add_argument("--split", type=int, default=0, metavar="L",
+                    help="delta rule: gdn_chunk_fwd_split with spans of L chunks")
+    ap.add_argument("--heads", type=int, default=0, help="override the workload's head count")
     ap.add_argument("--recurrent", type=int, default=0, metavar="N",
                     help="time gdn_recurrent_step over N sequences instead (one token each)")
     args = ap.parse_args()
@@ -265,7 +272,14 @@ def main():
     if args.recurrent > 0:
         bench_recurrent(args, w)
         return
-    inp = workload_inputs(args.workload, gate_channels=args.rule == "gla")
+    if args.heads > 0:
+        import dataclasses
+        w = dataclasses.replace(w, H=args.heads)
+        from gated_delta_rule_16_amd.inputs import make_inputs
+        inp = make_inputs(w.B, w.T, w.H, w.Dk, w.Dv, dtype=w.dtype, gated=w.gated, s0=w.s0,
+                          seed=w.seed, C=w.C, gate_channels=args.rule == "gla")
+    else:
+        inp = workload_inputs(args.workload, gate_channels=args.rule == "gla")
     dev = torch.device("cuda:0")
     d = inp.to(dev)
     B, T, H = inp.q.shape[:3]
@@ -277,8 +291,20 @@ def main():
             "gla": gdn.GDN_RULE_GLA}[args.rule]
     fwd = {"delta": gdn.gdn_chunk_fwd, "mamba2": gdn.gdn_mamba2_chunk_fwd,
            "gla": gdn.gdn_gla_chunk_fwd}[args.rule]
-    n_ws = gdn.gdn_rule_workspace_bytes(rule, B, T, H, w.Dk, w.Dv, w.C,
-                                        0 if inp.cu_seqlens is None else N, tdt)
+    # span length of the split scan: --split, else what gdn_chunk_fwd takes by
+    # itself for these sizes (0: the plain scan), so that the per-kernel times
+    # below come from the path the timed steps ran
+    auto_split = 0
+    if args.rule == "delta" and args.split == 0:
+        auto_split = gdn.gdn_chunk_fwd_auto_span_chunks(B, T, H, w.Dk, w.Dv, w.C,
+                                                        0 if inp.cu_seqlens is None else N, tdt)
+    span = args.split or auto_split
+    if args.split > 0:
+        assert args.rule == "delta" and inp.cu_seqlens is None, "--split: delta rule, fixed length"
+        n_ws = gdn.gdn_chunk_fwd_split_workspace_bytes(B, T, H, w.Dk, w.Dv, w.C, args.split, tdt)
+    else:
+        n_ws = gdn.gdn_rule_workspace_bytes(rule, B, T, H, w.Dk, w.Dv, w.C,
+                                            0 if inp.cu_seqlens is None else N, tdt)
     ws = torch.empty(n_ws, device=dev, dtype=torch.uint8)
     # Cache eviction between steps: one pass reading 512 MB (twice the MALL)
     # leaves L2 and MALL holding clean lines of this buffer, so every step reads
@@ -294,8 +320,12 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, d.cu_seqlens, chunk_size=w.C,
-            O=O, S_T=S_T, workspace=ws, stream=stream)
+        if args.split > 0:
+            gdn.gdn_chunk_fwd_split(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, span_chunks=args.split,
+                                    chunk_size=w.C, O=O, S_T=S_T, workspace=ws, stream=stream)
+        else:
+            fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, d.cu_seqlens, chunk_size=w.C,
+                O=O, S_T=S_T, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         evict()
@@ -319,21 +349,29 @@ def main():
     value = tokens / (ms / 1e3)
 
     # per-kernel device time (HIP events on the launch stream, inside the library)
-    kms = {"table": [], "prep": [], "scan": [], "unused": []}
+    if span > 0:
+        kms = {"prep": [], "span_maps": [], "span_chain": [], "scan": []}
+    else:
+        kms = {"table": [], "prep": [], "scan": [], "unused": []}
     for _ in range(args.profile_steps):
         evict()
-        _, _, t = gdn.gdn_rule_chunk_fwd_profiled(rule, d.q, d.k, d.v, d.log_alpha, d.beta,
-                                                  d.S0, d.cu_seqlens, chunk_size=w.C, O=O,
-                                                  S_T=S_T, workspace=ws, stream=stream)
+        if span > 0:
+            _, _, t = gdn.gdn_chunk_fwd_split(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0,
+                                              span_chunks=span, chunk_size=w.C, O=O,
+                                              S_T=S_T, workspace=ws, stream=stream, profiled=True)
+        else:
+            _, _, t = gdn.gdn_rule_chunk_fwd_profiled(rule, d.q, d.k, d.v, d.log_alpha, d.beta,
+                                                      d.S0, d.cu_seqlens, chunk_size=w.C, O=O,
+                                                      S_T=S_T, workspace=ws, stream=stream)
         for key, x in zip(kms, t):
             kms[key].append(x)
-    kms.pop("unused")
+    kms.pop("unused", None)
     kmean = {k_: (statistics.mean(v_) if v_ else 0.0) for k_, v_ in kms.items()}
 
     s_in = 2 if w.dtype == "bf16" else 4
     work = per_kernel_work(B, T, H, w.Dk, w.Dv, w.C, s_in, N, inp.S0 is not None,
                            inp.log_alpha is not None, args.rule)
-    dom = max(("prep", "scan"), key=lambda k_: kmean[k_])
+    dom = max((k_ for k_ in ("prep", "scan") if k_ in kmean), key=lambda k_: kmean[k_])
     rl_dom = roofline(dom, *work[dom], kmean[dom] / 1e3, w.dtype)
     tkey = args.workload if args.rule == "delta" else f"{args.rule}_{args.workload}"
     rl_dom["traffic"] = measured_traffic(tkey, dom)
@@ -361,7 +399,8 @@ def main():
     if args.cpu_sample > 0:
         cpu = cpu_baseline(inp, args.cpu_sample, no_erase=args.rule != "delta")
 
-    headline = args.workload == ap.get_default("workload") and args.rule == "delta"
+    headline = (args.workload == ap.get_default("workload") and args.rule == "delta"
+                and args.split == 0 and args.heads == 0)
     metric = METRIC if headline else f"tokens/sec gated-DeltaNet chunk fwd ({args.workload})"
     if args.rule == "mamba2":
         metric = f"tokens/sec Mamba2 (scalar gate, no erase) chunk fwd ({args.workload})"
@@ -373,7 +412,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload, "rule": args.rule, "B": B, "T": T, "H": H,
+        "config": {"workload": args.workload + (f"_h{H}" if args.heads > 0 else ""),
+                   "rule": args.rule, "split_span_chunks": span or None,
+                   "split": "forced" if args.split else ("auto" if auto_split else None), "B": B, "T": T, "H": H,
                    "Dk": w.Dk, "Dv": w.Dv,
                    "chunk": w.C, "state": "fp32", "S0": inp.S0 is not None,
                    "flush_l2_mall": flush is not None},

@@ -9,7 +9,8 @@ The Python functions carry the C names:
   gdn_chunk_fwd, gdn_chunk_fwd_profiled, gdn_chunk_fwd_noalloc, gdn_recurrent_step,
   gdn_chunk_fwd_workspace_bytes, gdn_chunk_fwd_supported, gdn_status_string,
   gdn_mamba2_chunk_fwd, gdn_gla_chunk_fwd, gdn_rule_chunk_fwd_profiled,
-  gdn_rule_workspace_bytes, gdn_rule_supported.
+  gdn_rule_workspace_bytes, gdn_rule_supported, gdn_chunk_fwd_split, gdn_chunk_fwd_auto_span_chunks,
+  gdn_chunk_fwd_split_workspace_bytes.
 """
 from __future__ import annotations
 
@@ -64,6 +65,12 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_mamba2_chunk_fwd.restype = I
     lib.gdn_gla_chunk_fwd.argtypes = lib.gdn_chunk_fwd.argtypes
     lib.gdn_gla_chunk_fwd.restype = I
+    lib.gdn_chunk_fwd_split_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.gdn_chunk_fwd_split_workspace_bytes.restype = SZ
+    lib.gdn_chunk_fwd_auto_span_chunks.argtypes = [I, I, I, I, I, I, I, I]
+    lib.gdn_chunk_fwd_auto_span_chunks.restype = I
+    lib.gdn_chunk_fwd_split.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, SZ, P, P]
+    lib.gdn_chunk_fwd_split.restype = I
     lib.gdn_rule_chunk_fwd_profiled.argtypes = [I] + lib.gdn_chunk_fwd.argtypes + [P]
     lib.gdn_rule_chunk_fwd_profiled.restype = I
     lib.gdn_rule_supported.argtypes = [I, I, I, I, I]
@@ -274,6 +281,65 @@ def gdn_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         B, T, H, Dk, Dv, chunk_size, _DT[dt], _stream(dev, stream))
     if rc != 0:
         raise GdnError(rc, "gdn_chunk_fwd_noalloc")
+
+
+def gdn_chunk_fwd_split_workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, C: int,
+                                        span_chunks: int, dtype: torch.dtype) -> int:
+    return int(load_library().gdn_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, C, span_chunks,
+                                                                  _DT[dtype]))
+
+
+def gdn_chunk_fwd_auto_span_chunks(B: int, T: int, H: int, Dk: int, Dv: int, C: int,
+                                   n_seqs: int, dtype: torch.dtype) -> int:
+    """Span length gdn_chunk_fwd splits these sizes into on the current device,
+    or 0 for the plain scan (include/gdn.h)."""
+    return int(load_library().gdn_chunk_fwd_auto_span_chunks(B, T, H, Dk, Dv, C, n_seqs, _DT[dtype]))
+
+
+def gdn_chunk_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        log_alpha: Optional[torch.Tensor], beta: torch.Tensor,
+                        S0: Optional[torch.Tensor] = None, *, span_chunks: int,
+                        chunk_size: int = 64, O: Optional[torch.Tensor] = None,
+                        S_T: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                        workspace: Optional[torch.Tensor] = None,
+                        stream: Optional[torch.cuda.Stream] = None, profiled: bool = False):
+    """gdn_chunk_fwd of a fixed-length batch with each sequence split into spans
+    of ``span_chunks`` chunks (include/gdn.h, gdn_chunk_fwd_split).  Returns
+    (O, S_T), and with ``profiled`` also the device milliseconds of
+    [prep, pass 1, pass 2, pass 3] (the call then blocks)."""
+    lib = load_library()
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,T,H,Dk] and v [B,T,H,Dv]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t in (("beta", beta), ("log_alpha", log_alpha)):
+        if t is not None and t.shape != (B, T, H):
+            raise ValueError(f"{name} must be [B,T,H]")
+    if S0 is not None and S0.shape != (B, H, Dv, Dk):
+        raise ValueError("S0 must be [B,H,Dv,Dk]")
+    if O is None:
+        O = torch.empty(B, T, H, Dv, device=dev, dtype=dt)
+    if S_T is None and output_final_state:
+        S_T = torch.empty(B, H, Dv, Dk, device=dev, dtype=torch.float32)
+    need = lib.gdn_chunk_fwd_split_workspace_bytes(B, T, H, Dk, Dv, chunk_size, span_chunks, _DT[dt])
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), device=dev, dtype=torch.uint8)
+    ms = (ctypes.c_float * 4)() if profiled else None
+    rc = lib.gdn_chunk_fwd_split(
+        _ptr(q, "q", dev, dt), _ptr(k, "k", dev, dt), _ptr(v, "v", dev, dt),
+        _ptr(log_alpha, "log_alpha", dev, torch.float32), _ptr(beta, "beta", dev, torch.float32),
+        _ptr(S0, "S0", dev, torch.float32), _ptr(O, "O", dev, dt), _ptr(S_T, "S_T", dev, torch.float32),
+        B, T, H, Dk, Dv, chunk_size, _DT[dt], span_chunks,
+        _ptr(workspace, "workspace", dev), workspace.numel() * workspace.element_size(),
+        _stream(dev, stream), ms)
+    if rc != 0:
+        raise GdnError(rc, "gdn_chunk_fwd_split")
+    if profiled:
+        return O, S_T, [float(x) for x in ms]
+    return O, S_T
 
 
 def gdn_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -21,6 +21,7 @@
 #include "gdn_gla_prep.h"
 #include "gdn_prep.h"
 #include "gdn_scan_cols.h"
+#include "gdn_span.h"
 #include "gdn_step.h"
 
 namespace gdn {
@@ -154,6 +155,38 @@ struct KernelTimer {
     }
 };
 
+// The column-wave scan over n_seqs sequences (or spans) of every head, with 32
+// state columns per workgroup where that fits in LDS and still gives every CU
+// a workgroup, else 16.
+template <typename T, int DK, int DV, int C, int RULE>
+gdn_status launch_scan(const T* q, const T* k, const T* v, const float* S0, const SeqGeom& geom,
+                       int H, int64_t n_seqs, const float* g_ws, const T* Tb_ws, T* O, float* S_T,
+                       ScanRows rows, hipStream_t stream, KernelTimer* tm) {
+    using C32 = ColCfg<T, DK, DV, C, (DV >= 32 ? 32 : 16), RULE>;
+    using C16 = ColCfg<T, DK, DV, C, 16, RULE>;
+    constexpr bool fit32 = DV >= 32 && C32::FITS, fit16 = C16::FITS;
+    const int64_t units = (int64_t)H * n_seqs;
+    auto launch_cols = [&](auto cfg_tag) -> gdn_status {
+        using CC = decltype(cfg_tag);
+        if constexpr (CC::FITS) {
+            constexpr int DVT = CC::NVW * 16;
+            constexpr auto ks = gdn_scan_cols_kernel<T, DK, DV, C, DVT, RULE>;
+            allow_smem<ks>(CC::SMEM);
+            tm->mark(stream);
+            hipLaunchKernelGGL(ks, dim3(DV / DVT, H, (unsigned)n_seqs), dim3(CC::NTHR), CC::SMEM, stream,
+                               q, k, v, S0, geom, H, g_ws, Tb_ws, O, S_T, rows);
+            if (gdn_status s = check_launch(stream)) return s;
+            tm->mark(stream);
+            return GDN_OK;
+        } else {
+            return GDN_ERR_INTERNAL;
+        }
+    };
+    static_assert(fit32 || fit16, "no column-scan configuration fits the LDS of one CU");
+    if (fit32 && (!fit16 || units * (DV / 32) >= device_cu_count())) return launch_cols(C32{});
+    return launch_cols(C16{});
+}
+
 template <typename T, int DK, int DV, int C, int RULE>
 gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     const bool varlen = a.cu != nullptr;
@@ -231,35 +264,92 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         if (gdn_status s = check_launch(a.stream)) return s;
         tm->mark(a.stream);
     }
-    {
-        // the column-wave scan, with 32 state columns per workgroup where that
-        // fits in LDS and still gives every CU a workgroup, else 16
-        using C32 = ColCfg<T, DK, DV, C, (DV >= 32 ? 32 : 16), RULE>;
-        using C16 = ColCfg<T, DK, DV, C, 16, RULE>;
-        constexpr bool fit32 = DV >= 32 && C32::FITS, fit16 = C16::FITS;
-        const int64_t units = (int64_t)a.H * L.N;
-        auto launch_cols = [&](auto cfg_tag) -> gdn_status {
-            using CC = decltype(cfg_tag);
-            if constexpr (CC::FITS) {
-                constexpr int DVT = CC::NVW * 16;
-                constexpr auto ks = gdn_scan_cols_kernel<T, DK, DV, C, DVT, RULE>;
-                allow_smem<ks>(CC::SMEM);
-                tm->mark(a.stream);
-                hipLaunchKernelGGL(ks, dim3(DV / DVT, a.H, (unsigned)L.N), dim3(CC::NTHR), CC::SMEM,
-                                   a.stream, q, k, v, a.S0, geom, a.H, g_ws, Tb_ws,
-                                   static_cast<T*>(a.O), a.S_T);
-                if (gdn_status s = check_launch(a.stream)) return s;
-                tm->mark(a.stream);
-                return GDN_OK;
-            } else {
-                return GDN_ERR_INTERNAL;
-            }
-        };
-        static_assert(fit32 || fit16, "no column-scan configuration fits the LDS of one CU");
-        if (fit32 && (!fit16 || units * (DV / 32) >= device_cu_count())) return launch_cols(C32{});
-        return launch_cols(C16{});
+    return launch_scan<T, DK, DV, C, RULE>(q, k, v, a.S0, geom, a.H, L.N, g_ws, Tb_ws,
+                                           static_cast<T*>(a.O), a.S_T, ScanRows{0, DV}, a.stream,
+                                           tm);
+}
+
+// ---------------------------------------------------------------------------
+// Split scan: the sequences of a fixed-length batch cut into spans of L
+// chunks; (1) the scan of every span from identity rows gives its map (M, b),
+// (2) gdn_span_chain_kernel chains the maps into each span's start state,
+// (3) the scan of every span from its start state writes O.  Compiled for
+// bf16 Dk = Dv = 128, C = 64 (the first pass runs the Dv = 256 scan).
+// ---------------------------------------------------------------------------
+struct SplitLayout {
+    int64_t P, slots;
+    size_t g, Tb, maps, sin, total;
+};
+
+SplitLayout make_split_layout(int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C,
+                              int64_t L, size_t es) {
+    SplitLayout S{};
+    const int64_t cps = (T + C - 1) / C;
+    S.P = cps > 0 ? (cps + L - 1) / L : 1;   // spans per sequence
+    S.slots = B * cps;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t at = off; off = align_up(off + bytes); return at; };
+    const size_t u = (size_t)(S.slots * H);
+    S.g = take(u * gate_rows(kDelta) * C * sizeof(float));
+    S.Tb = take(u * (size_t)tb_blocks((int)C, es == 2) * 1024);
+    S.maps = take((size_t)(B * S.P * H) * (Dk + Dv) * Dk * sizeof(float));
+    S.sin = take((size_t)(B * S.P * H) * Dv * Dk * sizeof(float));
+    S.total = off;
+    return S;
+}
+
+template <typename T, int DK, int DV, int C>
+gdn_status launch_split(const FwdArgs& a, int L, KernelTimer* tm) {
+    const SplitLayout S = make_split_layout(a.B, a.T, a.H, DK, DV, C, L, sizeof(T));
+    float* g_ws = reinterpret_cast<float*>(a.ws + S.g);
+    T* Tb_ws = reinterpret_cast<T*>(a.ws + S.Tb);
+    float* maps = reinterpret_cast<float*>(a.ws + S.maps);
+    float* sin = reinterpret_cast<float*>(a.ws + S.sin);
+    const T* q = static_cast<const T*>(a.q);
+    const T* k = static_cast<const T*>(a.k);
+    const T* v = static_cast<const T*>(a.v);
+    SeqGeom geom{};
+    geom.C = C;
+    geom.T = a.T;
+    geom.chunks_per_seq = (a.T + C - 1) / C;
+    // prep over every chunk: the chunk slots are the same split or not
+    tm->mark(a.stream);
+    if (S.slots > 0) {
+        using P = PrepCfg<T, DK, C>;
+        constexpr auto kp = gdn_prep_kernel<T, DK, C>;
+        allow_smem<kp>(P::SMEM);
+        const int64_t units = S.slots * a.H;
+        const int64_t resident = (int64_t)device_cu_count() * resident_per_cu<kp>(kThreads, P::SMEM);
+        const int64_t need = (units + P::WAVES - 1) / P::WAVES;
+        const unsigned grid = (unsigned)(need < resident ? need : resident);
+        hipLaunchKernelGGL(kp, dim3(grid), dim3(kThreads), P::SMEM, a.stream,
+                           k, a.log_alpha, a.beta, geom, a.H, (int)units, g_ws, Tb_ws);
+        if (gdn_status s = check_launch(a.stream)) return s;
     }
-    return GDN_OK;
+    tm->mark(a.stream);
+    SeqGeom sg = geom;
+    sg.span_chunks = L;
+    sg.spans = (int)S.P;
+    const int64_t NS = a.B * S.P;
+    // (1) span maps: DK identity rows with zero values, then the DV value rows
+    // from zero; no outputs
+    if (gdn_status s = launch_scan<T, DK, DK + DV, C, kDelta>(q, k, v, nullptr, sg, a.H, NS, g_ws, Tb_ws,
+                                                            nullptr, maps, ScanRows{DK, DV}, a.stream, tm))
+        return s;
+    // (2) each span's start state, and S_T
+    {
+        using SC = SpanCfg<DK, DV>;
+        constexpr auto kc = gdn_span_chain_kernel<DK, DV>;
+        allow_smem<kc>(SC::SMEM);
+        tm->mark(a.stream);
+        hipLaunchKernelGGL(kc, dim3(DV / SC::ROWS, a.H, a.B), dim3(SC::THREADS), SC::SMEM, a.stream,
+                           maps, a.S0, (int)S.P, a.H, sin, a.S_T);
+        if (gdn_status s = check_launch(a.stream)) return s;
+        tm->mark(a.stream);
+    }
+    // (3) the outputs of every span from its start state
+    return launch_scan<T, DK, DV, C, kDelta>(q, k, v, sin, sg, a.H, NS, g_ws, Tb_ws,
+                                             static_cast<T*>(a.O), nullptr, ScanRows{0, DV}, a.stream, tm);
 }
 
 typedef gdn_status (*FwdFn)(const FwdArgs&, KernelTimer*);
@@ -337,6 +427,29 @@ gdn_status check_sizes(int rule, int B, int T, int H, int Dk, int Dv, int C, boo
     return GDN_OK;
 }
 
+// Span length of gdn_chunk_fwd's automatic split (0: no split).  The plain
+// scan runs one workgroup per 32 state columns of each (sequence, head) unit,
+// B H Dv / 32 in all, each walking the whole sequence; with few units most CUs
+// idle.  The split costs about three scans' work (pass 1 carries Dk + Dv state
+// rows, pass 3 Dv) spread over P times the workgroups.  Measured on bf16
+// Dk = Dv = 128, T = 32768 (512 chunks), plain -> split: 4 heads 0.51 -> 0.17 ms,
+// 8 heads 0.53 -> 0.25 ms, 16 heads 0.58 -> 0.47 ms, 32 heads 0.72 -> 0.94 ms.
+// So: split when the plain scan's workgroups fill at most a quarter of the CUs
+// and sequences have at least 32 chunks, into P = CUs / workgroups spans (the
+// output pass then has a workgroup per CU), spans of at least 8 chunks.
+int auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt, bool varlen) {
+    if (varlen || dt != GDN_BF16 || Dk != 128 || Dv != 128 || C != 64 || T <= 0) return 0;
+    const int64_t cps = ((int64_t)T + C - 1) / C;
+    const int64_t cus = device_cu_count();
+    const int64_t units = (int64_t)B * H;
+    const int64_t wgs = units * (Dv / 32);   // workgroups of the plain scan
+    if (cps < 32 || wgs * 4 > cus) return 0;
+    int64_t P = cus / wgs;
+    if (P > cps / 8) P = cps / 8;
+    if (P < 2) return 0;
+    return (int)((cps + P - 1) / P);
+}
+
 }  // namespace
 }  // namespace gdn
 
@@ -354,7 +467,22 @@ extern "C" size_t gdn_rule_workspace_bytes(gdn_rule rule, int B, int T, int H, i
                                            int C, int n_seqs, gdn_dtype dt) {
     const bool varlen = n_seqs > 0;
     if (check_sizes(rule, B, T, H, Dk, Dv, C, varlen, n_seqs, dt) != GDN_OK) return 0;
-    return make_layout(rule, B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt)).total;
+    const size_t plain = make_layout(rule, B, T, H, Dk, Dv, C, varlen, n_seqs, elem_size(dt)).total;
+    if (rule == GDN_RULE_DELTA) {   // room for the automatic split where gdn_chunk_fwd takes it
+        const int L = auto_span_chunks(B, T, H, Dk, Dv, C, dt, varlen);
+        if (L > 0) {
+            const size_t split = make_split_layout(B, T, H, Dk, Dv, C, L, elem_size(dt)).total;
+            return split > plain ? split : plain;
+        }
+    }
+    return plain;
+}
+
+extern "C" int gdn_chunk_fwd_auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C,
+                                              int n_seqs, gdn_dtype dt) {
+    const bool varlen = n_seqs > 0;
+    if (check_sizes(GDN_RULE_DELTA, B, T, H, Dk, Dv, C, varlen, n_seqs, dt) != GDN_OK) return 0;
+    return auto_span_chunks(B, T, H, Dk, Dv, C, dt, varlen);
 }
 
 extern "C" size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
@@ -427,6 +555,13 @@ gdn_status chunk_fwd_impl(int rule, const void* q, const void* k, const void* v,
               B, T, H, Dk, Dv, C, dt, static_cast<unsigned char*>(workspace),
               static_cast<hipStream_t>(stream)};
     (void)hipGetLastError();   // report only errors raised by this call's launches
+    // the automatic split (plain, unprofiled calls of the delta rule with room
+    // for it in the workspace)
+    if (rule == GDN_RULE_DELTA && !use_scratch && !tm->on) {
+        const int Ls = auto_span_chunks(B, T, H, Dk, Dv, C, dt, varlen);
+        if (Ls > 0 && workspace_bytes >= make_split_layout(B, T, H, Dk, Dv, C, Ls, elem_size(dt)).total)
+            return launch_split<bf16, 128, 128, 64>(a, Ls, tm);
+    }
     return find_variant(rule, Dk, Dv, C, dt)->fn(a, tm);
 }
 }  // namespace
@@ -538,6 +673,70 @@ extern "C" gdn_status gdn_rule_chunk_fwd_profiled(gdn_rule rule, const void* q, 
             }
         }
         for (int i = 0; i < 8; ++i) (void)hipEventDestroy(tm.ev[i]);
+        return s;
+    } catch (...) {
+        return GDN_ERR_INTERNAL;
+    }
+}
+
+namespace {
+gdn_status check_split(int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt, int span_chunks) {
+    if (gdn_status s = check_sizes(GDN_RULE_DELTA, B, T, H, Dk, Dv, C, false, 0, dt)) return s;
+    if (Dk != 128 || Dv != 128 || C != 64 || dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (span_chunks < 1) return GDN_ERR_SHAPE;
+    const SplitLayout S = make_split_layout(B, T, H, Dk, Dv, C, span_chunks, elem_size(dt));
+    // the span maps, [B P][H][Dk + Dv][Dk], and the span grid
+    if (B * S.P * H * (int64_t)(Dk + Dv) * Dk > kMaxElems || B * S.P > 65535) return GDN_ERR_SHAPE;
+    return GDN_OK;
+}
+}  // namespace
+
+extern "C" size_t gdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
+                                                      int span_chunks, gdn_dtype dt) {
+    if (check_split(B, T, H, Dk, Dv, C, dt, span_chunks) != GDN_OK) return 0;
+    return make_split_layout(B, T, H, Dk, Dv, C, span_chunks, elem_size(dt)).total;
+}
+
+extern "C" gdn_status gdn_chunk_fwd_split(const void* q, const void* k, const void* v,
+                                          const float* log_alpha, const float* beta,
+                                          const float* S0, void* O, float* S_T, int B, int T,
+                                          int H, int Dk, int Dv, int C, gdn_dtype dt,
+                                          int span_chunks, void* workspace,
+                                          size_t workspace_bytes, void* stream,
+                                          float* kernel_ms) {
+    try {
+        if (T > 0 && (!q || !k || !v || !beta || !O)) return GDN_ERR_NULL;
+        if (gdn_status s = check_split(B, T, H, Dk, Dv, C, dt, span_chunks)) return s;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(O) || !aligned16(S0) ||
+            !aligned16(S_T) || !aligned16(workspace))
+            return GDN_ERR_SHAPE;
+        const size_t need = make_split_layout(B, T, H, Dk, Dv, C, span_chunks, elem_size(dt)).total;
+        if (!workspace) return GDN_ERR_NULL;
+        if (workspace_bytes < need) return GDN_ERR_WORKSPACE;
+        FwdArgs a{q, k, v, log_alpha, beta, S0, nullptr, B, O, S_T, B, T, H, Dk, Dv, C, dt,
+                  static_cast<unsigned char*>(workspace), static_cast<hipStream_t>(stream)};
+        KernelTimer tm;
+        tm.on = kernel_ms != nullptr;
+        int created = 0;
+        if (tm.on) {
+            for (int i = 0; i < 4; ++i) kernel_ms[i] = 0.f;
+            for (; created < 8; ++created)
+                if (hipEventCreate(&tm.ev[created]) != hipSuccess) break;
+            if (created < 8) {
+                for (int j = 0; j < created; ++j) (void)hipEventDestroy(tm.ev[j]);
+                return GDN_ERR_HIP;
+            }
+        }
+        (void)hipGetLastError();
+        gdn_status s = launch_split<bf16, 128, 128, 64>(a, span_chunks, &tm);
+        if (tm.on) {
+            // marks: prep, pass 1, chain, pass 3
+            if (s == GDN_OK && hipEventSynchronize(tm.ev[tm.n - 1]) != hipSuccess) s = GDN_ERR_HIP;
+            for (int i = 0; s == GDN_OK && i < 4 && 2 * i + 1 < tm.n; ++i)
+                if (hipEventElapsedTime(&kernel_ms[i], tm.ev[2 * i], tm.ev[2 * i + 1]) != hipSuccess)
+                    s = GDN_ERR_HIP;
+            for (int i = 0; i < 8; ++i) (void)hipEventDestroy(tm.ev[i]);
+        }
         return s;
     } catch (...) {
         return GDN_ERR_INTERNAL;

@@ -146,6 +146,9 @@ struct SeqGeom {
     int T;                   // fixed: tokens per sequence
     int chunks_per_seq;      // fixed: ceil(T / C)
     int C;
+    // fixed length, split into spans of span_chunks chunks (0: not split): the
+    // scan's sequence index s is then span s % spans of sequence s / spans
+    int span_chunks, spans;
 };
 
 __device__ __forceinline__ ChunkInfo chunk_info(const SeqGeom& g, int slot) {

@@ -216,12 +216,23 @@ __device__ __forceinline__ typename K16<T>::op kT_tile(const T* sK, int kb, int 
     }
 }
 
+// Rows of the scan's state beyond the plain forward (span maps):
+//  vz   the first vz state rows start at the identity (row r = e_r) and take
+//       zero values; row vz + j takes value column j of v.  After a span of
+//       chunks those rows hold the product of the chunk maps S -> S M_c + B_c,
+//       and the rest (from a zero start) hold the span's offset.
+//  vld  elements per (token, head) row of v and O (DV - vz).
+// O == NULL: no outputs; the output helpers and the writer only keep step.
+struct ScanRows {
+    int vz, vld;
+};
+
 template <typename T, int DK, int DV, int C, int DVT, int RULE>
 __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* S0, SeqGeom geom, int H,
     const float* __restrict__ g_ws, const T* __restrict__ Tb_ws,
-    T* __restrict__ O, float* S_T) {   // S_T may alias S0
+    T* __restrict__ O, float* S_T, ScanRows rows) {   // S_T may alias S0
     using Cfg = ColCfg<T, DK, DV, C, DVT, RULE>;
     static_assert(Cfg::FITS, "scan workgroup exceeds the LDS of one CU");
     using St16 = Step<T>;
@@ -262,6 +273,11 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         ts = geom.bounds[seq];
         te = geom.bounds[seq + 1];
         first = geom.seq_slot[seq];
+    } else if (geom.span_chunks > 0) {
+        const int b = seq / geom.spans, p = seq - b * geom.spans;
+        ts = b * geom.T + p * geom.span_chunks * C;
+        te = min(ts + geom.span_chunks * C, (b + 1) * geom.T);
+        first = b * geom.chunks_per_seq + p * geom.span_chunks;
     } else {
         ts = seq * geom.T;
         te = ts + geom.T;
@@ -269,7 +285,11 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
     }
     const int count = (te - ts + C - 1) / C;
     const int64_t sbase = ((int64_t)seq * H + h) * DV * DK;
-    const int64_t rs_k = (int64_t)H * DK * ES, rs_v = (int64_t)H * DV * ES;   // token strides (bytes)
+    // token strides (bytes); v and O rows hold vld values, column v0 - vz
+    const int64_t rs_k = (int64_t)H * DK * ES, rs_v = (int64_t)H * rows.vld * ES;
+    const bool vzero = v0 < rows.vz;           // whole slice in the identity rows
+    const int vc0 = v0 - rows.vz;              // first value column of the slice
+    const bool no_out = O == nullptr;
 
     auto barrier = [&]() __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
@@ -310,8 +330,16 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         const int vcol = v0 + vb * 16 + n;                 // this lane's state column
         f32x4 St[NDB];
 #pragma unroll
-        for (int i = 0; i < NDB; ++i)
-            St[i] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (int64_t)vcol * DK + drow<Cfg>(i, g4)) : zero4();
+        for (int i = 0; i < NDB; ++i) {
+            if (vcol < rows.vz) {   // identity row: 1 at d = vcol
+                const int d0 = drow<Cfg>(i, g4);
+                St[i] = f32x4{d0 == vcol ? 1.f : 0.f, d0 + 1 == vcol ? 1.f : 0.f, d0 + 2 == vcol ? 1.f : 0.f,
+                              d0 + 3 == vcol ? 1.f : 0.f};
+            } else {
+                St[i] = S0 ? *reinterpret_cast<const f32x4*>(S0 + sbase + (int64_t)vcol * DK + drow<Cfg>(i, g4))
+                           : zero4();
+            }
+        }
         // the state slice as MFMA operands (input dtype), for this wave's Y and
         // for the output helpers' Z^T of chunk 0
         Op Sb[NDB];
@@ -476,6 +504,12 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
     // step cc (kept in registers), their output in step cc + 1
     auto run_out = [&](auto hw_const) __attribute__((always_inline)) {
         constexpr int hw = decltype(hw_const)::value;
+        if (no_out) {   // (uniform) no outputs: keep step with the other waves
+            __syncthreads();
+            for (int cc = 0; cc < count; ++cc) barrier();
+            __syncthreads();
+            return;
+        }
         constexpr int NM = Cfg::nmine(hw);
         // without QLDS: Q rows of this helper's query blocks straight into
         // registers, lane (g, n) getting Q[qb*16 + n][kk*KS + g*EV ..] (rows past
@@ -699,10 +733,10 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             const int t0 = ts + cd * C, len = min(C, te - t0);
             const int64_t unit = (int64_t)(first + cd) * H + h;
             const T* kb = k + ((int64_t)t0 * H + h) * DK;
-            const T* vb_ = v + ((int64_t)t0 * H + h) * DV + v0;
+            const T* vb_ = v + ((int64_t)t0 * H + h) * rows.vld + (vzero ? 0 : vc0);
             const T* tb = Tb_ws + unit * (Cfg::NIT * 1024 / ES);
             const float* gb = g_ws + unit * Cfg::GF;
-            const int nk = (int)((len - 1) * rs_k + DK * ES), nv = (int)((len - 1) * rs_v + DVT * ES);
+            const int nk = (int)((len - 1) * rs_k + DK * ES), nv = vzero ? 0 : (int)((len - 1) * rs_v + DVT * ES);
             unsigned char* dst = smem + (cd % Cfg::NSTG) * Cfg::SZ_STAGE + f * 1024;
 #pragma unroll
             for (int j = 0; j < Cfg::NL; ++j) {
@@ -752,7 +786,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         auto write_out = [&](int cd) __attribute__((always_inline)) {
             const int t0 = ts + cd * C, len = min(C, te - t0);
             const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(O + ((int64_t)t0 * H + h) * DV + v0, (len - 1) * rs_v + DVT * ES);
+                make_rsrc(O + ((int64_t)t0 * H + h) * rows.vld + vc0, (len - 1) * rs_v + DVT * ES);
             const unsigned char* ob = obuf(cd);
 #pragma unroll
             for (int j = 0; j < Cfg::NOPL; ++j) {
@@ -781,20 +815,24 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                 for (int d = 0; d < Cfg::DIST; ++d) stage(min(d, count - 1));
                 wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
             } else if constexpr (QW) {
-                q_issue(qreg[0], 0);
-                q_commit(qreg[0], 0);
-                q_issue(qreg[1], min(1, count - 1));
-                q_issue(qreg[0], min(2, count - 1));
-                wait_vm_lgkm0<63>();
+                if (!no_out) {
+                    q_issue(qreg[0], 0);
+                    q_commit(qreg[0], 0);
+                    q_issue(qreg[1], min(1, count - 1));
+                    q_issue(qreg[0], min(2, count - 1));
+                    wait_vm_lgkm0<63>();
+                }
             }
         }
         __syncthreads();
         auto writer_step = [&](int cc, u32x4* qr) __attribute__((always_inline)) {
             if constexpr (QW) {
-                q_commit(qr, min(cc + 1, count - 1));
-                q_issue(qr, min(cc + 3, count - 1));
+                if (!no_out) {
+                    q_commit(qr, min(cc + 1, count - 1));
+                    q_issue(qr, min(cc + 3, count - 1));
+                }
             }
-            if (cc >= 2) write_out(cc - 2);                  // formed by the output helpers last step
+            if (cc >= 2 && !no_out) write_out(cc - 2);       // formed by the output helpers last step
             wait_vm_lgkm0<63>();
             barrier();
         };
@@ -814,8 +852,8 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         wait_vm_lgkm0<0>();   // no load still writing LDS when the workgroup ends
         __syncthreads();      // the output helpers have formed the last output slice
         if constexpr (!LOADER) {
-            if (count >= 2) write_out(count - 2);
-            if (count >= 1) write_out(count - 1);
+            if (count >= 2 && !no_out) write_out(count - 2);
+            if (count >= 1 && !no_out) write_out(count - 1);
         }
     };
 

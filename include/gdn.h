@@ -116,6 +116,14 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
  *  stream      hipStream_t to enqueue on.
  * With T = 0 nothing but S_T = S0 is computed and q, k, v, beta, O (and the
  * workspace, whose required size may then be 0) may be NULL.
+ * Long sequences with few units: for a fixed-length bf16 batch with
+ * Dk = Dv = 128, C = 64, at least 32 chunks per sequence and B H Dv / 32 (the
+ * plain scan's workgroups) at most a quarter of the device's CUs, the call runs
+ * the split scan of gdn_chunk_fwd_split (spans sized so that its output pass
+ * gives every CU a workgroup, see gdn_chunk_fwd_auto_span_chunks) when the
+ * workspace holds gdn_chunk_fwd_workspace_bytes(...) for these sizes, which then
+ * includes room for it; the results equal the plain scan's up to rounding.  gdn_chunk_fwd_profiled and gdn_chunk_fwd_noalloc
+ * always run the plain scan.
  * Errors: GDN_ERR_NULL (q, k, v, beta, O or workspace NULL), GDN_ERR_SHAPE
  * (B, H < 1, T < 0, n_seqs < 1 or B != 1 with cu_seqlens, more than 2^31-1
  * elements in a tensor, C * H * max(Dk, Dv) * element size above 2^31-1 bytes,
@@ -155,6 +163,50 @@ gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
                                  void *O, float *S_T,
                                  int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
                                  void *stream);
+
+/* gdn_chunk_fwd of a fixed-length batch with each sequence split into spans of
+ * span_chunks chunks, for long sequences with few (sequence, head) units, where
+ * one workgroup per state slice walking the whole sequence leaves most of the
+ * GPU idle.  Over a span the state map is affine and the same for every row of
+ * S: S_out = S_in M + b (the Qiita article on the Linear Attention lineage,
+ * section "Gated-DeltaNet": the state after i tokens is an affine function of
+ * S_0, gamma_i S_0 (I - W K^T) + sum (gamma_i / gamma_s) u_s k_s^T; section
+ * "Chunk Computation": each chunk starts from the last state of the one before).
+ * Three passes:
+ *   1. every span's (M, b): the scan of the span with Dk extra state rows that
+ *      start at the identity and take zero values (they end as M) next to the
+ *      Dv rows from zero (they end as b);
+ *   2. per sequence, in span order: S_in(0) = S0, S_in(p+1) = S_in(p) M_p + b_p,
+ *      S_T = S_in(last + 1) (fp32);
+ *   3. every span's outputs from its start state S_in(p).
+ * The result equals gdn_chunk_fwd's up to rounding (passes 1 and 3 run the
+ * same chunk arithmetic; pass 2 is an fp32 product).  Passes 1 and 3 hold
+ * (Dk + 2 Dv) / Dv times the state columns of one plain scan, spread over the
+ * spans in parallel: it pays when B H Dv / 16 is well below the CU count.
+ * Arguments as gdn_chunk_fwd for a fixed-length batch (no cu_seqlens), plus:
+ *  span_chunks  chunks per span (>= 1); the last span of a sequence may be
+ *               shorter;
+ *  workspace    at least gdn_chunk_fwd_split_workspace_bytes(...) bytes;
+ *  kernel_ms    NULL, or a HOST array of 4 floats: then the call BLOCKS and
+ *               returns the device milliseconds of [prep, pass 1, pass 2, pass 3].
+ * Compiled for bf16, Dk = Dv = 128, C = 64 only (GDN_ERR_UNSUPPORTED
+ * otherwise).  Errors: as gdn_chunk_fwd; GDN_ERR_SHAPE also for span_chunks < 1
+ * or more than 65535 spans in the batch. */
+size_t gdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
+                                           int span_chunks, gdn_dtype dt);
+/* Span length in chunks that gdn_chunk_fwd splits a call of these sizes into
+ * on the current device (the policy in gdn_chunk_fwd's description: spans of
+ * ceil(chunks / P), P = min(CUs / (B H Dv / 32), chunks / 8)), or 0 when it runs
+ * the plain scan (also for sizes gdn_chunk_fwd rejects).  n_seqs > 0 (a packed
+ * batch) always gives 0. */
+int gdn_chunk_fwd_auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C, int n_seqs,
+                                   gdn_dtype dt);
+gdn_status gdn_chunk_fwd_split(const void *q, const void *k, const void *v,
+                               const float *log_alpha, const float *beta, const float *S0,
+                               void *O, float *S_T,
+                               int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt,
+                               int span_chunks, void *workspace, size_t workspace_bytes,
+                               void *stream, float *kernel_ms);
 
 /* Measurement variant of gdn_chunk_fwd: same arguments and result, plus
  * kernel_ms, a HOST array of 4 floats that receives the device time in

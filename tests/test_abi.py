@@ -181,6 +181,52 @@ def test_noalloc_argument_errors(lib):
     assert "scratch" in lib.gdn_status_string(GDN_ERR_SCRATCH_LIMIT).decode()
 
 
+def test_workspace_holds_the_automatic_split(lib):
+    # few long units (B1 H2 T8192, bf16 D128): gdn_chunk_fwd's workspace query
+    # is the split scan's (with the 256 CUs assumed when no device answers:
+    # 256 / (2 x 4) = 32 spans, capped at 128 / 8 = 16, of 8 chunks), equal to
+    # gdn_chunk_fwd_split_workspace_bytes with that span length; many units
+    # (B4 H16): the plain query, below any split's
+    few = lib.gdn_chunk_fwd_workspace_bytes(1, 8192, 2, 128, 128, 64, 0, BF16)
+    assert few == lib.gdn_chunk_fwd_split_workspace_bytes(1, 8192, 2, 128, 128, 64, 8, BF16)
+    assert few >= 16 * 2 * (256 + 128) * 128 * 4
+    many = lib.gdn_chunk_fwd_workspace_bytes(4, 4096, 16, 128, 128, 64, 0, BF16)
+    assert many < lib.gdn_chunk_fwd_split_workspace_bytes(4, 4096, 16, 128, 128, 64, 64, BF16)
+    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 8192, 2, 128, 128, 64, 0, BF16) == 8
+    assert lib.gdn_chunk_fwd_auto_span_chunks(4, 4096, 16, 128, 128, 64, 0, BF16) == 0
+    # 16 heads of 512 chunks: 64 workgroups, 4 spans of 128 chunks; 32 heads: none
+    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 32768, 16, 128, 128, 64, 0, BF16) == 128
+    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 32768, 32, 128, 128, 64, 0, BF16) == 0
+    # fewer than 32 chunks: none
+    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 31 * 64, 1, 128, 128, 64, 0, BF16) == 0
+    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 8192, 2, 128, 128, 64, 3, BF16) == 0
+    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 8192, 2, 128, 128, 64, 0, F32) == 0
+    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 8192, 2, 100, 128, 64, 0, BF16) == 0
+    # the scalar-gate and per-channel rules never split
+    assert lib.gdn_rule_workspace_bytes(1, 1, 8192, 2, 128, 128, 64, 0, BF16) < few
+
+
+def test_split_queries_and_errors(lib):
+    f = lib.gdn_chunk_fwd_split_workspace_bytes
+    n = f(1, 32768, 32, 128, 128, 64, 64, BF16)
+    # prep's per-chunk data, the span maps [8 spans][32][256][128] and the span
+    # starts [8][32][128][128], fp32
+    assert n >= 8 * 32 * 256 * 128 * 4 + 8 * 32 * 128 * 128 * 4
+    assert f(1, 32768, 32, 64, 64, 64, 64, F32) == 0          # compiled for bf16 D128 only
+    assert f(1, 32768, 32, 128, 128, 64, 0, BF16) == 0        # span_chunks >= 1
+    p = ctypes.c_void_p(1 << 20)
+    g = lib.gdn_chunk_fwd_split
+    args = [p, p, p, None, p, None, p, None, 1, 128, 1, 128, 128, 64, BF16, 1, p, 1 << 40, None, None]
+    bad = list(args); bad[0] = None
+    assert g(*bad) == GDN_ERR_NULL
+    bad = list(args); bad[15] = 0
+    assert g(*bad) == GDN_ERR_SHAPE
+    bad = list(args); bad[14] = F32
+    assert g(*bad) == GDN_ERR_UNSUPPORTED
+    bad = list(args); bad[17] = 16
+    assert g(*bad) == GDN_ERR_WORKSPACE
+
+
 def test_recurrent_step_argument_errors(lib):
     p = ctypes.c_void_p(1 << 20)
     f = lib.gdn_recurrent_step
