@@ -63,7 +63,7 @@ struct FwdArgs {
 // Workspace regions, in order; every region starts on a 256-byte boundary.
 struct Layout {
     int64_t slots, N;
-    size_t g, Tb, qt, kh, bounds, seq_slot, table, total;
+    size_t g, Tb, qt, kh, bounds, seq_slot, table, order, total;
 };
 
 Layout make_layout(int rule, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_t Dv, int64_t C,
@@ -87,6 +87,7 @@ Layout make_layout(int rule, int64_t B, int64_t T, int64_t H, int64_t Dk, int64_
         L.bounds = take((size_t)(n_seqs + 1) * sizeof(int));
         L.seq_slot = take((size_t)(n_seqs + 1) * sizeof(int));
         L.table = take((size_t)L.slots * 4 * sizeof(int));
+        L.order = take((size_t)n_seqs * sizeof(int));
     }
     L.total = off;
     return L;
@@ -202,14 +203,16 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         int* bounds = reinterpret_cast<int*>(a.ws + L.bounds);
         int* seq_slot = reinterpret_cast<int*>(a.ws + L.seq_slot);
         int* table = reinterpret_cast<int*>(a.ws + L.table);
+        int* order = reinterpret_cast<int*>(a.ws + L.order);
         tm->mark(a.stream);
         hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(kTableThreads), 0, a.stream,
-                           a.cu, a.n_seqs, a.T, C, (int)L.slots, bounds, seq_slot, table);
+                           a.cu, a.n_seqs, a.T, C, (int)L.slots, bounds, seq_slot, table, order);
         if (gdn_status s = check_launch(a.stream)) return s;
         tm->mark(a.stream);
         geom.table = table;
         geom.seq_slot = seq_slot;
         geom.bounds = bounds;
+        geom.order = order;
     }
     const T* q = static_cast<const T*>(a.q);
     const T* k = static_cast<const T*>(a.k);

@@ -143,6 +143,8 @@ struct SeqGeom {
     const int* table;        // varlen: [slots][4] = {seq, t0, len, pad}; NULL for fixed length
     const int* seq_slot;     // varlen: [N+1] first slot of each sequence
     const int* bounds;       // varlen: [N+1] clamped token offsets of the sequences
+    const int* order;        // varlen: [N] sequences by chunk count, longest first (the
+                             // scan's dispatch order); NULL: in index order
     int T;                   // fixed: tokens per sequence
     int chunks_per_seq;      // fixed: ceil(T / C)
     int C;

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         }
         v0 = vs * DVT;
         h = u % H;
-        seq = u / H;
+        seq = geom.order ? geom.order[u / H] : u / H;   // packed batches: longest first
     }
     const int l = lane_id(), w = wave_id();
     const int n = l & 15, g4 = 4 * (l >> 4);

@@ -121,11 +121,21 @@ __device__ __forceinline__ int block_scan(int x, int* wsum) {
     return x;
 }
 
+// Order of the sequences for the scan, by chunk count, longest first: a
+// counting sort over kOrderBins bins (counts of kOrderBins - 1 chunks and more
+// share the first bin); equal counts in no fixed order.  With the longest
+// sequences' workgroups dispatched first, a CU that frees up takes shorter
+// work last, which shortens the scan's makespan over a mixed batch.
+constexpr int kOrderBins = 4096;
+static_assert(kOrderBins % kTableThreads == 0, "bins per thread");
+
 __global__ __launch_bounds__(kTableThreads) void gdn_chunk_table_kernel(
     const int* __restrict__ cu, int n_seqs, int T, int C, int max_slots,
-    int* __restrict__ bounds, int* __restrict__ seq_slot, int* __restrict__ table) {
+    int* __restrict__ bounds, int* __restrict__ seq_slot, int* __restrict__ table,
+    int* __restrict__ order) {
     __shared__ int wsum[kTableThreads / 64];
     __shared__ int carry;
+    __shared__ int bins[kOrderBins];
     const int tid = threadIdx.x;
     // phase 1: running max of cu, clamped to [0, T] (values are >= 0, so 0 is
     // the identity of the max)
@@ -177,6 +187,30 @@ __global__ __launch_bounds__(kTableThreads) void gdn_chunk_table_kernel(
         const int len = (bounds[lo + 1] - st) < C ? (bounds[lo + 1] - st) : C;
         tab[s] = make_int4(lo, st, len, 0);
     }
+    // phase 4: order, longest first.  Bin b holds the sequences of
+    // kOrderBins - 1 - b chunks (the first bin also longer ones).
+    constexpr int BPT = kOrderBins / kTableThreads;
+    auto bin_of = [&](int i) {
+        const int cnt = seq_slot[i + 1] - seq_slot[i];
+        return kOrderBins - 1 - (cnt < kOrderBins - 1 ? cnt : kOrderBins - 1);
+    };
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) bins[tid * BPT + j] = 0;
+    __syncthreads();
+    for (int i = tid; i < n_seqs; i += kTableThreads) atomicAdd(&bins[bin_of(i)], 1);
+    __syncthreads();
+    // exclusive prefix sum over the bins (thread tid owns BPT consecutive ones)
+    int loc[BPT], sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        loc[j] = sum;
+        sum += bins[tid * BPT + j];
+    }
+    const int before = block_scan<false>(sum, wsum) - sum;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) bins[tid * BPT + j] = before + loc[j];   // first position of the bin
+    __syncthreads();
+    for (int i = tid; i < n_seqs; i += kTableThreads) order[atomicAdd(&bins[bin_of(i)], 1)] = i;
 }
 
 }  // namespace gdn
