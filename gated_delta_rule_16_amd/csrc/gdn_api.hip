@@ -277,7 +277,7 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
 // chunks; (1) the scan of every span from identity rows gives its map (M, b),
 // (2) gdn_span_chain_kernel chains the maps into each span's start state,
 // (3) the scan of every span from its start state writes O.  Compiled for
-// bf16 Dk = Dv = 128, C = 64 (the first pass runs the Dv = 256 scan).
+// the shapes of kSplitVariants.
 // ---------------------------------------------------------------------------
 struct SplitLayout {
     int64_t P, slots;
@@ -355,6 +355,25 @@ gdn_status launch_split(const FwdArgs& a, int L, KernelTimer* tm) {
                                              static_cast<T*>(a.O), nullptr, ScanRows{0, DV}, a.stream, tm);
 }
 
+// compiled instantiations of the split scan (the first pass runs the scan
+// with Dk + Dv state columns)
+typedef gdn_status (*SplitFn)(const FwdArgs&, int, KernelTimer*);
+struct SplitVariant {
+    int dk, dv, c;
+    gdn_dtype dt;
+    SplitFn fn;
+};
+const SplitVariant kSplitVariants[] = {
+    {64, 64, 64, GDN_F32, launch_split<float, 64, 64, 64>},
+    {128, 128, 64, GDN_F32, launch_split<float, 128, 128, 64>},
+    {128, 128, 64, GDN_BF16, launch_split<bf16, 128, 128, 64>},
+};
+const SplitVariant* find_split(int dk, int dv, int c, gdn_dtype dt) {
+    for (const SplitVariant& v : kSplitVariants)
+        if (v.dk == dk && v.dv == dv && v.c == c && v.dt == dt) return &v;
+    return nullptr;
+}
+
 typedef gdn_status (*FwdFn)(const FwdArgs&, KernelTimer*);
 struct Variant {
     int dk, dv, c;
@@ -430,27 +449,63 @@ gdn_status check_sizes(int rule, int B, int T, int H, int Dk, int Dv, int C, boo
     return GDN_OK;
 }
 
-// Span length of gdn_chunk_fwd's automatic split (0: no split).  The plain
-// scan runs one workgroup per 32 state columns of each (sequence, head) unit,
-// B H Dv / 32 in all, each walking the whole sequence; with few units most CUs
-// idle.  The split costs about three scans' work (pass 1 carries Dk + Dv state
-// rows, pass 3 Dv) spread over P times the workgroups.  Measured on bf16
-// Dk = Dv = 128, T = 32768 (512 chunks), plain -> split: 4 heads 0.51 -> 0.17 ms,
-// 8 heads 0.53 -> 0.25 ms, 16 heads 0.58 -> 0.47 ms, 32 heads 0.72 -> 0.94 ms.
-// So: split when the plain scan's workgroups fill at most a quarter of the CUs
-// and sequences have at least 32 chunks, into P = CUs / workgroups spans (the
-// output pass then has a workgroup per CU), spans of at least 8 chunks.
+// Span length of gdn_chunk_fwd's automatic split (0: no split), from a cost
+// model of the two paths with per-step costs measured on MI355X.  The plain
+// scan runs each (sequence, head) unit's chunks one after another, so with few
+// units most CUs idle; the split runs three kernels more (the span maps over
+// Dk + Dv state columns, the chain of the maps, the output pass) over P times
+// the workgroups:
+//   plain    = f + chunks * s_plain
+//   split(P) = 3 f + L (s1 r1 + s3 r3) + P (c0 + c1 units),  L = ceil(chunks / P),
+// with r1, r3 the rounds of workgroups each pass needs on the device (32-column
+// slices where they fill it, else 16-column ones) and f a kernel's fixed
+// cost.  The split is taken at the best P when it is under 0.95 of the plain
+// estimate.  Measured (ms per call, plain -> split at the chosen span length):
+// bf16 D128 T = 32768: 4 heads 0.51 -> 0.17, 8 heads 0.53 -> 0.25, 16 heads
+// 0.58 -> 0.47, 32 heads 0.72 (split 0.94: not taken); 4 heads T = 4096 0.085 ->
+// 0.067; 16 heads T = 2048 0.057 (split 0.073: not taken); fp32 D64 B2 H4
+// T = 1024 0.078 -> 0.055.  Packed batches always run the plain scan.
+struct SplitModel {
+    int dk, dv, c;
+    gdn_dtype dt;
+    double s_plain, s1, s3, c0, c1;   // microseconds
+};
+const SplitModel kSplitModels[] = {
+    {128, 128, 64, GDN_BF16, 1.05, 0.95, 1.40, 2.5, 0.18},
+    {64, 64, 64, GDN_F32, 3.30, 4.00, 4.00, 0.8, 0.04},
+};
+constexpr double kKernelFixedUs = 6.0;
+
 int auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt, bool varlen) {
-    if (varlen || dt != GDN_BF16 || Dk != 128 || Dv != 128 || C != 64 || T <= 0) return 0;
+    if (varlen || T <= 0) return 0;
+    const SplitModel* m = nullptr;
+    for (const SplitModel& x : kSplitModels)
+        if (x.dk == Dk && x.dv == Dv && x.c == C && x.dt == dt) m = &x;
+    if (!m || !find_split(Dk, Dv, C, dt)) return 0;
     const int64_t cps = ((int64_t)T + C - 1) / C;
     const int64_t cus = device_cu_count();
     const int64_t units = (int64_t)B * H;
-    const int64_t wgs = units * (Dv / 32);   // workgroups of the plain scan
-    if (cps < 32 || wgs * 4 > cus) return 0;
-    int64_t P = cus / wgs;
-    if (P > cps / 8) P = cps / 8;
-    if (P < 2) return 0;
-    return (int)((cps + P - 1) / P);
+    if (cps < 2 || units * (Dv / 16) > cus) return 0;   // the plain scan already fills the device
+    const double plain = kKernelFixedUs + (double)cps * m->s_plain;
+    auto rounds = [&](int64_t n, int cols) {   // workgroup rounds of a pass over n span-units
+        const int64_t w32 = n * cols / 32;
+        const int64_t w = w32 >= cus ? w32 : n * cols / 16;
+        return (double)((w + cus - 1) / cus);
+    };
+    double best = 0.95 * plain;
+    int best_l = 0;
+    for (int64_t P = 2; P <= cps && P <= 64; ++P) {
+        const int64_t L = (cps + P - 1) / P, Pe = (cps + L - 1) / L;
+        const int64_t n = units * Pe;
+        if ((int64_t)B * Pe > 65535) break;   // spans of the batch: the scan grid's third dimension
+        const double cost = 3 * kKernelFixedUs + (double)L * (m->s1 * rounds(n, Dk + Dv) + m->s3 * rounds(n, Dv)) +
+                            (double)Pe * (m->c0 + m->c1 * (double)units);
+        if (cost < best) {
+            best = cost;
+            best_l = (int)L;
+        }
+    }
+    return best_l;
 }
 
 }  // namespace
@@ -563,7 +618,7 @@ gdn_status chunk_fwd_impl(int rule, const void* q, const void* k, const void* v,
     if (rule == GDN_RULE_DELTA && !use_scratch && !tm->on) {
         const int Ls = auto_span_chunks(B, T, H, Dk, Dv, C, dt, varlen);
         if (Ls > 0 && workspace_bytes >= make_split_layout(B, T, H, Dk, Dv, C, Ls, elem_size(dt)).total)
-            return launch_split<bf16, 128, 128, 64>(a, Ls, tm);
+            return find_split(Dk, Dv, C, dt)->fn(a, Ls, tm);
     }
     return find_variant(rule, Dk, Dv, C, dt)->fn(a, tm);
 }
@@ -685,7 +740,7 @@ extern "C" gdn_status gdn_rule_chunk_fwd_profiled(gdn_rule rule, const void* q, 
 namespace {
 gdn_status check_split(int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt, int span_chunks) {
     if (gdn_status s = check_sizes(GDN_RULE_DELTA, B, T, H, Dk, Dv, C, false, 0, dt)) return s;
-    if (Dk != 128 || Dv != 128 || C != 64 || dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!find_split(Dk, Dv, C, dt)) return GDN_ERR_UNSUPPORTED;
     if (span_chunks < 1) return GDN_ERR_SHAPE;
     const SplitLayout S = make_split_layout(B, T, H, Dk, Dv, C, span_chunks, elem_size(dt));
     // the span maps, [B P][H][Dk + Dv][Dk], and the span grid
@@ -731,7 +786,7 @@ extern "C" gdn_status gdn_chunk_fwd_split(const void* q, const void* k, const vo
             }
         }
         (void)hipGetLastError();
-        gdn_status s = launch_split<bf16, 128, 128, 64>(a, span_chunks, &tm);
+        gdn_status s = find_split(Dk, Dv, C, dt)->fn(a, span_chunks, &tm);
         if (tm.on) {
             // marks: prep, pass 1, chain, pass 3
             if (s == GDN_OK && hipEventSynchronize(tm.ev[tm.n - 1]) != hipSuccess) s = GDN_ERR_HIP;

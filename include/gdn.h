@@ -116,14 +116,15 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
  *  stream      hipStream_t to enqueue on.
  * With T = 0 nothing but S_T = S0 is computed and q, k, v, beta, O (and the
  * workspace, whose required size may then be 0) may be NULL.
- * Long sequences with few units: for a fixed-length bf16 batch with
- * Dk = Dv = 128, C = 64, at least 32 chunks per sequence and B H Dv / 32 (the
- * plain scan's workgroups) at most a quarter of the device's CUs, the call runs
- * the split scan of gdn_chunk_fwd_split (spans sized so that its output pass
- * gives every CU a workgroup, see gdn_chunk_fwd_auto_span_chunks) when the
- * workspace holds gdn_chunk_fwd_workspace_bytes(...) for these sizes, which then
- * includes room for it; the results equal the plain scan's up to rounding.  gdn_chunk_fwd_profiled and gdn_chunk_fwd_noalloc
- * always run the plain scan.
+ * Long sequences with few units: for a fixed-length batch of bf16 with
+ * Dk = Dv = 128 or fp32 with Dk = Dv = 64 (C = 64), where the plain scan leaves
+ * most CUs idle and a cost model of the two paths (per-step costs measured on
+ * MI355X) puts the split scan of gdn_chunk_fwd_split under 0.95 of the plain
+ * one, the call runs that split scan, with the span length
+ * gdn_chunk_fwd_auto_span_chunks reports, when the workspace holds
+ * gdn_chunk_fwd_workspace_bytes(...) for these sizes, which then includes room
+ * for it; the results equal the plain scan's up to rounding.
+ * gdn_chunk_fwd_profiled and gdn_chunk_fwd_noalloc always run the plain scan.
  * Errors: GDN_ERR_NULL (q, k, v, beta, O or workspace NULL), GDN_ERR_SHAPE
  * (B, H < 1, T < 0, n_seqs < 1 or B != 1 with cu_seqlens, more than 2^31-1
  * elements in a tensor, C * H * max(Dk, Dv) * element size above 2^31-1 bytes,
@@ -189,16 +190,15 @@ gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
  *  workspace    at least gdn_chunk_fwd_split_workspace_bytes(...) bytes;
  *  kernel_ms    NULL, or a HOST array of 4 floats: then the call BLOCKS and
  *               returns the device milliseconds of [prep, pass 1, pass 2, pass 3].
- * Compiled for bf16, Dk = Dv = 128, C = 64 only (GDN_ERR_UNSUPPORTED
- * otherwise).  Errors: as gdn_chunk_fwd; GDN_ERR_SHAPE also for span_chunks < 1
- * or more than 65535 spans in the batch. */
+ * Compiled for C = 64 with bf16 Dk = Dv = 128, fp32 Dk = Dv = 64 and fp32
+ * Dk = Dv = 128 (GDN_ERR_UNSUPPORTED otherwise).  Errors: as gdn_chunk_fwd;
+ * GDN_ERR_SHAPE also for span_chunks < 1 or more than 65535 spans in the batch. */
 size_t gdn_chunk_fwd_split_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
                                            int span_chunks, gdn_dtype dt);
 /* Span length in chunks that gdn_chunk_fwd splits a call of these sizes into
- * on the current device (the policy in gdn_chunk_fwd's description: spans of
- * ceil(chunks / P), P = min(CUs / (B H Dv / 32), chunks / 8)), or 0 when it runs
- * the plain scan (also for sizes gdn_chunk_fwd rejects).  n_seqs > 0 (a packed
- * batch) always gives 0. */
+ * on the current device (the cost model in gdn_chunk_fwd's description), or 0
+ * when it runs the plain scan (also for sizes gdn_chunk_fwd rejects).
+ * n_seqs > 0 (a packed batch) always gives 0. */
 int gdn_chunk_fwd_auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C, int n_seqs,
                                    gdn_dtype dt);
 gdn_status gdn_chunk_fwd_split(const void *q, const void *k, const void *v,

@@ -182,26 +182,34 @@ def test_noalloc_argument_errors(lib):
 
 
 def test_workspace_holds_the_automatic_split(lib):
-    # few long units (B1 H2 T8192, bf16 D128): gdn_chunk_fwd's workspace query
-    # is the split scan's (with the 256 CUs assumed when no device answers:
-    # 256 / (2 x 4) = 32 spans, capped at 128 / 8 = 16, of 8 chunks), equal to
-    # gdn_chunk_fwd_split_workspace_bytes with that span length; many units
-    # (B4 H16): the plain query, below any split's
+    # The automatic split's choices on a device of 256 CUs (the count assumed
+    # when no device answers), from the cost model in gdn_api.hip: few long
+    # units split, into the span lengths measured best; many units, or
+    # sequences too short for the three extra kernels to pay, do not
+    auto = lib.gdn_chunk_fwd_auto_span_chunks
+    assert auto(1, 32768, 4, 128, 128, 64, 0, BF16) == 32
+    assert auto(1, 32768, 8, 128, 128, 64, 0, BF16) == 64
+    assert auto(1, 32768, 16, 128, 128, 64, 0, BF16) == 128
+    assert auto(1, 4096, 4, 128, 128, 64, 0, BF16) == 8
+    assert auto(1, 32768, 32, 128, 128, 64, 0, BF16) == 0      # every CU busy
+    assert auto(4, 4096, 16, 128, 128, 64, 0, BF16) == 0       # the headline workload
+    assert auto(1, 2048, 16, 128, 128, 64, 0, BF16) == 0       # 32 chunks, 16 heads
+    assert auto(2, 1024, 4, 64, 64, 64, 0, F32) == 2           # the fp32 D64 workload
+    assert auto(1, 2048, 32, 64, 64, 64, 0, F32) == 0
+    assert auto(1, 8192, 2, 128, 128, 64, 3, BF16) == 0        # packed batches never split
+    assert auto(1, 8192, 2, 128, 128, 64, 0, F32) == 0         # fp32 D128: no model, never automatic
+    assert auto(1, 8192, 2, 100, 128, 64, 0, BF16) == 0        # unsupported sizes
+    # gdn_chunk_fwd's workspace query is then the split scan's, equal to
+    # gdn_chunk_fwd_split_workspace_bytes with that span length; otherwise the
+    # plain layout, below any split's
+    L = auto(1, 8192, 2, 128, 128, 64, 0, BF16)
+    assert L > 0
     few = lib.gdn_chunk_fwd_workspace_bytes(1, 8192, 2, 128, 128, 64, 0, BF16)
-    assert few == lib.gdn_chunk_fwd_split_workspace_bytes(1, 8192, 2, 128, 128, 64, 8, BF16)
-    assert few >= 16 * 2 * (256 + 128) * 128 * 4
+    assert few == lib.gdn_chunk_fwd_split_workspace_bytes(1, 8192, 2, 128, 128, 64, L, BF16)
+    P = -(-128 // L)
+    assert few >= P * 2 * (256 + 128) * 128 * 4                 # span maps and starts, fp32
     many = lib.gdn_chunk_fwd_workspace_bytes(4, 4096, 16, 128, 128, 64, 0, BF16)
     assert many < lib.gdn_chunk_fwd_split_workspace_bytes(4, 4096, 16, 128, 128, 64, 64, BF16)
-    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 8192, 2, 128, 128, 64, 0, BF16) == 8
-    assert lib.gdn_chunk_fwd_auto_span_chunks(4, 4096, 16, 128, 128, 64, 0, BF16) == 0
-    # 16 heads of 512 chunks: 64 workgroups, 4 spans of 128 chunks; 32 heads: none
-    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 32768, 16, 128, 128, 64, 0, BF16) == 128
-    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 32768, 32, 128, 128, 64, 0, BF16) == 0
-    # fewer than 32 chunks: none
-    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 31 * 64, 1, 128, 128, 64, 0, BF16) == 0
-    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 8192, 2, 128, 128, 64, 3, BF16) == 0
-    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 8192, 2, 128, 128, 64, 0, F32) == 0
-    assert lib.gdn_chunk_fwd_auto_span_chunks(1, 8192, 2, 100, 128, 64, 0, BF16) == 0
     # the scalar-gate and per-channel rules never split
     assert lib.gdn_rule_workspace_bytes(1, 1, 8192, 2, 128, 128, 64, 0, BF16) < few
 
@@ -212,7 +220,10 @@ def test_split_queries_and_errors(lib):
     # prep's per-chunk data, the span maps [8 spans][32][256][128] and the span
     # starts [8][32][128][128], fp32
     assert n >= 8 * 32 * 256 * 128 * 4 + 8 * 32 * 128 * 128 * 4
-    assert f(1, 32768, 32, 64, 64, 64, 64, F32) == 0          # compiled for bf16 D128 only
+    assert f(1, 32768, 32, 64, 64, 64, 64, F32) > 0           # fp32 Dk = Dv = 64, C = 64
+    assert f(1, 32768, 32, 128, 128, 64, 64, F32) > 0         # fp32 Dk = Dv = 128
+    assert f(1, 32768, 32, 128, 256, 64, 64, BF16) == 0       # not compiled: Dv = 256
+    assert f(1, 32768, 32, 64, 64, 16, 64, F32) == 0          # not compiled: C = 16
     assert f(1, 32768, 32, 128, 128, 64, 0, BF16) == 0        # span_chunks >= 1
     p = ctypes.c_void_p(1 << 20)
     g = lib.gdn_chunk_fwd_split
@@ -221,7 +232,7 @@ def test_split_queries_and_errors(lib):
     assert g(*bad) == GDN_ERR_NULL
     bad = list(args); bad[15] = 0
     assert g(*bad) == GDN_ERR_SHAPE
-    bad = list(args); bad[14] = F32
+    bad = list(args); bad[12] = 256
     assert g(*bad) == GDN_ERR_UNSUPPORTED
     bad = list(args); bad[17] = 16
     assert g(*bad) == GDN_ERR_WORKSPACE

@@ -95,6 +95,19 @@ def test_workload_gdn_f32_b2_h4_t1024_d64():
     check(workload_inputs("gdn_f32_b2_h4_t1024_d64"), "f32", tag="workload 2")
 
 
+def test_workload_gdn_f32_b2_h4_t1024_d64_plain_scan():
+    # gdn_chunk_fwd splits this workload (few units); the plain scan on the same
+    # inputs through the profiled call, which always runs it
+    inp = workload_inputs("gdn_f32_b2_h4_t1024_d64")
+    d = inp.to(DEV)
+    O, S, _ = gdn.gdn_chunk_fwd_profiled(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0)
+    torch.cuda.synchronize()
+    Or, Sr = run_oracle(inp)
+    eo, es = rel(O.double().cpu().numpy(), Or), rel(S.double().cpu().numpy(), Sr)
+    say(f"      workload 2, plain scan: max rel err O {eo:.3e}  S_T {es:.3e}")
+    assert eo <= TOL["f32"] and es <= TOL["f32"], (eo, es)
+
+
 def test_workload_gdn_bf16_b4_h16_t4096_d128():
     check(workload_inputs("gdn_bf16_b4_h16_t4096_d128"), "bf16", tag="workload 3")
 
