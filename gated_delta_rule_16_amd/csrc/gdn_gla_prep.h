@@ -30,6 +30,12 @@
 // is the decay across the block; while it stays below e^64 on every channel
 // the same product is used, else that block is formed term by term (exact for
 // any gate, slow; only extreme gates take it).
+// Whole-chunk fast path.  When every channel decays by less than e^64 over the
+// whole chunk (b_n > -64), e^{b_id - b_sd} = e^{b_id} e^{-b_sd} with both
+// factors between e^-64 and e^64, so P = Q~ K'^T with K' = K o e^{-b}: each
+// tile is one MFMA chain over the operands as they are, with no per-tile
+// scaling, and K^ = diag(beta) K' diag(e^{b_n}).  Chunks with a stronger decay
+// on some channel take the blocked form above.
 // Padding: rows past the chunk end act as tokens with q = k = 0, beta = 0,
 // log alpha = 0.
 #pragma once
@@ -50,6 +56,8 @@ struct GlaPrepCfg {
     static constexpr int PARTS = THREADS / DK;             // cumsum: token ranges per channel
     static constexpr int TPP = C / PARTS;                  // tokens per range
     static constexpr float kMaxDiagLog = 64.f;             // diagonal fast path: c_II < e^64
+    static constexpr float kMaxChunkLog = 64.f;            // whole-chunk fast path: -b_n < 64
+    static constexpr int FLAG_SLOW_CHUNK = 15;             // sflag slot: the chunk takes the blocked form
     // LDS: b [C][LB] fp32; Q^, K~ [C][DK] in T; c_IJ [NPAIR][DK], e^{b_16I} and
     // e^{b_n - b_eI} [NB][DK] fp32; beta [C]; per-block slow-path flags
     static constexpr int LB = DK + 4;                      // b row pitch (floats)
@@ -171,6 +179,48 @@ __global__ __launch_bounds__(256, 2) void gdn_gla_prep_kernel(
                 __syncthreads();
             }
 
+            // ---- the path: fast unless some channel decays by e^64 or more
+            if (tid < DK && !(sb[(C - 1) * LB + tid] > -Cfg::kMaxChunkLog)) sflag[Cfg::FLAG_SLOW_CHUNK] = 1;
+            __syncthreads();
+        }
+        const bool fast = len > 0 && sflag[Cfg::FLAG_SLOW_CHUNK] == 0;   // (uniform)
+        if (fast) {
+            // ---- e^{b_n} per channel, then Q~, K^ out (valid rows), Q~ and K' into LDS
+            for (int d = tid; d < DK; d += Cfg::THREADS) {
+                const float en = __expf(sb[(C - 1) * LB + d]);
+                ses[d] = en;
+                bn_ws[(int64_t)u * DK + d] = en;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int x = tid + j * Cfg::THREADS, i = x / (DK / EV), d0 = (x % (DK / EV)) * EV;
+                if (x >= NPC) break;
+                const T* qp = reinterpret_cast<const T*>(&qv[j]);
+                const T* kp = reinterpret_cast<const T*>(&kv[j]);
+                T qo[EV], ko[EV], kq[EV];
+                const float be = sbeta[i];
+#pragma unroll
+                for (int e = 0; e < EV; ++e) {
+                    const int d = d0 + e;
+                    const float bi = sb[i * LB + d];
+                    const float qt = to_f32(qp[e]) * __expf(bi);     // q e^{b_i}
+                    const float kq_ = to_f32(kp[e]) * __expf(-bi);   // k e^{-b_i} (< e^64 |k|)
+                    qo[e] = from_f32<T>(qt);
+                    kq[e] = from_f32<T>(kq_);
+                    ko[e] = from_f32<T>(be * kq_ * ses[d]);          // beta k e^{b_n - b_i}
+                }
+                *reinterpret_cast<u32x4*>(sqh + i * LQ + d0) = *reinterpret_cast<const u32x4*>(qo);
+                *reinterpret_cast<u32x4*>(skt + i * LQ + d0) = *reinterpret_cast<const u32x4*>(kq);
+                if (i < len) {
+                    *reinterpret_cast<u32x4*>(qt_ws + (row0 * DK + (int64_t)i * rs + d0)) =
+                        *reinterpret_cast<const u32x4*>(qo);
+                    *reinterpret_cast<u32x4*>(kh_ws + (row0 * DK + (int64_t)i * rs + d0)) =
+                        *reinterpret_cast<const u32x4*>(ko);
+                }
+            }
+            __syncthreads();
+        } else if (len > 0) {
             // ---- per-channel block factors: e^{b_16I}, e^{b_n - b_eI}, c_IJ, e^{b_n};
             // diagonal blocks whose decay reaches e^64 on some channel take the slow path
             for (int x = tid; x < DK * (2 * NB + Cfg::NPAIR + 1); x += Cfg::THREADS) {
@@ -238,8 +288,26 @@ __global__ __launch_bounds__(256, 2) void gdn_gla_prep_kernel(
             auto tile = [&](int I, int J) __attribute__((always_inline)) -> f32x4 {
                 if (J > I) return zero4();
                 f32x4 acc = zero4();
-                const bool slow = J == I && sflag[I] != 0;
-                if (!slow) {
+                const bool slow = !fast && J == I && sflag[I] != 0;
+                if (fast) {
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) {
+                        Frag a, b;
+                        if constexpr (Cfg::BF) {
+                            const int dd = kk * KS + g * EV;
+                            a = *reinterpret_cast<const Frag*>(skt + (16 * J + n) * LQ + dd);
+                            b = *reinterpret_cast<const Frag*>(sqh + (16 * I + n) * LQ + dd);
+                        } else {
+                            const int d4 = kk * KS + 4 * g;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                a[r] = skt[(16 * J + n) * LQ + d4 + r];
+                                b[r] = sqh[(16 * I + n) * LQ + d4 + r];
+                            }
+                        }
+                        acc = St::mma(a, b, acc);
+                    }
+                } else if (!slow) {
                     const float* cp = sc + gla_pair(I, J) * DK;
 #pragma unroll
                     for (int kk = 0; kk < NKK; ++kk) {

@@ -105,12 +105,17 @@ def test_gla_equal_channels_match_scalar_rule(dtype, D):
     assert rel(S1, S2.double().cpu().numpy()) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("case", ["decay30", "resets", "mixed_channels"])
+@pytest.mark.parametrize("case", ["decay30", "resets", "mixed_channels", "chunk_decay_61",
+                                  "chunk_decay_67"])
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
 def test_gla_degenerate_gates(case, dtype, D):
     # decay30: log alpha = -30 on every channel and token (every diagonal block
     # of P~ takes the term-by-term path); resets: -80 every 37 tokens on every
-    # channel; mixed: half the channels at -30, the others drawn
+    # channel; mixed: half the channels at -30, the others drawn;
+    # chunk_decay_61 / _67: -0.95 / -1.05 on every channel and token, a decay of
+    # e^-60.8 / e^-67.2 over a 64-token chunk, on either side of the bound of
+    # e^-64 below which a chunk leaves the whole-chunk form (Q~ and K e^-b) for
+    # the blocked one (full chunks; the last, partial chunk decays less)
     inp = make_inputs(B=2, T=200, H=2, Dk=D, Dv=D, dtype=dtype, gated=True, s0=True, seed=730,
                       gate_channels=True)
     if case == "decay30":
@@ -118,6 +123,10 @@ def test_gla_degenerate_gates(case, dtype, D):
     elif case == "resets":
         inp.log_alpha = torch.zeros_like(inp.log_alpha)
         inp.log_alpha[:, 5::37] = -80.0
+    elif case == "chunk_decay_61":
+        inp.log_alpha = torch.full_like(inp.log_alpha, -0.95)
+    elif case == "chunk_decay_67":
+        inp.log_alpha = torch.full_like(inp.log_alpha, -1.05)
     else:
         inp.log_alpha[..., ::2] = -30.0
     check(inp, dtype, tag=f"gates {case}")
