@@ -464,15 +464,19 @@ gdn_status check_sizes(int rule, int B, int T, int H, int Dk, int Dv, int C, boo
 // bf16 D128 T = 32768: 4 heads 0.51 -> 0.17, 8 heads 0.53 -> 0.25, 16 heads
 // 0.58 -> 0.47, 32 heads 0.72 (split 0.94: not taken); 4 heads T = 4096 0.085 ->
 // 0.067; 16 heads T = 2048 0.057 (split 0.073: not taken); fp32 D64 B2 H4
-// T = 1024 0.078 -> 0.055.  Packed batches always run the plain scan.
+// T = 1024 0.078 -> 0.055; fp32 D128 B1 H2 T = 8192 0.693 -> 0.206, 16 heads
+// T = 4096 0.368 (split 0.568: not taken).  Packed batches always run the
+// plain scan.
 struct SplitModel {
     int dk, dv, c;
     gdn_dtype dt;
+    bool w32;                         // both passes have a 32-column slice that fits the LDS
     double s_plain, s1, s3, c0, c1;   // microseconds
 };
 const SplitModel kSplitModels[] = {
-    {128, 128, 64, GDN_BF16, 1.05, 0.95, 1.40, 2.5, 0.18},
-    {64, 64, 64, GDN_F32, 3.30, 4.00, 4.00, 0.8, 0.04},
+    {128, 128, 64, GDN_BF16, true, 1.05, 0.95, 1.40, 2.5, 0.18},
+    {64, 64, 64, GDN_F32, true, 3.30, 4.00, 4.00, 0.8, 0.04},
+    {128, 128, 64, GDN_F32, false, 5.00, 5.00, 5.00, 2.0, 0.05},
 };
 constexpr double kKernelFixedUs = 6.0;
 
@@ -489,7 +493,7 @@ int auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt, b
     const double plain = kKernelFixedUs + (double)cps * m->s_plain;
     auto rounds = [&](int64_t n, int cols) {   // workgroup rounds of a pass over n span-units
         const int64_t w32 = n * cols / 32;
-        const int64_t w = w32 >= cus ? w32 : n * cols / 16;
+        const int64_t w = m->w32 && w32 >= cus ? w32 : n * cols / 16;
         return (double)((w + cus - 1) / cus);
     };
     double best = 0.95 * plain;

@@ -117,7 +117,7 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
  * With T = 0 nothing but S_T = S0 is computed and q, k, v, beta, O (and the
  * workspace, whose required size may then be 0) may be NULL.
  * Long sequences with few units: for a fixed-length batch of bf16 with
- * Dk = Dv = 128 or fp32 with Dk = Dv = 64 (C = 64), where the plain scan leaves
+ * Dk = Dv = 128 or fp32 with Dk = Dv = 64 or 128 (C = 64), where the plain scan leaves
  * most CUs idle and a cost model of the two paths (per-step costs measured on
  * MI355X) puts the split scan of gdn_chunk_fwd_split under 0.95 of the plain
  * one, the call runs that split scan, with the span length

@@ -197,7 +197,8 @@ def test_workspace_holds_the_automatic_split(lib):
     assert auto(2, 1024, 4, 64, 64, 64, 0, F32) == 2           # the fp32 D64 workload
     assert auto(1, 2048, 32, 64, 64, 64, 0, F32) == 0
     assert auto(1, 8192, 2, 128, 128, 64, 3, BF16) == 0        # packed batches never split
-    assert auto(1, 8192, 2, 128, 128, 64, 0, F32) == 0         # fp32 D128: no model, never automatic
+    assert auto(1, 8192, 2, 128, 128, 64, 0, F32) == 8         # fp32 D128 (16-column slices only)
+    assert auto(1, 4096, 16, 128, 128, 64, 0, F32) == 0
     assert auto(1, 8192, 2, 100, 128, 64, 0, BF16) == 0        # unsupported sizes
     # gdn_chunk_fwd's workspace query is then the split scan's, equal to
     # gdn_chunk_fwd_split_workspace_bytes with that span length; otherwise the
