@@ -229,6 +229,19 @@ def test_varlen_many_sequences(dtype, D, C):
     check(inp, dtype, C=C, tag=f"varlen {len(lengths)} sequences")
 
 
+def test_varlen_longest_first_order_edges():
+    # the scan dispatches packed sequences by chunk count, longest first (a
+    # counting sort over 4096 bins, counts of 4095 chunks and more sharing the
+    # first bin): sequences longer than that (4100 and 4300 chunks of 16), equal
+    # lengths, ascending and descending runs and empty ones, all against the
+    # oracle
+    C = 16
+    lengths = [4100 * C - 3, 5, 5, 0, 4300 * C, 17, 33, 64, 0, 65, 300, 299, 3, 1, 5]
+    inp = make_inputs(B=1, T=sum(lengths), H=1, Dk=16, Dv=16, dtype="f32", gated=True, s0=True,
+                      seed=81, lengths=lengths)
+    check(inp, "f32", C=C, tag="varlen order edges")
+
+
 def test_varlen_equals_separate_calls():
     lengths = [100, 37, 256]
     inp = make_inputs(B=1, T=sum(lengths), H=4, Dk=128, Dv=128, dtype="bf16", gated=True,
