@@ -158,7 +158,8 @@ struct KernelTimer {
 
 // The column-wave scan over n_seqs sequences (or spans) of every head, with 32
 // state columns per workgroup where that fits in LDS and still gives every CU
-// a workgroup, else 16.
+// a workgroup, else 16; 64 (bf16 outputs) where 32 would need more than one
+// workgroup per CU.
 template <typename T, int DK, int DV, int C, int RULE>
 gdn_status launch_scan(const T* q, const T* k, const T* v, const float* S0, const SeqGeom& geom,
                        int H, int64_t n_seqs, const float* g_ws, const T* Tb_ws, T* O, float* S_T,
@@ -184,6 +185,16 @@ gdn_status launch_scan(const T* q, const T* k, const T* v, const float* S0, cons
         }
     };
     static_assert(fit32 || fit16, "no column-scan configuration fits the LDS of one CU");
+    // 64-column slices (bf16, C = 64) where 32-column ones would take more
+    // than one workgroup per CU: a wide workgroup's chunk step is about 1.45
+    // times a 32-column one's, against two narrow workgroups in turn
+    if constexpr (sizeof(T) == 2 && C == 64 && DV % 64 == 0) {
+        using C64 = ColCfg<T, DK, DV, C, 64, RULE>;
+        if constexpr (C64::FITS) {
+            if (O != nullptr && rows.vz == 0 && units * (DV / 32) > device_cu_count())
+                return launch_cols(C64{});
+        }
+    }
     if (fit32 && (!fit16 || units * (DV / 32) >= device_cu_count())) return launch_cols(C32{});
     return launch_cols(C16{});
 }

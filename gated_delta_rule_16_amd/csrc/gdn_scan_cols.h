@@ -46,6 +46,17 @@
 // helpers get a SIMD each; the staging waves, which issue little, share the
 // column waves' SIMDs.  One barrier per chunk.
 //
+// Wide slices (DVT = 64, bf16, for calls with more slices than CUs): a chunk's
+// K, Q, Tb and gates are staged once per CU whatever the slice width, so a
+// 64-column slice halves those bytes per state column.  Four column waves,
+// four output helpers (one query block each) and the two staging waves: ten
+// waves, three on two of the SIMDs, so every wave keeps to 168 registers.
+// For that the helpers load Q into registers (there is no room for it in LDS
+// beside three staging buffers), read their K, Q and state operands at the
+// start of each contraction step rather than a step ahead, read V' at the
+// output and form the decay factors after the products; the column waves keep
+// two contraction steps of K fragments in flight instead of four.
+//
 // State tile layout.  Column wave vb keeps Dk / 16 tiles; lane (g, n) of tile i
 // holds S^T[drow(i, 4g + r)][vb*16 + n], r = 0..3.  bf16: tile 2m + h covers
 // d = 32m + 8a + 4h + r for its rows 4a + r, so that the lane values of tiles
@@ -68,9 +79,12 @@ struct ColCfg {
     static constexpr int ES = sizeof(T);
     static constexpr int NW = C / 16;                      // 16-token blocks of a chunk
     static constexpr int NVW = DVT / 16;                   // column waves
-    static constexpr int NPW = 4;                          // helper waves: the first NPP
-    static constexpr int NPP = 2;                          // form the output, the others
+    static constexpr bool WIDE = NVW > 2;                  // four column waves (see above)
+    static constexpr int NPP = WIDE ? NW : 2;              // helper waves: the first NPP
+    static constexpr int NPW = NPP + 2;                    // form the output, the others
     static constexpr int NWG = NVW + NPW, NTHR = NWG * 64; // stage chunks and write out O
+    // launch bound: the narrow slices keep the register budget of six waves
+    static constexpr int BOUND = NTHR > 384 ? NTHR : 384;
     static constexpr int NF = NPW - NPP;                   // staging waves: NLD load
     static constexpr int NLD = NF - 1;                     // chunks, the last writes out O
     static constexpr int EV = 16 / ES;                     // elements per 16 bytes
@@ -129,8 +143,9 @@ struct ColCfg {
     static constexpr size_t OFF_O = OFF_VO + 2 * SZ_VO;
     static constexpr size_t SMEM = OFF_O + 2 * SZ_O;
     static constexpr bool FITS = SMEM <= 160 * 1024;
-    // output helper of query block qb: 0 takes blocks 0 and NW - 1, 1 the middle ones
-    static constexpr int pwave(int qb) { return (qb < NW - 1 - qb ? qb : NW - 1 - qb) % NPP; }
+    // output helper of query block qb: 0 takes blocks 0 and NW - 1, 1 the middle
+    // ones (wide slices: helper qb)
+    static constexpr int pwave(int qb) { return NPP >= NW ? qb : (qb < NW - 1 - qb ? qb : NW - 1 - qb) % NPP; }
     // the query blocks of helper hw, and how many
     static constexpr int nmine(int hw) {
         int c = 0;
@@ -142,11 +157,11 @@ struct ColCfg {
             if (pwave(qb) == hw && j-- == 0) return qb;
         return 0;
     }
-    static constexpr int NQB = (NW + 1) / 2;               // query blocks per helper, at most
+    static constexpr int NQB = NPP >= NW ? 1 : (NW + 1) / 2;   // query blocks per helper, at most
     // Q register sets without QLDS: three where a set takes at most 32 registers,
     // two below 64, else one (fp32 with Dk = 128: two sets would spill)
     static constexpr int NQS = NQB * NKK * 16 <= 128 ? 3 : NQB * NKK * 16 < 256 ? 2 : 1;
-    static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && NVW <= 2, "tile counts");
+    static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && NVW <= 4 && NPP <= 4, "tile counts");
     static_assert(DV % DVT == 0 && DVT % 16 == 0 && DK % KS == 0 && DK % 16 == 0, "tile shapes");
     static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && (VB % 4 == 0 || VB == 2) && DK % 32 == 0),
                   "bf16 swizzles and tile pairs");
@@ -228,7 +243,7 @@ struct ScanRows {
 };
 
 template <typename T, int DK, int DV, int C, int DVT, int RULE>
-__global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
+__global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_scan_cols_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* S0, SeqGeom geom, int H,
     const float* __restrict__ g_ws, const T* __restrict__ Tb_ws,
@@ -355,7 +370,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         // update right after the Y instructions.
         // K fragments in flight: all contraction steps of Y where they take at
         // most 64 registers, else a ring of that many
-        constexpr int KPF = NKK * NW * (int)sizeof(Frag) <= 256 ? NKK : 256 / (NW * (int)sizeof(Frag));
+        constexpr int KPF = Cfg::WIDE ? 2 : NKK * NW * (int)sizeof(Frag) <= 256 ? NKK : 256 / (NW * (int)sizeof(Frag));
         auto step = [&](const int cc) __attribute__((always_inline)) {
             const Staged st = staged(cc);
             float4 dec4[NW];
@@ -533,10 +548,16 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         PFrag pp[Cfg::NQB][NPQ];
         f32x4 zp[Cfg::NQB][NVW];
         // output of chunk cd (its V' published by the last barrier, read into vo)
-        auto out = [&](int cd, const Op (*vo)[NW]) __attribute__((always_inline)) {
+        auto out = [&](int cd, const Op (*vo_in)[NW]) __attribute__((always_inline)) {
             unsigned char* ob = obuf(cd) + n * Cfg::LDO + g4 * ES;
 #pragma unroll
             for (int vb = 0; vb < NVW; ++vb) {
+                Op vw[NW];   // V' tiles of column wave vb (wide slices: read here)
+#pragma unroll
+                for (int jb = 0; jb < NW; ++jb) {
+                    if constexpr (Cfg::WIDE) vw[jb] = *vo_tile(cd, vb, jb);
+                    else vw[jb] = vo_in[vb][jb];
+                }
 #pragma unroll
                 for (int j = 0; j < NM; ++j) {
                     const int qb = Cfg::mine(hw, j);
@@ -545,12 +566,12 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
 #pragma unroll
                         for (int p = 0; p < NP; ++p)
                             if (2 * p <= qb)
-                                acc = KO::mma2(vo[vb][2 * p], vo[vb][2 * p + 1], __builtin_shufflevector(pp[j][p], pp[j][p], 0, 1, 2, 3),
+                                acc = KO::mma2(vw[2 * p], vw[2 * p + 1], __builtin_shufflevector(pp[j][p], pp[j][p], 0, 1, 2, 3),
                                                __builtin_shufflevector(pp[j][p], pp[j][p], 4, 5, 6, 7), acc);
                     } else {
 #pragma unroll
                         for (int jb = 0; jb < NW; ++jb)
-                            if (jb <= qb) acc = KO::mma1(vo[vb][jb], pp[j][jb], acc);
+                            if (jb <= qb) acc = KO::mma1(vw[jb], pp[j][jb], acc);
                     }
                     store4(reinterpret_cast<T*>(ob + qb * 16 * Cfg::LDO + vb * 16 * ES), acc[0], acc[1], acc[2], acc[3]);
                 }
@@ -561,9 +582,10 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             const Staged st = staged(cc);
             const T* sQ = reinterpret_cast<const T*>(qbuf(cc));
             // K and Q fragments and state tiles of one contraction step,
-            // requested a step ahead of their use (two register sets)
-            Frag kf[2][NW], qf[2][Cfg::NQB];
-            Op sbk[2][NVW][2];
+            // requested a step ahead of their use (two register sets; wide
+            // slices: one set, requested as the step starts)
+            Frag kf[Cfg::WIDE ? 1 : 2][NW], qf[Cfg::WIDE ? 1 : 2][Cfg::NQB];
+            Op sbk[Cfg::WIDE ? 1 : 2][NVW][2];
             auto fetch = [&](int kk, int s) __attribute__((always_inline)) {
                 if constexpr (!Cfg::GLA) {   // kGla: P~ arrives formed
 #pragma unroll
@@ -572,17 +594,19 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
 #pragma unroll
                 for (int j = 0; j < NM; ++j)
                     qf[s][j] = Cfg::QLDS ? kfrag_rows<Cfg>(sQ, Cfg::mine(hw, j) * 16, kk * KS) : qcur[j][kk];
+                if constexpr (!Cfg::WIDE) {
 #pragma unroll
-                for (int vb = 0; vb < NVW; ++vb) {
-                    sbk[s][vb][0] = *sb_tile(cc, vb, Cfg::BF ? 2 * kk : kk);
-                    if constexpr (Cfg::BF) sbk[s][vb][1] = *sb_tile(cc, vb, 2 * kk + 1);
+                    for (int vb = 0; vb < NVW; ++vb) {
+                        sbk[s][vb][0] = *sb_tile(cc, vb, Cfg::BF ? 2 * kk : kk);
+                        if constexpr (Cfg::BF) sbk[s][vb][1] = *sb_tile(cc, vb, 2 * kk + 1);
+                    }
                 }
             };
             // the first contraction step's operands and V' of the pending chunk
             // (whose output goes out after the first step's instructions)
-            fetch(0, 0);
-            Op vo[NVW][NW];
-            if (cc > 0) {
+            if constexpr (!Cfg::WIDE) fetch(0, 0);
+            Op vo[Cfg::WIDE ? 1 : NVW][NW];
+            if (!Cfg::WIDE && cc > 0) {
 #pragma unroll
                 for (int vb = 0; vb < NVW; ++vb)
 #pragma unroll
@@ -621,27 +645,36 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const int s = kk & 1;
-                if (kk + 1 < NKK) fetch(kk + 1, s ^ 1);
+                const int ss = Cfg::WIDE ? 0 : s;
+                if constexpr (Cfg::WIDE) {
+#pragma unroll
+                    for (int vb = 0; vb < NVW; ++vb) {
+                        sbk[0][vb][0] = *sb_tile(cc, vb, Cfg::BF ? 2 * kk : kk);
+                        if constexpr (Cfg::BF) sbk[0][vb][1] = *sb_tile(cc, vb, 2 * kk + 1);
+                    }
+                }
+                if constexpr (Cfg::WIDE) fetch(kk, 0);
+                else if (kk + 1 < NKK) fetch(kk + 1, s ^ 1);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < NM; ++j) {
                     const int qb = Cfg::mine(hw, j);
                     if constexpr (!Cfg::GLA) {
 #pragma unroll
-                        for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] = St16::mma(kf[s][jb], qf[s][j], Pt[j][jb]);
+                        for (int jb = 0; jb <= qb; ++jb) Pt[j][jb] = St16::mma(kf[ss][jb], qf[ss][j], Pt[j][jb]);
                     }
 #pragma unroll
                     for (int vb = 0; vb < NVW; ++vb) {
                         if constexpr (Cfg::BF) {
-                            const s16x8 qs = __builtin_bit_cast(s16x8, qf[s][j]);
-                            Zt[j][vb] = KO::mma2(sbk[s][vb][0], sbk[s][vb][1], __builtin_shufflevector(qs, qs, 0, 1, 2, 3),
+                            const s16x8 qs = __builtin_bit_cast(s16x8, qf[ss][j]);
+                            Zt[j][vb] = KO::mma2(sbk[ss][vb][0], sbk[ss][vb][1], __builtin_shufflevector(qs, qs, 0, 1, 2, 3),
                                                  __builtin_shufflevector(qs, qs, 4, 5, 6, 7), Zt[j][vb]);
                         } else {
-                            Zt[j][vb] = St16::mma(sbk[s][vb][0], qf[s][j], Zt[j][vb]);
+                            Zt[j][vb] = St16::mma(sbk[ss][vb][0], qf[ss][j], Zt[j][vb]);
                         }
                     }
                 }
-                if constexpr (!Cfg::GLA) {
+                if constexpr (!Cfg::GLA && !Cfg::WIDE) {
 #pragma unroll
                     for (int jb = kk; jb < NW; jb += NKK) decay(jb);
                     if (kk == NKK - 1) {
@@ -649,10 +682,14 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
                         for (int jb = NKK; jb < NW; ++jb) decay(jb);
                     }
                 }
-                if (kk == 0 && cc > 0) out(cc - 1, vo);
+                if (kk == 0 && cc > 0) out(cc - 1, Cfg::WIDE ? nullptr : vo);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // decay and mask P^T, scale Z^T by gamma at the query token; keep both
+            if constexpr (!Cfg::GLA && Cfg::WIDE) {
+#pragma unroll
+                for (int jb = 0; jb < NW; ++jb) decay(jb);
+            }
 #pragma unroll
             for (int j = 0; j < NM; ++j) {
                 const int qb = Cfg::mine(hw, j);
@@ -711,7 +748,7 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
             for (int vb = 0; vb < NVW; ++vb)
 #pragma unroll
                 for (int jb = 0; jb < NW; ++jb) vo[vb][jb] = *vo_tile(count - 1, vb, jb);
-            out(count - 1, vo);
+            out(count - 1, Cfg::WIDE ? nullptr : vo);
         }
         __syncthreads();
     };
@@ -857,14 +894,31 @@ __global__ __launch_bounds__(384) void gdn_scan_cols_kernel(
         }
     };
 
-    if (w < NVW) {
-        if (w == 0) run_col(std::integral_constant<int, 0>{});
-        else if constexpr (NVW > 1) run_col(std::integral_constant<int, (NVW > 1 ? 1 : 0)>{});
+    // waves: the column waves, the output helpers, the loader, the writer
+    if constexpr (!Cfg::WIDE) {
+        if (w < NVW) {
+            if (w == 0) run_col(std::integral_constant<int, 0>{});
+            else if constexpr (NVW > 1) run_col(std::integral_constant<int, (NVW > 1 ? 1 : 0)>{});
+        } else {
+            switch (w - NVW) {
+                case 0: run_out(std::integral_constant<int, 0>{}); break;
+                case 1: run_out(std::integral_constant<int, 1>{}); break;
+                case 2: run_stage(std::integral_constant<int, 0>{}); break;
+                default: run_stage(std::integral_constant<int, 1>{}); break;
+            }
+        }
     } else {
-        switch (w - NVW) {
-            case 0: run_out(std::integral_constant<int, 0>{}); break;
-            case 1: run_out(std::integral_constant<int, 1>{}); break;
-            case 2: run_stage(std::integral_constant<int, 0>{}); break;
+        static_assert(NVW == 4 && Cfg::NPP == 4, "wide slices: four column waves and four helpers");
+        switch (w) {
+            case 0: run_col(std::integral_constant<int, 0>{}); break;
+            case 1: run_col(std::integral_constant<int, 1>{}); break;
+            case 2: run_col(std::integral_constant<int, 2>{}); break;
+            case 3: run_col(std::integral_constant<int, 3>{}); break;
+            case 4: run_out(std::integral_constant<int, 0>{}); break;
+            case 5: run_out(std::integral_constant<int, 1>{}); break;
+            case 6: run_out(std::integral_constant<int, 2>{}); break;
+            case 7: run_out(std::integral_constant<int, 3>{}); break;
+            case 8: run_stage(std::integral_constant<int, 0>{}); break;
             default: run_stage(std::integral_constant<int, 1>{}); break;
         }
     }

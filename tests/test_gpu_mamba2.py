@@ -109,3 +109,10 @@ def test_mamba2_profiled_matches_plain_call():
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(S1, S2)
     assert ms[1] > 0 and ms[2] > 0
+
+
+def test_mamba2_wide_slices():
+    # bf16 calls with more 32-column slices than CUs take 64-column slices
+    inp = make_inputs(B=8, T=300, H=32, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True,
+                      seed=420)
+    check(inp, "bf16", tag="64-column slices")

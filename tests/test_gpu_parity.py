@@ -150,6 +150,25 @@ def test_f32_d64_two_column_waves(C):
     check(inp, "f32", C=C, tag="fp32 D64 32-column slices")
 
 
+@pytest.mark.parametrize("B,H,T,Dv", [(8, 32, 300, 128), (4, 32, 200, 256), (3, 32, 130, 128)])
+def test_wide_slices(B, H, T, Dv):
+    # bf16 calls whose 32-column slices would need more than one workgroup per
+    # CU take 64-column slices (four column waves, one output helper per query
+    # block); ragged last chunks, every head against the oracle
+    inp = make_inputs(B=B, T=T, H=H, Dk=128, Dv=Dv, dtype="bf16", gated=True, s0=True,
+                      seed=410 + B)
+    check(inp, "bf16", tag="64-column slices")
+
+
+def test_wide_slices_varlen():
+    # packed batch in 64-column slices: empty, one-token, chunk-edge and
+    # several-chunk sequences over 32 heads
+    lengths = [0, 1, 63, 64, 65, 200, 0, 7, 130, 129, 2]
+    inp = make_inputs(B=1, T=sum(lengths), H=32, Dk=128, Dv=128, dtype="bf16", gated=True,
+                      s0=True, seed=415, lengths=lengths)
+    check(inp, "bf16", tag="varlen 64-column slices")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_largest_accepted_sizes(dtype):
     # the largest token tensors gdn_chunk_fwd accepts (one token more passes
