@@ -22,7 +22,9 @@
  * Conventions shared by every entry point
  *  - All tensor arguments are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
  *    to dense row-major arrays.  The caller owns every buffer, the workspace
- *    included; the library allocates nothing and keeps no mutable global state.
+ *    included; the library allocates nothing.  Its only global state is a cache
+ *    of per-device queries (CU count, occupancy) and the static scratch buffer
+ *    of gdn_chunk_fwd_noalloc (see there).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream).
  *    Argument errors are detected on the host before anything is enqueued and
  *    nothing is written then.  Faults inside kernels surface at the caller's next
