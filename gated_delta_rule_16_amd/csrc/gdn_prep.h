@@ -25,10 +25,10 @@
 //
 // Work split: one wave prepares one unit (chunk slot, head) at a time, with no
 // synchronisation beyond the wave.  Waves are persistent: wave w of workgroup
-// b walks units b*4 + w, then that plus 4 gridDim, ...  Two waves share each
-// SIMD (the register budget is held to half the file), so that one computes
-// while the other waits for its unit's keys -- this measured faster than one
-// wave per SIMD with the next unit's keys prefetched into registers.
+// b walks units b*4 + w, then that plus 4 gridDim, ...  At least two waves
+// share each SIMD (the register budget is held to half the file), so that one
+// computes while another waits for its unit's keys -- this measured faster
+// than one wave per SIMD with the next unit's keys prefetched into registers.
 // Per unit:
 //  - the keys arrive as MFMA row fragments (lane (g, n): row 16b + n, 16 bytes
 //    at contraction offset 16 g of each step), so K K^T needs no LDS;
