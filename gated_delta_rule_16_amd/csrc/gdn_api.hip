@@ -11,6 +11,7 @@
 // (Q~, K^, P~ and the chunk decay per chunk) and runs the scan on those.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <iterator>
 #include <cstdlib>
@@ -191,7 +192,7 @@ gdn_status launch_scan(const T* q, const T* k, const T* v, const float* S0, cons
     if constexpr (sizeof(T) == 2 && C == 64 && DV % 64 == 0) {
         using C64 = ColCfg<T, DK, DV, C, 64, RULE>;
         if constexpr (C64::FITS) {
-            if (O != nullptr && rows.vz == 0 && units * (DV / 32) > device_cu_count())
+            if (units * (DV / 32) > device_cu_count())
                 return launch_cols(C64{});
         }
     }
@@ -468,12 +469,15 @@ gdn_status check_sizes(int rule, int B, int T, int H, int Dk, int Dv, int C, boo
 // the workgroups:
 //   plain    = f + chunks * s_plain
 //   split(P) = 3 f + L (s1 r1 + s3 r3) + P (c0 + c1 units),  L = ceil(chunks / P),
+// with s_plain rising from its few-workgroup value to s_full as the plain
+// scan's workgroups go from half the CUs to all of them,
 // with r1, r3 the rounds of workgroups each pass needs on the device (32-column
-// slices where they fill it, else 16-column ones) and f a kernel's fixed
-// cost.  The split is taken at the best P when it is under 0.95 of the plain
+// slices where they fill it, else 16-column ones; bf16: 64-column slices, at
+// their own step cost, where 32-column ones would need more than one round)
+// and f a kernel's fixed cost.  The split is taken at the best P when it is under 0.95 of the plain
 // estimate.  Measured (ms per call, plain -> split at the chosen span length):
-// bf16 D128 T = 32768: 4 heads 0.51 -> 0.17, 8 heads 0.53 -> 0.25, 16 heads
-// 0.58 -> 0.47, 32 heads 0.72 (split 0.94: not taken); 4 heads T = 4096 0.085 ->
+// bf16 D128 T = 32768: 4 heads 0.51 -> 0.15, 8 heads 0.53 -> 0.21, 16 heads
+// 0.58 -> 0.36, 32 heads 0.72 -> 0.645; 4 heads T = 4096 0.085 ->
 // 0.067; 16 heads T = 2048 0.057 (split 0.073: not taken); fp32 D64 B2 H4
 // T = 1024 0.078 -> 0.055; fp32 D128 B1 H2 T = 8192 0.693 -> 0.206, 16 heads
 // T = 4096 0.368 (split 0.568: not taken).  Packed batches always run the
@@ -482,12 +486,13 @@ struct SplitModel {
     int dk, dv, c;
     gdn_dtype dt;
     bool w32;                         // both passes have a 32-column slice that fits the LDS
-    double s_plain, s1, s3, c0, c1;   // microseconds
+    double s_plain, s_full, s1, s3, c0, c1;   // microseconds
+    double s1w, s3w;                          // 64-column slices (0: none)
 };
 const SplitModel kSplitModels[] = {
-    {128, 128, 64, GDN_BF16, true, 1.05, 0.95, 1.40, 2.5, 0.18},
-    {64, 64, 64, GDN_F32, true, 3.30, 4.00, 4.00, 0.8, 0.04},
-    {128, 128, 64, GDN_F32, false, 5.00, 5.00, 5.00, 2.0, 0.05},
+    {128, 128, 64, GDN_BF16, true, 1.05, 1.25, 0.95, 1.40, 2.5, 0.18, 1.05, 1.95},
+    {64, 64, 64, GDN_F32, true, 3.30, 3.30, 4.00, 4.00, 0.8, 0.04, 0.0, 0.0},
+    {128, 128, 64, GDN_F32, false, 5.00, 5.00, 5.00, 5.00, 2.0, 0.05, 0.0, 0.0},
 };
 constexpr double kKernelFixedUs = 6.0;
 
@@ -501,11 +506,16 @@ int auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt, b
     const int64_t cus = device_cu_count();
     const int64_t units = (int64_t)B * H;
     if (cps < 2 || units * (Dv / 16) > cus) return 0;   // the plain scan already fills the device
-    const double plain = kKernelFixedUs + (double)cps * m->s_plain;
-    auto rounds = [&](int64_t n, int cols) {   // workgroup rounds of a pass over n span-units
+    const int64_t wp = m->w32 && units * (Dv / 32) >= cus ? units * (Dv / 32) : units * (Dv / 16);
+    const double fill = std::min(1.0, std::max(0.0, 2.0 * (double)wp / (double)cus - 1.0));
+    const double plain = kKernelFixedUs + (double)cps * (m->s_plain + fill * (m->s_full - m->s_plain));
+    // time of one chunk step of a pass over n span-units: rounds of workgroups
+    // times the step cost of the slice width the scan takes (launch_scan)
+    auto step = [&](int64_t n, int cols, double s, double sw) {
         const int64_t w32 = n * cols / 32;
+        if (sw > 0 && cols % 64 == 0 && w32 > cus) return sw * (double)((n * cols / 64 + cus - 1) / cus);
         const int64_t w = m->w32 && w32 >= cus ? w32 : n * cols / 16;
-        return (double)((w + cus - 1) / cus);
+        return s * (double)((w + cus - 1) / cus);
     };
     double best = 0.95 * plain;
     int best_l = 0;
@@ -513,7 +523,7 @@ int auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt, b
         const int64_t L = (cps + P - 1) / P, Pe = (cps + L - 1) / L;
         const int64_t n = units * Pe;
         if ((int64_t)B * Pe > 65535) break;   // spans of the batch: the scan grid's third dimension
-        const double cost = 3 * kKernelFixedUs + (double)L * (m->s1 * rounds(n, Dk + Dv) + m->s3 * rounds(n, Dv)) +
+        const double cost = 3 * kKernelFixedUs + (double)L * (step(n, Dk + Dv, m->s1, m->s1w) + step(n, Dv, m->s3, m->s3w)) +
                             (double)Pe * (m->c0 + m->c1 * (double)units);
         if (cost < best) {
             best = cost;

@@ -123,9 +123,10 @@ def test_gdn_chunk_fwd_takes_the_split_for_few_long_units():
     inp = make_inputs(B=1, T=8192, H=2, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True, seed=3400)
     L = gdn.gdn_chunk_fwd_auto_span_chunks(1, 8192, 2, 128, 128, 64, 0, torch.bfloat16)
     assert 8 <= L <= 64, L
-    # the headline and long workloads keep the plain scan
+    # the headline keeps the plain scan; the long workload (32 units of 512
+    # chunks) is split into spans of 128 chunks
     assert gdn.gdn_chunk_fwd_auto_span_chunks(4, 4096, 16, 128, 128, 64, 0, torch.bfloat16) == 0
-    assert gdn.gdn_chunk_fwd_auto_span_chunks(1, 32768, 32, 128, 128, 64, 0, torch.bfloat16) == 0
+    assert gdn.gdn_chunk_fwd_auto_span_chunks(1, 32768, 32, 128, 128, 64, 0, torch.bfloat16) == 128
     d = inp.to(DEV)
     O, S = gdn.gdn_chunk_fwd(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0)
     Os, Ss = gdn.gdn_chunk_fwd_split(d.q, d.k, d.v, d.log_alpha, d.beta, d.S0, span_chunks=L)
