@@ -289,6 +289,15 @@ def test_bitwise_deterministic():
     assert np.array_equal(O1, O2) and np.array_equal(S1, S2)
 
 
+def test_bitwise_deterministic_wide_slices_and_split():
+    # the 64-column slices (B8 H32) and the automatic split (B1 H4 T8192)
+    for inp in (make_inputs(B=8, T=300, H=32, Dk=128, Dv=128, dtype="bf16", seed=417),
+                make_inputs(B=1, T=8192, H=4, Dk=128, Dv=128, dtype="bf16", seed=418)):
+        O1, S1 = run_gpu(inp)
+        O2, S2 = run_gpu(inp)
+        assert np.array_equal(O1, O2) and np.array_equal(S1, S2)
+
+
 def test_workspace_reused_across_inputs():
     """One workspace, filled with 0xff bytes first, serves calls on different
     inputs in turn: each call's results match the oracle, so nothing a previous
