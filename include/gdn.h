@@ -119,10 +119,10 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
  * With T = 0 nothing but S_T = S0 is computed and q, k, v, beta, O (and the
  * workspace, whose required size may then be 0) may be NULL.
  * Long sequences with few units: for a fixed-length batch of bf16 with
- * Dk = Dv = 128 or fp32 with Dk = Dv = 64 or 128 (C = 64), where the plain scan leaves
- * most CUs idle and a cost model of the two paths (per-step costs measured on
- * MI355X) puts the split scan of gdn_chunk_fwd_split under 0.95 of the plain
- * one, the call runs that split scan, with the span length
+ * Dk = Dv = 128 or fp32 with Dk = Dv = 64 or 128 (C = 64), where a cost model
+ * of the two paths (per-step costs measured on MI355X) puts the split scan of
+ * gdn_chunk_fwd_split under 0.95 of the plain one (few units, or few units per
+ * CU over long sequences), the call runs that split scan, with the span length
  * gdn_chunk_fwd_auto_span_chunks reports, when the workspace holds
  * gdn_chunk_fwd_workspace_bytes(...) for these sizes, which then includes room
  * for it; the results equal the plain scan's up to rounding.
@@ -185,7 +185,9 @@ gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
  * The result equals gdn_chunk_fwd's up to rounding (passes 1 and 3 run the
  * same chunk arithmetic; pass 2 is an fp32 product).  Passes 1 and 3 hold
  * (Dk + 2 Dv) / Dv times the state columns of one plain scan, spread over the
- * spans in parallel: it pays when B H Dv / 16 is well below the CU count.
+ * spans in parallel: it pays when B H Dv / 16 is well below the CU count, and
+ * for long sequences that fill the device with few units (gdn_chunk_fwd's cost
+ * model decides; see gdn_chunk_fwd_auto_span_chunks).
  * Arguments as gdn_chunk_fwd for a fixed-length batch (no cu_seqlens), plus:
  *  span_chunks  chunks per span (>= 1); the last span of a sequence may be
  *               shorter;
