@@ -200,6 +200,41 @@ gdn_status launch_scan(const T* q, const T* k, const T* v, const float* S0, cons
     return launch_cols(C16{});
 }
 
+// Whether the split scan's span maps over n span-units run 128-column slices
+// (bf16, C = 64): where 64-column ones would need more than one round of the
+// device.  Those slices write no outputs, so eight column waves take the place
+// of the output helpers and each workgroup covers twice the columns.
+template <typename T, int DK, int DV, int C>
+constexpr bool kMaps128 = sizeof(T) == 2 && C == 64 && (DK + DV) % 128 == 0 &&
+                          ColCfg<T, DK, DK + DV, C, 128, kDelta>::FITS;
+
+bool maps128_pays(int64_t span_units, int cols) {
+    return span_units * (cols / 64) > device_cu_count();
+}
+
+// The split scan's first pass: every span from identity state rows (DK of
+// them, zero values) and from zero for the DV value rows; no outputs.
+template <typename T, int DK, int DV, int C>
+gdn_status launch_maps(const T* q, const T* k, const T* v, const SeqGeom& geom, int H, int64_t n_seqs,
+                       const float* g_ws, const T* Tb_ws, float* maps, hipStream_t stream, KernelTimer* tm) {
+    if constexpr (kMaps128<T, DK, DV, C>) {
+        if (maps128_pays(n_seqs * H, DK + DV)) {
+            using CM = ColCfg<T, DK, DK + DV, C, 128, kDelta>;
+            constexpr auto ks = gdn_scan_cols_kernel<T, DK, DK + DV, C, 128, kDelta>;
+            allow_smem<ks>(CM::SMEM);
+            tm->mark(stream);
+            hipLaunchKernelGGL(ks, dim3((DK + DV) / 128, H, (unsigned)n_seqs), dim3(CM::NTHR), CM::SMEM, stream,
+                               q, k, v, (const float*)nullptr, geom, H, g_ws, Tb_ws, (T*)nullptr, maps,
+                               ScanRows{DK, DV});
+            if (gdn_status s = check_launch(stream)) return s;
+            tm->mark(stream);
+            return GDN_OK;
+        }
+    }
+    return launch_scan<T, DK, DK + DV, C, kDelta>(q, k, v, nullptr, geom, H, n_seqs, g_ws, Tb_ws, nullptr, maps,
+                                                  ScanRows{DK, DV}, stream, tm);
+}
+
 template <typename T, int DK, int DV, int C, int RULE>
 gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
     const bool varlen = a.cu != nullptr;
@@ -348,9 +383,7 @@ gdn_status launch_split(const FwdArgs& a, int L, KernelTimer* tm) {
     const int64_t NS = a.B * S.P;
     // (1) span maps: DK identity rows with zero values, then the DV value rows
     // from zero; no outputs
-    if (gdn_status s = launch_scan<T, DK, DK + DV, C, kDelta>(q, k, v, nullptr, sg, a.H, NS, g_ws, Tb_ws,
-                                                            nullptr, maps, ScanRows{DK, DV}, a.stream, tm))
-        return s;
+    if (gdn_status s = launch_maps<T, DK, DV, C>(q, k, v, sg, a.H, NS, g_ws, Tb_ws, maps, a.stream, tm)) return s;
     // (2) each span's start state, and S_T
     {
         using SC = SpanCfg<DK, DV>;
@@ -488,11 +521,12 @@ struct SplitModel {
     bool w32;                         // both passes have a 32-column slice that fits the LDS
     double s_plain, s_full, s1, s3, c0, c1;   // microseconds
     double s1w, s3w;                          // 64-column slices (0: none)
+    double s1m;                               // span maps on 128-column slices (0: none)
 };
 const SplitModel kSplitModels[] = {
-    {128, 128, 64, GDN_BF16, true, 1.05, 1.25, 0.95, 1.40, 2.5, 0.18, 1.05, 1.95},
-    {64, 64, 64, GDN_F32, true, 3.30, 3.30, 4.00, 4.00, 0.8, 0.04, 0.0, 0.0},
-    {128, 128, 64, GDN_F32, false, 5.00, 5.00, 5.00, 5.00, 2.0, 0.05, 0.0, 0.0},
+    {128, 128, 64, GDN_BF16, true, 1.05, 1.25, 0.95, 1.40, 2.5, 0.18, 1.05, 1.95, 1.50},
+    {64, 64, 64, GDN_F32, true, 3.30, 3.30, 4.00, 4.00, 0.8, 0.04, 0.0, 0.0, 0.0},
+    {128, 128, 64, GDN_F32, false, 5.00, 5.00, 5.00, 5.00, 2.0, 0.05, 0.0, 0.0, 0.0},
 };
 constexpr double kKernelFixedUs = 6.0;
 
@@ -517,13 +551,20 @@ int auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt, b
         const int64_t w = m->w32 && w32 >= cus ? w32 : n * cols / 16;
         return s * (double)((w + cus - 1) / cus);
     };
+    // the span maps: 128-column slices where 64-column ones need more than one
+    // round (launch_maps)
+    auto step_maps = [&](int64_t n) {
+        const int cols = Dk + Dv;
+        if (m->s1m > 0 && n * (cols / 64) > cus) return m->s1m * (double)((n * cols / 128 + cus - 1) / cus);
+        return step(n, cols, m->s1, m->s1w);
+    };
     double best = 0.95 * plain;
     int best_l = 0;
     for (int64_t P = 2; P <= cps && P <= 64; ++P) {
         const int64_t L = (cps + P - 1) / P, Pe = (cps + L - 1) / L;
         const int64_t n = units * Pe;
         if ((int64_t)B * Pe > 65535) break;   // spans of the batch: the scan grid's third dimension
-        const double cost = 3 * kKernelFixedUs + (double)L * (step(n, Dk + Dv, m->s1, m->s1w) + step(n, Dv, m->s3, m->s3w)) +
+        const double cost = 3 * kKernelFixedUs + (double)L * (step_maps(n) + step(n, Dv, m->s3, m->s3w)) +
                             (double)Pe * (m->c0 + m->c1 * (double)units);
         if (cost < best) {
             best = cost;

@@ -57,6 +57,11 @@
 // output and form the decay factors after the products; the column waves keep
 // two contraction steps of K fragments in flight instead of four.
 //
+// Span-map slices (DVT = 128, bf16): the first pass of the split scan writes
+// no outputs, so where its 64-column slices would need more than one round of
+// the device it runs 128-column ones: eight column waves and the two staging
+// waves, no output helpers and no hand-over buffers, half the workgroups.
+//
 // State tile layout.  Column wave vb keeps Dk / 16 tiles; lane (g, n) of tile i
 // holds S^T[drow(i, 4g + r)][vb*16 + n], r = 0..3.  bf16: tile 2m + h covers
 // d = 32m + 8a + 4h + r for its rows 4a + r, so that the lane values of tiles
@@ -79,8 +84,11 @@ struct ColCfg {
     static constexpr int ES = sizeof(T);
     static constexpr int NW = C / 16;                      // 16-token blocks of a chunk
     static constexpr int NVW = DVT / 16;                   // column waves
-    static constexpr bool WIDE = NVW > 2;                  // four column waves (see above)
-    static constexpr int NPP = WIDE ? NW : 2;              // helper waves: the first NPP
+    // 128-column slices (eight column waves) serve the split scan's span maps,
+    // which write no outputs: no output helpers and no hand-over buffers
+    static constexpr bool MAPS = NVW == 8;
+    static constexpr bool WIDE = NVW > 2;                  // four or eight column waves
+    static constexpr int NPP = MAPS ? 0 : WIDE ? NW : 2;   // helper waves: the first NPP
     static constexpr int NPW = NPP + 2;                    // form the output, the others
     static constexpr int NWG = NVW + NPW, NTHR = NWG * 64; // stage chunks and write out O
     // launch bound: the narrow slices keep the register budget of six waves
@@ -117,13 +125,13 @@ struct ColCfg {
     // column wave) and V' (NW tiles per column wave); two buffers each (chunk
     // parity)
     static constexpr int TILE = 64 * 4 * ES;
-    static constexpr size_t SZ_SB = (size_t)NVW * NDB * TILE, SZ_VO = (size_t)NVW * NW * TILE;
+    static constexpr size_t SZ_SB = MAPS ? 0 : (size_t)NVW * NDB * TILE, SZ_VO = MAPS ? 0 : (size_t)NVW * NW * TILE;
     // the chunk's output slice, handed from the output helpers to the staging
     // waves: rows of DVT values padded by 16 bytes; two buffers (chunk parity)
     static constexpr int LDO = DVT * ES + 16;                  // row pitch (bytes)
     static constexpr int OPR = DVT * ES / 16;                  // 16-byte pieces per row
     static constexpr int NOPL = cdiv(C * OPR, 64);             // pieces per writing lane
-    static constexpr size_t SZ_O = (size_t)C * LDO;
+    static constexpr size_t SZ_O = MAPS ? 0 : (size_t)C * LDO;
     // Q of a chunk: staged by the loader one chunk ahead in two LDS buffers
     // (rows as K's) where that fits next to three staging buffers (QLDS), else
     // loaded by the output helpers straight into registers, NQS chunks ahead
@@ -135,7 +143,7 @@ struct ColCfg {
     static constexpr bool fits(int ns, bool q) {
         return ns * SZ_STAGE + SZ_REST + (q ? 2 * SZ_Q : 0) <= 160 * 1024 && cdiv(NI, NLD) * (ns - 2) < 64;
     }
-    static constexpr bool QLDS = fits(3, true);
+    static constexpr bool QLDS = !MAPS && fits(3, true);
     static constexpr int NSTG = QLDS ? 3 : fits(4, false) ? 4 : fits(3, false) ? 3 : 2;
     static constexpr int DIST = NSTG - 1;                  // chunks staged ahead
     static constexpr size_t OFF_QB = NSTG * SZ_STAGE, OFF_SB = OFF_QB + (QLDS ? 2 * SZ_Q : 0);
@@ -145,7 +153,9 @@ struct ColCfg {
     static constexpr bool FITS = SMEM <= 160 * 1024;
     // output helper of query block qb: 0 takes blocks 0 and NW - 1, 1 the middle
     // ones (wide slices: helper qb)
-    static constexpr int pwave(int qb) { return NPP >= NW ? qb : (qb < NW - 1 - qb ? qb : NW - 1 - qb) % NPP; }
+    static constexpr int pwave(int qb) {
+        return NPP == 0 ? 0 : NPP >= NW ? qb : (qb < NW - 1 - qb ? qb : NW - 1 - qb) % NPP;
+    }
     // the query blocks of helper hw, and how many
     static constexpr int nmine(int hw) {
         int c = 0;
@@ -161,7 +171,7 @@ struct ColCfg {
     // Q register sets without QLDS: three where a set takes at most 32 registers,
     // two below 64, else one (fp32 with Dk = 128: two sets would spill)
     static constexpr int NQS = NQB * NKK * 16 <= 128 ? 3 : NQB * NKK * 16 < 256 ? 2 : 1;
-    static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && NVW <= 4 && NPP <= 4, "tile counts");
+    static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && (NVW <= 4 || MAPS) && NPP <= 4, "tile counts");
     static_assert(DV % DVT == 0 && DVT % 16 == 0 && DK % KS == 0 && DK % 16 == 0, "tile shapes");
     static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && (VB % 4 == 0 || VB == 2) && DK % 32 == 0),
                   "bf16 swizzles and tile pairs");
@@ -304,7 +314,7 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
     const int64_t rs_k = (int64_t)H * DK * ES, rs_v = (int64_t)H * rows.vld * ES;
     const bool vzero = v0 < rows.vz;           // whole slice in the identity rows
     const int vc0 = v0 - rows.vz;              // first value column of the slice
-    const bool no_out = O == nullptr;
+    const bool no_out = Cfg::MAPS || O == nullptr;   // 128-column slices: span maps only
 
     auto barrier = [&]() __attribute__((always_inline)) {
         asm volatile("" ::: "memory");
@@ -361,7 +371,7 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
 #pragma unroll
         for (int i = 0; i < NDB; ++i) {
             Sb[i] = KO::tile(St[i]);
-            *sb_tile(0, vb, i) = Sb[i];
+            if constexpr (!Cfg::MAPS) *sb_tile(0, vb, i) = Sb[i];
         }
         __syncthreads();
 
@@ -485,8 +495,10 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
                 Vd[jb] = KO::tile(f32x4{Vp[jb][0] * dec4[jb].x, Vp[jb][1] * dec4[jb].y, Vp[jb][2] * dec4[jb].z,
                                         Vp[jb][3] * dec4[jb].w});
             // V' for the output helpers (A operand of O^T = V'^T P^T)
+            if constexpr (!Cfg::MAPS) {
 #pragma unroll
-            for (int jb = 0; jb < NW; ++jb) *vo_tile(cc, vb, jb) = KO::tile(Vp[jb]);
+                for (int jb = 0; jb < NW; ++jb) *vo_tile(cc, vb, jb) = KO::tile(Vp[jb]);
+            }
 #pragma unroll
             for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -500,7 +512,7 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
 #pragma unroll
             for (int i = 0; i < NDB; ++i) {
                 Sb[i] = KO::tile(St[i]);
-                *sb_tile(cc + 1, vb, i) = Sb[i];
+                if constexpr (!Cfg::MAPS) *sb_tile(cc + 1, vb, i) = Sb[i];
             }
             wait_vm_lgkm0<63>();
             barrier();
@@ -895,7 +907,21 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
     };
 
     // waves: the column waves, the output helpers, the loader, the writer
-    if constexpr (!Cfg::WIDE) {
+    if constexpr (Cfg::MAPS) {
+        static_assert(NVW == 8 && Cfg::NPP == 0, "span-map slices: eight column waves, no helpers");
+        switch (w) {
+            case 0: run_col(std::integral_constant<int, 0>{}); break;
+            case 1: run_col(std::integral_constant<int, 1>{}); break;
+            case 2: run_col(std::integral_constant<int, 2>{}); break;
+            case 3: run_col(std::integral_constant<int, 3>{}); break;
+            case 4: run_col(std::integral_constant<int, 4>{}); break;
+            case 5: run_col(std::integral_constant<int, 5>{}); break;
+            case 6: run_col(std::integral_constant<int, 6>{}); break;
+            case 7: run_col(std::integral_constant<int, 7>{}); break;
+            case 8: run_stage(std::integral_constant<int, 0>{}); break;
+            default: run_stage(std::integral_constant<int, 1>{}); break;
+        }
+    } else if constexpr (!Cfg::WIDE) {
         if (w < NVW) {
             if (w == 0) run_col(std::integral_constant<int, 0>{});
             else if constexpr (NVW > 1) run_col(std::integral_constant<int, (NVW > 1 ? 1 : 0)>{});

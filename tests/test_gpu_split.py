@@ -45,14 +45,16 @@ def check(inp, span_chunks, tag="", dtype="bf16"):
 
 
 def test_split_long_workload_all_heads():
-    # the long-context workload, 512 chunks per sequence in 8 spans of 64 (its
-    # output pass, 256 span-head units, runs in 64-column slices)
+    # the long-context workload, 512 chunks per sequence in 8 spans of 64 (256
+    # span-head units: the span maps run in 128-column slices, the output pass
+    # in 64-column ones)
     check(workload_inputs("gdn_bf16_long_b1_h32_t32768_d128"), 64, tag="workload 4")
 
 
 def test_split_output_pass_in_wide_slices_ragged():
     # 16 heads x 2 sequences x 8 spans of one chunk, the last one ragged: the
-    # output pass has more 32-column slices than CUs and runs 64-column ones
+    # output pass has more 32-column slices than CUs and runs 64-column ones,
+    # the span maps more 64-column slices than CUs and run 128-column ones
     inp = make_inputs(B=2, T=64 * 7 + 5, H=16, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True,
                       seed=3050)
     check(inp, 1, tag="wide output pass")
