@@ -374,6 +374,8 @@ def main():
     dom = max((k_ for k_ in ("prep", "scan") if k_ in kmean), key=lambda k_: kmean[k_])
     rl_dom = roofline(dom, *work[dom], kmean[dom] / 1e3, w.dtype)
     tkey = args.workload if args.rule == "delta" else f"{args.rule}_{args.workload}"
+    if args.heads > 0:   # the counter records hold the workloads' own head counts
+        tkey = f"{tkey}_h{args.heads}"
     rl_dom["traffic"] = measured_traffic(tkey, dom)
     # the metric is the call's % roofline: the whole call is the headline
     rl = roofline("call (" + " + ".join(k_ for k_ in kms if kmean[k_] > 0) + ")", *work["path"],
