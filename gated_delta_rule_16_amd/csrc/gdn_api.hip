@@ -384,8 +384,18 @@ gdn_status launch_split(const FwdArgs& a, int L, KernelTimer* tm) {
     // (1) span maps: DK identity rows with zero values, then the DV value rows
     // from zero; no outputs
     if (gdn_status s = launch_maps<T, DK, DV, C>(q, k, v, sg, a.H, NS, g_ws, Tb_ws, maps, a.stream, tm)) return s;
-    // (2) each span's start state, and S_T
-    {
+    // (2) each span's start state, and S_T: on MFMA for bf16 inputs (split
+    // products), on fp32 FMAs for fp32 ones
+    if constexpr (sizeof(T) == 2 && DK % 64 == 0 && DV % 16 == 0) {
+        using SC = SpanMfmaCfg<DK, DV>;
+        constexpr auto kc = gdn_span_chain_mfma_kernel<DK, DV>;
+        allow_smem<kc>(SC::SMEM);
+        tm->mark(a.stream);
+        hipLaunchKernelGGL(kc, dim3(DV / SC::ROWS, a.H, a.B), dim3(SC::THREADS), SC::SMEM, a.stream,
+                           maps, a.S0, (int)S.P, a.H, sin, a.S_T);
+        if (gdn_status s = check_launch(a.stream)) return s;
+        tm->mark(a.stream);
+    } else {
         using SC = SpanCfg<DK, DV>;
         constexpr auto kc = gdn_span_chain_kernel<DK, DV>;
         allow_smem<kc>(SC::SMEM);
@@ -506,15 +516,18 @@ gdn_status check_sizes(int rule, int B, int T, int H, int Dk, int Dv, int C, boo
 // scan's workgroups go from half the CUs to all of them,
 // with r1, r3 the rounds of workgroups each pass needs on the device (32-column
 // slices where they fill it, else 16-column ones; bf16: 64-column slices, at
-// their own step cost, where 32-column ones would need more than one round)
-// and f a kernel's fixed cost.  The split is taken at the best P when it is under 0.95 of the plain
-// estimate.  Measured (ms per call, plain -> split at the chosen span length):
-// bf16 D128 T = 32768: 4 heads 0.51 -> 0.15, 8 heads 0.53 -> 0.21, 16 heads
-// 0.58 -> 0.36, 32 heads 0.72 -> 0.645; 4 heads T = 4096 0.085 ->
-// 0.067; 16 heads T = 2048 0.057 (split 0.073: not taken); fp32 D64 B2 H4
-// T = 1024 0.078 -> 0.055; fp32 D128 B1 H2 T = 8192 0.693 -> 0.206, 16 heads
-// T = 4096 0.368 (split 0.568: not taken).  Packed batches always run the
-// plain scan.
+// their own step cost, where 32-column ones would need more than one round;
+// the span maps on 128-column slices where 64-column ones would) and f a
+// kernel's fixed cost.  The split is taken at the best P when it is under a
+// share of the plain estimate (bf16 0.90, fp32 0.95).  Measured (ms per call,
+// sums of the kernels' device times, plain -> split at the chosen span
+// length): bf16 D128 T = 32768: 2 heads 0.49 -> 0.125, 4 heads 0.51 -> 0.14,
+// 8 heads 0.53 -> 0.18, 16 heads 0.59 -> 0.32, 32 heads 0.66 -> 0.53; 4 heads
+// T = 4096 0.077 -> 0.063; 32 heads T = 16384 0.338 -> 0.315, T = 8192 0.168
+// (split 0.180: not taken); 16 heads T = 2048 0.057 (split 0.073: not taken);
+// fp32 D64 B2 H4 T = 1024 0.078 -> 0.055; fp32 D128 B1 H2 T = 8192 0.693 ->
+// 0.206, 16 heads T = 4096 0.368 (split 0.568: not taken).  Packed batches
+// always run the plain scan.
 struct SplitModel {
     int dk, dv, c;
     gdn_dtype dt;
@@ -522,11 +535,12 @@ struct SplitModel {
     double s_plain, s_full, s1, s3, c0, c1;   // microseconds
     double s1w, s3w;                          // 64-column slices (0: none)
     double s1m;                               // span maps on 128-column slices (0: none)
+    double take;                              // the split is taken under this share of plain
 };
 const SplitModel kSplitModels[] = {
-    {128, 128, 64, GDN_BF16, true, 1.05, 1.25, 0.95, 1.40, 2.5, 0.18, 1.05, 1.95, 1.50},
-    {64, 64, 64, GDN_F32, true, 3.30, 3.30, 4.00, 4.00, 0.8, 0.04, 0.0, 0.0, 0.0},
-    {128, 128, 64, GDN_F32, false, 5.00, 5.00, 5.00, 5.00, 2.0, 0.05, 0.0, 0.0, 0.0},
+    {128, 128, 64, GDN_BF16, true, 1.05, 1.25, 0.95, 1.40, 2.5, 0.10, 1.05, 1.95, 1.50, 0.90},
+    {64, 64, 64, GDN_F32, true, 3.30, 3.30, 4.00, 4.00, 0.8, 0.04, 0.0, 0.0, 0.0, 0.95},
+    {128, 128, 64, GDN_F32, false, 5.00, 5.00, 5.00, 5.00, 2.0, 0.05, 0.0, 0.0, 0.0, 0.95},
 };
 constexpr double kKernelFixedUs = 6.0;
 
@@ -558,7 +572,7 @@ int auto_span_chunks(int B, int T, int H, int Dk, int Dv, int C, gdn_dtype dt, b
         if (m->s1m > 0 && n * (cols / 64) > cus) return m->s1m * (double)((n * cols / 128 + cus - 1) / cus);
         return step(n, cols, m->s1, m->s1w);
     };
-    double best = 0.95 * plain;
+    double best = m->take * plain;
     int best_l = 0;
     for (int64_t P = 2; P <= cps && P <= 64; ++P) {
         const int64_t L = (cps + P - 1) / P, Pe = (cps + L - 1) / L;

@@ -12,12 +12,14 @@
 //     S_in(0) = S0,   S_in(p + 1) = S_in(p) M_p + b_p,   S_T = S_in(P),
 // writing each span's start state for the last pass, all in fp32.
 //
-// A workgroup owns 4 rows of one (sequence, head) state, so that short
-// batches still spread over the CUs; M_{p+1} is loaded into registers while
-// the product with M_p runs from LDS.
+// fp32 inputs (gdn_span_chain_kernel): a workgroup owns 4 rows of one
+// (sequence, head) state, so that short batches still spread over the CUs;
+// M_{p+1} is loaded into registers while the product with M_p runs from LDS,
+// on fp32 FMAs.  bf16 inputs (gdn_span_chain_mfma_kernel, below): 16 rows per
+// workgroup, the product on bf16 MFMAs with split operands.
 #pragma once
 
-#include "gdn_device.h"
+#include "gdn_ops.h"
 
 namespace gdn {
 
@@ -98,6 +100,163 @@ __global__ __launch_bounds__(256, 2) void gdn_span_chain_kernel(const float* __r
     if (S_T) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) S_T[srow + j] = s[j];
+    }
+}
+
+// The same chain on MFMA, for bf16 inputs (whose tolerance leaves room for
+// products of split operands): S_in(p + 1)^T = M_p^T S_in(p)^T + b_p^T, one
+// workgroup per 16 state rows of one (sequence, head), so that each M is read
+// by DV / 16 workgroups instead of DV / 4.  Per span, wave w forms output tile
+// t = w (columns 16 t .. 16 t + 15 of the 16 rows) with 16x16x16 bf16 MFMAs
+// over the DK / 16 blocks of d:
+//   A (lane (g, n)): M^T[16 t + n][16 kt + 4 g + r] = M[16 kt + 4 g + r][16 t + n]
+//   B (lane (g, n)): S^T[16 kt + 4 g + r][n], the accumulator layout of the
+//   previous span's tile kt (all waves' tiles pass through LDS),
+// each operand split as x = hi + lo (hi = bf16(x), lo = bf16(x - hi)) and the
+// product taken as hi hi + hi lo + lo hi, in three separate fp32 accumulation
+// chains per tile (about 2^-16 of relative error per product, fp32 sums).
+// Each wave loads its share of M_{p+3} and its lanes' piece of b_{p+3} into
+// one of two register sets at the end of span p, two spans before they are
+// needed, and writes the other set (M_{p+1}) to the free one of two LDS
+// buffers after the span's products; one barrier per span.
+template <int DK, int DV>
+struct SpanMfmaCfg {
+    static constexpr int ROWS = 16;
+    static constexpr int NT = DK / 16;             // 16-column tiles of a state row block
+    static constexpr int WAVES = NT, THREADS = WAVES * 64;   // one output tile per wave
+    static constexpr int MB = DK * DK * 4;         // bytes of one M (fp32)
+    static constexpr int NLD = MB / 1024 / WAVES;  // 16-byte loads per lane per span
+    static constexpr int SXB = NT * 1024;          // one exchange buffer of S^T tiles
+    static constexpr size_t OFF_SX = 2 * (size_t)MB;
+    static constexpr size_t SMEM = OFF_SX + 2 * (size_t)SXB;
+    static_assert(DK % 64 == 0 && (MB / 1024) % WAVES == 0 && DV % ROWS == 0 && THREADS <= 1024, "tile shapes");
+    static_assert(SMEM <= 160 * 1024, "LDS of one CU");
+};
+
+// LDS image of M (row-major, DK floats per row): 16-byte chunk j of row d sits
+// at chunk j ^ (4 ((d / 4) mod 4)), so that the 64 lanes of an A read (16
+// columns of four rows d = 4 g + r) fall in 64 different banks
+__device__ __forceinline__ int span_mchunk(int d, int j) { return j ^ (((d >> 2) & 3) << 2); }
+
+// maps, S0, S_in, S_T as for gdn_span_chain_kernel.  Grid (DV / 16, H, N).
+template <int DK, int DV>
+__global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain_mfma_kernel(
+    const float* __restrict__ maps, const float* S0, int P, int H, float* __restrict__ S_in, float* S_T) {
+    using Cfg = SpanMfmaCfg<DK, DV>;
+    using KO = K16<bf16>;
+    typedef typename KO::op Op;
+    constexpr int NT = Cfg::NT, NLD = Cfg::NLD;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int l = lane_id(), w = wave_id();
+    const int n = l & 15, g = l >> 4;
+    const int t = w;   // this wave's output tile
+    const int row0 = (int)blockIdx.x * Cfg::ROWS, h = (int)blockIdx.y, sq = (int)blockIdx.z;
+    const int64_t mstride = (int64_t)H * (DK + DV) * DK;                      // between spans
+    const float* m0 = maps + ((int64_t)sq * P * H + h) * (int64_t)(DK + DV) * DK;   // span 0
+    // this lane's piece of tile t (row row0 + n, columns 16 t + 4 g .. + 3)
+    // inside a [DV][DK] state
+    const int64_t soff = (int64_t)(row0 + n) * DK + 16 * t + 4 * g;
+    const int64_t st_base = (((int64_t)sq * H + h) * DV) * DK;
+    auto sin_at = [&](int p) __attribute__((always_inline)) {
+        return reinterpret_cast<f32x4*>(S_in + ((((int64_t)sq * P + p) * H + h) * DV) * DK + soff);
+    };
+
+    // M in registers: piece i of a set is the 16-byte chunk q = (w NLD + i) 64 + l
+    // of M; piece NLD is this lane's piece of b (the first accumulator of its tile)
+    f32x4 m0r[NLD + 1], m1r[NLD + 1];
+    auto m_load = [&](f32x4* mr, int p) __attribute__((always_inline)) {
+        const float* mp = m0 + p * mstride;
+        mr[NLD] = *reinterpret_cast<const f32x4*>(mp + (int64_t)DK * DK + soff);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) mr[i] = reinterpret_cast<const f32x4*>(mp)[(w * NLD + i) * 64 + l];
+    };
+    auto m_store = [&](const f32x4* mr, int buf) __attribute__((always_inline)) {
+        float* sm = reinterpret_cast<float*>(smem + (size_t)buf * Cfg::MB);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int q = (w * NLD + i) * 64 + l, d = q / (DK / 4), j = q % (DK / 4);
+            *reinterpret_cast<f32x4*>(sm + d * DK + 4 * span_mchunk(d, j)) = mr[i];
+        }
+    };
+    auto sx = [&](int buf, int tt) __attribute__((always_inline)) {
+        return reinterpret_cast<f32x4*>(smem + Cfg::OFF_SX + (size_t)buf * Cfg::SXB + tt * 1024) + l;
+    };
+    auto split = [&](f32x4 x, Op& hi, Op& lo) __attribute__((always_inline)) {
+        hi = KO::tile(x);
+        const bf16x4 hb = __builtin_bit_cast(bf16x4, hi);
+        lo = KO::tile(f32x4{x[0] - (float)hb[0], x[1] - (float)hb[1], x[2] - (float)hb[2], x[3] - (float)hb[3]});
+    };
+
+    // S_in(0) = S0 (zeros if NULL): this wave's tile to the exchange buffer and,
+    // when there is a span, to the first span's start state
+    {
+        const f32x4 s = S0 ? *reinterpret_cast<const f32x4*>(S0 + st_base + soff) : zero4();
+        *sx(0, t) = s;
+        if (P > 0) *sin_at(0) = s;
+        else if (S_T) *reinterpret_cast<f32x4*>(S_T + st_base + soff) = s;
+    }
+    f32x4 bcur = zero4();   // b_p of this lane's piece of tile t
+    if (P > 0) {
+        m_load(m0r, 0);
+        m_store(m0r, 0);
+        bcur = m0r[NLD];
+        m_load(m1r, min(1, P - 1));
+        m_load(m0r, min(2, P - 1));
+    }
+    __syncthreads();
+
+    // span p from LDS buffer p & 1 (the products of this wave's tile)
+    auto product = [&](int p) __attribute__((always_inline)) {
+        const float* sm = reinterpret_cast<const float*>(smem + (size_t)(p & 1) * Cfg::MB);
+        // b_p row row0 + n, columns 16 t + 4 g .. + 3 starts the first chain
+        f32x4 acc0 = bcur;
+        f32x4 acc1 = zero4(), acc2 = zero4();
+#pragma unroll
+        for (int kt = 0; kt < NT; ++kt) {
+            Op bh, bl, ah, al;
+            split(*sx(p & 1, kt), bh, bl);
+            f32x4 a;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * kt + 4 * g + r, c = 16 * t + n;
+                a[r] = sm[d * DK + 4 * span_mchunk(d, c >> 2) + (c & 3)];
+            }
+            split(a, ah, al);
+            acc0 = KO::mma1(ah, bh, acc0);
+            acc1 = KO::mma1(ah, bl, acc1);
+            acc2 = KO::mma1(al, bh, acc2);
+        }
+        return acc0 + (acc1 + acc2);
+    };
+    // a span with a successor: S_in(p + 1) out, M_{p+1} from register set nxt
+    // to the other LDS buffer (its M_{p-1} was read before the last barrier),
+    // the map two spans on into that set (past the end: the last one again).
+    // No branches, so that the waits for each set count only its own loads.
+    auto mid = [&](int p, f32x4* nxt) __attribute__((always_inline)) {
+        const f32x4 s = product(p);
+        *sx((p + 1) & 1, t) = s;
+        *sin_at(p + 1) = s;
+        m_store(nxt, (p + 1) & 1);
+        bcur = nxt[NLD];
+        m_load(nxt, min(p + 3, P - 1));
+        __syncthreads();
+    };
+    // the last span: S_T
+    auto last = [&](int p) __attribute__((always_inline)) {
+        const f32x4 s = product(p);
+        if (S_T) *reinterpret_cast<f32x4*>(S_T + st_base + soff) = s;
+    };
+    // two spans per iteration, so that each register set is a fixed one
+    int p = 0;
+    for (; p + 2 < P; p += 2) {
+        mid(p, m1r);
+        mid(p + 1, m0r);
+    }
+    if (p + 1 < P) {
+        mid(p, m1r);
+        last(p + 1);
+    } else if (p < P) {
+        last(p);
     }
 }
 

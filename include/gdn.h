@@ -121,7 +121,7 @@ size_t gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int Dk, int Dv, int C,
  * Long sequences with few units: for a fixed-length batch of bf16 with
  * Dk = Dv = 128 or fp32 with Dk = Dv = 64 or 128 (C = 64), where a cost model
  * of the two paths (per-step costs measured on MI355X) puts the split scan of
- * gdn_chunk_fwd_split under 0.95 of the plain one (few units, or few units per
+ * gdn_chunk_fwd_split under 0.90 (bf16) or 0.95 (fp32) of the plain one (few units, or few units per
  * CU over long sequences), the call runs that split scan, with the span length
  * gdn_chunk_fwd_auto_span_chunks reports, when the workspace holds
  * gdn_chunk_fwd_workspace_bytes(...) for these sizes, which then includes room
@@ -180,10 +180,12 @@ gdn_status gdn_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
  *      start at the identity and take zero values (they end as M) next to the
  *      Dv rows from zero (they end as b);
  *   2. per sequence, in span order: S_in(0) = S0, S_in(p+1) = S_in(p) M_p + b_p,
- *      S_T = S_in(last + 1) (fp32);
+ *      S_T = S_in(last + 1) (fp32 values; fp32 inputs: fp32 products, bf16
+ *      inputs: products of operands split into two bf16 parts, about 2^-16
+ *      relative error, fp32 sums);
  *   3. every span's outputs from its start state S_in(p).
  * The result equals gdn_chunk_fwd's up to rounding (passes 1 and 3 run the
- * same chunk arithmetic; pass 2 is an fp32 product).  Passes 1 and 3 hold
+ * same chunk arithmetic; pass 2 adds a rounding per span).  Passes 1 and 3 hold
  * (Dk + 2 Dv) / Dv times the state columns of one plain scan, spread over the
  * spans in parallel: it pays when B H Dv / 16 is well below the CU count, and
  * for long sequences that fill the device with few units (gdn_chunk_fwd's cost

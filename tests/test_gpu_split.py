@@ -83,6 +83,14 @@ def test_split_weak_gate_carries_state_across_spans():
     check(inp, 8, tag="weak gate")
 
 
+def test_split_weak_gate_long_chain():
+    # 32 spans of 4 chunks under a weak gate: the chained start states (bf16
+    # split products on MFMA) carry the state through every span
+    inp = make_inputs(B=1, T=8192, H=2, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True, seed=3160)
+    inp.log_alpha = torch.full_like(inp.log_alpha, -2e-4)
+    check(inp, 4, tag="weak gate, 32 spans")
+
+
 def test_split_deltanet_and_zero_state():
     inp = make_inputs(B=1, T=2000, H=2, Dk=128, Dv=128, dtype="bf16", gated=False, s0=False, seed=3200)
     check(inp, 4, tag="alpha=1, S0=0")
