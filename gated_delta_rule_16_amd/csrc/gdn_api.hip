@@ -6,7 +6,8 @@
 //   prep  (chunk slot, head)            g, Tb = T diag(beta)   (independent chunks)
 //   scan  (Dv slice, head, sequence)    O, S_T                 (serial over chunks)
 // gdn_mamba2_chunk_fwd (the no-erase rule) replaces prep by the gates kernel
-// (g and beta per chunk) and runs the same scan without the prediction step.
+// (g and beta per chunk; the scan's 64-column and fp32 slices form them
+// themselves instead) and runs the same scan without the prediction step.
 // gdn_gla_chunk_fwd (per-channel gate) replaces it by the GLA prep kernel
 // (Q~, K^, P~ and the chunk decay per chunk) and runs the scan on those.
 #include <hip/hip_runtime.h>
@@ -164,7 +165,7 @@ struct KernelTimer {
 template <typename T, int DK, int DV, int C, int RULE>
 gdn_status launch_scan(const T* q, const T* k, const T* v, const float* S0, const SeqGeom& geom,
                        int H, int64_t n_seqs, const float* g_ws, const T* Tb_ws, T* O, float* S_T,
-                       ScanRows rows, hipStream_t stream, KernelTimer* tm) {
+                       ScanRows rows, hipStream_t stream, KernelTimer* tm, RawGates raw = RawGates{}) {
     using C32 = ColCfg<T, DK, DV, C, (DV >= 32 ? 32 : 16), RULE>;
     using C16 = ColCfg<T, DK, DV, C, 16, RULE>;
     constexpr bool fit32 = DV >= 32 && C32::FITS, fit16 = C16::FITS;
@@ -174,10 +175,23 @@ gdn_status launch_scan(const T* q, const T* k, const T* v, const float* S0, cons
         if constexpr (CC::FITS) {
             constexpr int DVT = CC::NVW * 16;
             constexpr auto ks = gdn_scan_cols_kernel<T, DK, DV, C, DVT, RULE>;
+            if constexpr (RULE == kNoErase && !CC::GATES_INLINE) {
+                // the gate rows of every chunk, before a scan that stages them
+                constexpr int WPB = kThreads / 64;
+                const int64_t gu = raw.slots * H;
+                tm->mark(stream);
+                if (gu > 0) {
+                    hipLaunchKernelGGL(gdn_gates_kernel<C>, dim3((unsigned)((gu + WPB - 1) / WPB)), dim3(kThreads),
+                                       0, stream, raw.log_alpha, raw.beta, geom, H, (int)gu,
+                                       const_cast<float*>(g_ws));
+                    if (gdn_status s = check_launch(stream)) return s;
+                }
+                tm->mark(stream);
+            }
             allow_smem<ks>(CC::SMEM);
             tm->mark(stream);
             hipLaunchKernelGGL(ks, dim3(DV / DVT, H, (unsigned)n_seqs), dim3(CC::NTHR), CC::SMEM, stream,
-                               q, k, v, S0, geom, H, g_ws, Tb_ws, O, S_T, rows);
+                               q, k, v, S0, geom, H, g_ws, Tb_ws, O, S_T, rows, raw);
             if (gdn_status s = check_launch(stream)) return s;
             tm->mark(stream);
             return GDN_OK;
@@ -225,7 +239,7 @@ gdn_status launch_maps(const T* q, const T* k, const T* v, const SeqGeom& geom, 
             tm->mark(stream);
             hipLaunchKernelGGL(ks, dim3((DK + DV) / 128, H, (unsigned)n_seqs), dim3(CM::NTHR), CM::SMEM, stream,
                                q, k, v, (const float*)nullptr, geom, H, g_ws, Tb_ws, (T*)nullptr, maps,
-                               ScanRows{DK, DV});
+                               ScanRows{DK, DV}, RawGates{});
             if (gdn_status s = check_launch(stream)) return s;
             tm->mark(stream);
             return GDN_OK;
@@ -287,17 +301,6 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         k = kh;
     }
 
-    if constexpr (RULE == kNoErase) {
-        constexpr int WPB = kThreads / 64;
-        const int64_t units = L.slots * a.H;
-        tm->mark(a.stream);
-        if (units > 0) {
-            hipLaunchKernelGGL(gdn_gates_kernel<C>, dim3((unsigned)((units + WPB - 1) / WPB)), dim3(kThreads), 0,
-                               a.stream, a.log_alpha, a.beta, geom, a.H, (int)units, g_ws);
-            if (gdn_status s = check_launch(a.stream)) return s;
-        }
-        tm->mark(a.stream);
-    }
     if constexpr (RULE == kDelta) if (L.slots > 0) {
         using P = PrepCfg<T, DK, C>;
         constexpr auto kp = gdn_prep_kernel<T, DK, C>;
@@ -314,9 +317,12 @@ gdn_status launch_fwd(const FwdArgs& a, KernelTimer* tm) {
         if (gdn_status s = check_launch(a.stream)) return s;
         tm->mark(a.stream);
     }
+    // the no-erase rule: its gate rows (formed by the scan itself, or by the
+    // gates kernel launch_scan runs first)
+    const RawGates raw = RULE == kNoErase ? RawGates{a.log_alpha, a.beta, L.slots} : RawGates{};
     return launch_scan<T, DK, DV, C, RULE>(q, k, v, a.S0, geom, a.H, L.N, g_ws, Tb_ws,
                                            static_cast<T*>(a.O), a.S_T, ScanRows{0, DV}, a.stream,
-                                           tm);
+                                           tm, raw);
 }
 
 // ---------------------------------------------------------------------------

@@ -115,9 +115,6 @@ struct ColCfg {
     static constexpr int NIK = blocks(C * LDK * ES), NIV = blocks(C * LDV * ES);
     static constexpr int NIT = HAS_TB ? tb_blocks(C, BF) : 0, NIG = blocks(GF * 4);
     static constexpr int BT = NIK, BV = BT + NIT, BG = BV + NIV, NI = BG + NIG;
-    static constexpr int NL = cdiv(NI, NLD);               // loads per loading lane per chunk
-    // loads loading wave f issues per chunk
-    static constexpr int nload(int f) { return NI / NLD + (f < NI % NLD ? 1 : 0); }
     static constexpr size_t SZ_STAGE = (size_t)NI * 1024;
     static constexpr size_t OFF_T = (size_t)BT * 1024, OFF_V = (size_t)BV * 1024, OFF_G = (size_t)BG * 1024;
     // column-wave hand-over, lane by lane in MFMA operand form (one tile is 64
@@ -144,6 +141,17 @@ struct ColCfg {
         return ns * SZ_STAGE + SZ_REST + (q ? 2 * SZ_Q : 0) <= 160 * 1024 && cdiv(NI, NLD) * (ns - 2) < 64;
     }
     static constexpr bool QLDS = !MAPS && fits(3, true);
+    // The no-erase rule's gate rows: where the writing wave stages no Q (no
+    // QLDS) it forms them itself in each chunk's staging buffer from log alpha
+    // and beta (RawGates), and the loaders stage only the blocks before the
+    // gate region; elsewhere a per-chunk kernel writes them before the scan
+    // (next to its Q pipeline the writing wave's loads would not keep their
+    // order, and the scan measured slower)
+    static constexpr bool GATES_INLINE = RULE == kNoErase && !QLDS;
+    static constexpr int NIL = GATES_INLINE ? BG : NI;    // blocks loaded per chunk
+    static constexpr int NL = cdiv(NIL, NLD);              // loads per loading lane per chunk
+    // loads loading wave f issues per chunk
+    static constexpr int nload(int f) { return NIL / NLD + (f < NIL % NLD ? 1 : 0); }
     static constexpr int NSTG = QLDS ? 3 : fits(4, false) ? 4 : fits(3, false) ? 3 : 2;
     static constexpr int DIST = NSTG - 1;                  // chunks staged ahead
     static constexpr size_t OFF_QB = NSTG * SZ_STAGE, OFF_SB = OFF_QB + (QLDS ? 2 * SZ_Q : 0);
@@ -252,12 +260,22 @@ struct ScanRows {
     int vz, vld;
 };
 
+// Per-token gates of the no-erase rule: log_alpha (NULL: 0) and beta (NULL:
+// 1), [tokens][H] fp32, and the call's chunk slots.  Where the scan's
+// configuration forms the gate rows itself (ColCfg::GATES_INLINE), its writing
+// wave reads them; elsewhere the launcher runs the per-chunk gates kernel
+// first.
+struct RawGates {
+    const float *log_alpha, *beta;
+    int64_t slots;
+};
+
 template <typename T, int DK, int DV, int C, int DVT, int RULE>
 __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_scan_cols_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* S0, SeqGeom geom, int H,
     const float* __restrict__ g_ws, const T* __restrict__ Tb_ws,
-    T* __restrict__ O, float* S_T, ScanRows rows) {   // S_T may alias S0
+    T* __restrict__ O, float* S_T, ScanRows rows, RawGates raw) {   // S_T may alias S0
     using Cfg = ColCfg<T, DK, DV, C, DVT, RULE>;
     static_assert(Cfg::FITS, "scan workgroup exceeds the LDS of one CU");
     using St16 = Step<T>;
@@ -858,7 +876,47 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
         // vmcnt with the stores, leaves the newer stores in flight.)  Past the
         // end the last chunk is re-read (the same values).
         static_assert(ND * (Cfg::DIST - 1) < 64, "vmcnt range");
+        // no-erase rule: the writing wave forms chunk cd's gate rows (g, e^g,
+        // e^(g_n - g), beta; lane = token, rows past the chunk end as tokens with
+        // log alpha = 0 and beta = 0) in its staging buffer, from the inputs it
+        // requested a step before (gate_issue).  The loads take no branch (a
+        // NULL input reads as an empty range), so that the waits the compiler
+        // places for them and for the Q register sets count exactly.
+        constexpr bool GW = !LOADER && Cfg::GATES_INLINE;
+        float g_la = 0.f, g_be = 0.f;
+        auto gate_issue = [&](int cd) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const int64_t row0 = (int64_t)t0 * H + h;
+            const int gbytes = ((len - 1) * H + 1) * 4;
+            const uint32_t goff = l < C ? (uint32_t)(l * H * 4) : kOutOfRange;
+            const float* la = raw.log_alpha ? raw.log_alpha + row0 : nullptr;
+            const float* be = raw.beta ? raw.beta + row0 : nullptr;
+            g_la = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(la, la ? gbytes : 0), goff, 0, 0));
+            const float b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(be, be ? gbytes : 0), goff, 0, 0));
+            g_be = be ? b : (l < len ? 1.f : 0.f);
+        };
+        auto gate_commit = [&](int cd) __attribute__((always_inline)) {
+            float gs = g_la;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(gs, off, 64);
+                if (l >= off) gs += y;
+            }
+            const float glast = __shfl(gs, C - 1, 64);
+            float* gb = reinterpret_cast<float*>(smem + (cd % Cfg::NSTG) * Cfg::SZ_STAGE + Cfg::OFF_G);
+            if (l < C) {
+                gb[l] = gs;
+                gb[C + l] = __expf(gs);
+                gb[2 * C + l] = __expf(glast - gs);
+                gb[3 * C + l] = g_be;
+            }
+        };
         if (count > 0) {
+            if constexpr (GW) {
+                gate_issue(0);
+                gate_commit(0);
+                gate_issue(min(1, count - 1));
+            }
             if constexpr (LOADER) {
 #pragma unroll
                 for (int d = 0; d < Cfg::DIST; ++d) stage(min(d, count - 1));
@@ -875,6 +933,11 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
         }
         __syncthreads();
         auto writer_step = [&](int cc, u32x4* qr) __attribute__((always_inline)) {
+            // past the end the last chunk's gates are formed again (the same values)
+            if constexpr (GW) {
+                gate_commit(min(cc + 1, count - 1));
+                gate_issue(min(cc + 2, count - 1));
+            }
             if constexpr (QW) {
                 if (!no_out) {
                     q_commit(qr, min(cc + 1, count - 1));

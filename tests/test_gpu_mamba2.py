@@ -116,3 +116,34 @@ def test_mamba2_wide_slices():
     inp = make_inputs(B=8, T=300, H=32, Dk=128, Dv=128, dtype="bf16", gated=True, s0=True,
                       seed=420)
     check(inp, "bf16", tag="64-column slices")
+
+
+# Where the scan's writing wave stages no Q (64-column bf16 slices, 32-column
+# fp32 D64 slices) it forms each chunk's gate rows itself from log alpha and
+# beta instead of a gates kernel; these cases reach that path.
+def test_mamba2_f32_d64_two_column_waves():
+    # 256 (sequence, head) units: fp32 D64 32-column slices (compiled for C = 64)
+    inp = make_inputs(B=4, T=200, H=64, Dk=64, Dv=64, dtype="f32", gated=True, s0=True, seed=650)
+    check(inp, "f32", tag="fp32 D64 32-column slices")
+
+
+@pytest.mark.parametrize("case", ["beta1", "linear", "decay30", "resets"])
+def test_mamba2_wide_gate_cases(case):
+    # 64-column slices with beta NULL, log alpha NULL, and gates at the edges
+    # of the exponentials' range
+    inp = make_inputs(B=8, T=136, H=32, Dk=128, Dv=128, dtype="bf16", gated=case != "linear",
+                      s0=case != "linear", seed=660)
+    if case == "decay30":
+        inp.log_alpha = torch.full_like(inp.log_alpha, -30.0)
+    elif case == "resets":
+        inp.log_alpha = torch.zeros_like(inp.log_alpha)
+        inp.log_alpha[:, 5::37] = -80.0
+    check(inp, "bf16", beta_none=case in ("beta1", "linear"), tag=f"64-column slices, {case}")
+
+
+def test_mamba2_wide_varlen_short_and_empty():
+    # packed sequences of 0 .. 200 tokens over 32 heads: 64-column slices
+    lengths = [0, 1, 63, 64, 65, 200, 0, 7, 130]
+    inp = make_inputs(B=1, T=sum(lengths), H=32, Dk=128, Dv=128, dtype="bf16", gated=True,
+                      s0=True, seed=670, lengths=lengths)
+    check(inp, "bf16", tag=f"64-column slices, varlen {lengths}")
