@@ -128,6 +128,11 @@ struct ColCfg {
     static constexpr int LDO = DVT * ES + 16;                  // row pitch (bytes)
     static constexpr int OPR = DVT * ES / 16;                  // 16-byte pieces per row
     static constexpr int NOPL = cdiv(C * OPR, 64);             // pieces per writing lane
+    // cache policy of the output stores: a slice row of less than a 128-byte
+    // line leaves the rest of the line to the neighbouring slices, so its
+    // stores stay in L2 (which holds a unit's slices) until the line is whole;
+    // whole lines stream past the caches (nontemporal)
+    static constexpr int OAUX = DVT * ES < 128 ? 0 : 2;
     static constexpr size_t SZ_O = MAPS ? 0 : (size_t)C * LDO;
     // Q of a chunk: staged by the loader one chunk ahead in two LDS buffers
     // (rows as K's) where that fits next to three staging buffers (QLDS), else
@@ -849,7 +854,7 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
                     asm volatile("ds_write_b128 %0, %1" ::"v"(base + j * Cfg::NLD * 1024), "v"(qr[j]) : "memory");
         };
         // chunk cd's output slice from LDS to memory, 16 bytes per lane, rows
-        // past the chunk end dropped by the buffer range; streamed past the caches
+        // past the chunk end dropped by the buffer range (cache policy OAUX)
         auto write_out = [&](int cd) __attribute__((always_inline)) {
             const int t0 = ts + cd * C, len = min(C, te - t0);
             const __amdgpu_buffer_rsrc_t ro =
@@ -861,7 +866,7 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
                 if (Cfg::NOPL * 64 == C * Cfg::OPR || piece < C * Cfg::OPR) {
                     const int r = piece / Cfg::OPR, b = piece - r * Cfg::OPR;
                     const u32x4 d = *reinterpret_cast<const u32x4*>(ob + r * Cfg::LDO + b * 16);
-                    __builtin_amdgcn_raw_buffer_store_b128(d, ro, (uint32_t)(r * rs_v) + b * 16, 0, 2);
+                    __builtin_amdgcn_raw_buffer_store_b128(d, ro, (uint32_t)(r * rs_v) + b * 16, 0, Cfg::OAUX);
                 }
             }
         };
