@@ -90,6 +90,13 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, unsigned ch
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
+// 4 bytes per lane from a buffer straight into LDS (lane l's at lds + 4 l);
+// otherwise as lds_load16
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+
 // XOR swizzles of 16-byte blocks in LDS rows: data block b of row r sits at
 // block b ^ swz(r).  Kinds: 0 none; 1 (K / Q rows of 8+ blocks) 2 (r mod 4) +
 // (r / 4 mod 2); 2 (V rows of 4+ blocks) 2 (r / 2 mod 2); 3 (Tb / X^T rows of 8+

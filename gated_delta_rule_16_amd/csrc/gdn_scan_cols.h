@@ -149,10 +149,14 @@ struct ColCfg {
     // The no-erase rule's gate rows: where the writing wave stages no Q (no
     // QLDS) it forms them itself in each chunk's staging buffer from log alpha
     // and beta (RawGates), and the loaders stage only the blocks before the
-    // gate region; elsewhere a per-chunk kernel writes them before the scan
-    // (next to its Q pipeline the writing wave's loads would not keep their
-    // order, and the scan measured slower)
-    static constexpr bool GATES_INLINE = RULE == kNoErase && !QLDS;
+    // gate region; with QLDS, for fp32 and C = 64, the loading wave forms them
+    // (GATES_BY_LOADER); elsewhere a per-chunk kernel writes them before the
+    // scan.  Next to its Q pipeline the writing wave's loads would not keep
+    // their order; for bf16 the loading wave's reads of the gates (a line per
+    // token, in every column slice of a unit) cost the scan more than the
+    // gates kernel takes, while fp32's longer chunk step absorbs them.
+    static constexpr bool GATES_BY_LOADER = RULE == kNoErase && QLDS && C == 64 && !BF;
+    static constexpr bool GATES_INLINE = RULE == kNoErase && (!QLDS || GATES_BY_LOADER);
     static constexpr int NIL = GATES_INLINE ? BG : NI;    // blocks loaded per chunk
     static constexpr int NL = cdiv(NIL, NLD);              // loads per loading lane per chunk
     // loads loading wave f issues per chunk
@@ -162,7 +166,10 @@ struct ColCfg {
     static constexpr size_t OFF_QB = NSTG * SZ_STAGE, OFF_SB = OFF_QB + (QLDS ? 2 * SZ_Q : 0);
     static constexpr size_t OFF_VO = OFF_SB + 2 * SZ_SB;
     static constexpr size_t OFF_O = OFF_VO + 2 * SZ_VO;
-    static constexpr size_t SMEM = OFF_O + 2 * SZ_O;
+    // the no-erase rule's raw gates (log alpha, beta) where the loading wave
+    // forms the gate rows: three slots of 2 C floats
+    static constexpr size_t OFF_RG = OFF_O + 2 * SZ_O;
+    static constexpr size_t SMEM = OFF_RG + (GATES_BY_LOADER ? 3 * 2 * C * 4 : 0);
     static constexpr bool FITS = SMEM <= 160 * 1024;
     // output helper of query block qb: 0 takes blocks 0 and NW - 1, 1 the middle
     // ones (wide slices: helper qb)
@@ -182,8 +189,10 @@ struct ColCfg {
     }
     static constexpr int NQB = NPP >= NW ? 1 : (NW + 1) / 2;   // query blocks per helper, at most
     // Q register sets without QLDS: three where a set takes at most 32 registers,
-    // two below 64, else one (fp32 with Dk = 128: two sets would spill)
-    static constexpr int NQS = NQB * NKK * 16 <= 128 ? 3 : NQB * NKK * 16 < 256 ? 2 : 1;
+    // two below 64, else one (fp32 with Dk = 128: two sets would spill); the
+    // wide slices one (with three, their ten-wave budget of 168 registers
+    // spilled loop invariants, and each reload waited for every load in flight)
+    static constexpr int NQS = WIDE ? 1 : NQB * NKK * 16 <= 128 ? 3 : NQB * NKK * 16 < 256 ? 2 : 1;
     static_assert(C % 16 == 0 && NW >= 1 && NW <= 4 && NVW >= 1 && (NVW <= 4 || MAPS) && NPP <= 4, "tile counts");
     static_assert(DV % DVT == 0 && DVT % 16 == 0 && DK % KS == 0 && DK % 16 == 0, "tile shapes");
     static_assert(!BF || (C % 32 == 0 && KB % 8 == 0 && (VB % 4 == 0 || VB == 2) && DK % 32 == 0),
@@ -268,8 +277,8 @@ struct ScanRows {
 // Per-token gates of the no-erase rule: log_alpha (NULL: 0) and beta (NULL:
 // 1), [tokens][H] fp32, and the call's chunk slots.  Where the scan's
 // configuration forms the gate rows itself (ColCfg::GATES_INLINE), its writing
-// wave reads them; elsewhere the launcher runs the per-chunk gates kernel
-// first.
+// wave (or, with GATES_BY_LOADER, its loading wave) reads them; elsewhere the
+// launcher runs the per-chunk gates kernel first.
 struct RawGates {
     const float *log_alpha, *beta;
     int64_t slots;
@@ -887,7 +896,7 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
         // requested a step before (gate_issue).  The loads take no branch (a
         // NULL input reads as an empty range), so that the waits the compiler
         // places for them and for the Q register sets count exactly.
-        constexpr bool GW = !LOADER && Cfg::GATES_INLINE;
+        constexpr bool GW = Cfg::GATES_INLINE && (Cfg::GATES_BY_LOADER ? LOADER : !LOADER);
         float g_la = 0.f, g_be = 0.f;
         auto gate_issue = [&](int cd) __attribute__((always_inline)) {
             const int t0 = ts + cd * C, len = min(C, te - t0);
@@ -897,8 +906,14 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
             const float* la = raw.log_alpha ? raw.log_alpha + row0 : nullptr;
             const float* be = raw.beta ? raw.beta + row0 : nullptr;
             g_la = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(la, la ? gbytes : 0), goff, 0, 0));
-            const float b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(be, be ? gbytes : 0), goff, 0, 0));
-            g_be = be ? b : (l < len ? 1.f : 0.f);
+            g_be = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(be, be ? gbytes : 0), goff, 0, 0));
+        };
+        // beta of lane l in chunk cd: as loaded, or 1 inside the chunk where
+        // beta is NULL (chosen where the rows are written, so that no wait for
+        // the load is placed where it is issued)
+        auto gate_beta = [&](int cd, float b) __attribute__((always_inline)) {
+            const int len = min(C, te - (ts + cd * C));
+            return raw.beta ? b : (l < len ? 1.f : 0.f);
         };
         auto gate_commit = [&](int cd) __attribute__((always_inline)) {
             float gs = g_la;
@@ -913,20 +928,78 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
                 gb[l] = gs;
                 gb[C + l] = __expf(gs);
                 gb[2 * C + l] = __expf(glast - gs);
-                gb[3 * C + l] = g_be;
+                gb[3 * C + l] = gate_beta(cd, g_be);
             }
         };
+        // the same rows formed by the loading wave, which has direct-to-LDS loads
+        // in flight (the compiler waits for all of them before any LDS access it
+        // knows of): log alpha and beta arrive direct-to-LDS too, 4 bytes per
+        // lane, in one of three slots (chunk index mod 3: a chunk's inputs are
+        // requested while those of the two before it may be unread), and the
+        // rows are formed from them with inline-assembly LDS reads and writes
+        // and a DPP prefix sum (row shifts, then row broadcasts).  C = 64: one
+        // lane per token.
+        auto rg_slot = [&](int x) __attribute__((always_inline)) { return smem + Cfg::OFF_RG + (x % 3) * (2 * C * 4); };
+        auto rg_issue = [&](int cd, int x) __attribute__((always_inline)) {
+            const int t0 = ts + cd * C, len = min(C, te - t0);
+            const int64_t row0 = (int64_t)t0 * H + h;
+            const int gbytes = ((len - 1) * H + 1) * 4;
+            const uint32_t goff = l < C ? (uint32_t)(l * H * 4) : kOutOfRange;
+            const float* la = raw.log_alpha ? raw.log_alpha + row0 : nullptr;
+            const float* be = raw.beta ? raw.beta + row0 : nullptr;
+            lds_load4(make_rsrc(la, la ? gbytes : 0), rg_slot(x), goff);
+            lds_load4(make_rsrc(be, be ? gbytes : 0), rg_slot(x) + C * 4, goff);
+        };
+        auto rg_commit = [&](int cd, int x) __attribute__((always_inline)) {
+            static_assert(!GW || !LOADER || C == 64, "one lane per token");
+            typedef __attribute__((address_space(3))) unsigned char lds_u8;
+            const uint32_t ra = (uint32_t)(uintptr_t)(lds_u8*)rg_slot(x) + l * 4;
+            float gs, b;
+            asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:256\n\ts_waitcnt lgkmcnt(0)"
+                         : "=&v"(gs), "=&v"(b) : "v"(ra) : "memory");
+            auto dpp = [](float v, auto ctrl, auto rmask) __attribute__((always_inline)) {
+                return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                             decltype(ctrl)::value, decltype(rmask)::value, 0xf, true));
+            };
+            gs += dpp(gs, std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{});   // row_shr:1
+            gs += dpp(gs, std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{});   // row_shr:2
+            gs += dpp(gs, std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{});   // row_shr:4
+            gs += dpp(gs, std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{});   // row_shr:8
+            gs += dpp(gs, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{});   // row_bcast:15
+            gs += dpp(gs, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{});   // row_bcast:31
+            const float glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gs), C - 1));
+            const uint32_t a0 = (uint32_t)(uintptr_t)(lds_u8*)(smem + (cd % Cfg::NSTG) * Cfg::SZ_STAGE + Cfg::OFF_G) + l * 4;
+            const float ge = __expf(gs), gd = __expf(glast - gs), bv = gate_beta(cd, b);
+            asm volatile("ds_write_b32 %0, %1" ::"v"(a0), "v"(gs) : "memory");
+            asm volatile("ds_write_b32 %0, %1" ::"v"(a0 + C * 4), "v"(ge) : "memory");
+            asm volatile("ds_write_b32 %0, %1" ::"v"(a0 + 2 * C * 4), "v"(gd) : "memory");
+            asm volatile("ds_write_b32 %0, %1" ::"v"(a0 + 3 * C * 4), "v"(bv) : "memory");
+        };
         if (count > 0) {
-            if constexpr (GW) {
+            if constexpr (LOADER && GW) {
+                // the loads in the order of the steps (the raw gates of chunk
+                // x + 2 ahead of the staging of chunk x + 1), then the rows of
+                // chunks 0 and 1
+                static_assert(Cfg::DIST == 2 && 2 * ND + 2 < 64, "staging two chunks ahead, vmcnt range");
+                rg_issue(0, 0);
+                rg_issue(min(1, count - 1), 1);
+                stage(0);
+                rg_issue(min(2, count - 1), 2);
+                stage(min(1, count - 1));
+                wait_vm_lgkm0<2 * ND + 2>();   // the raw gates of chunks 0 and 1
+                rg_commit(0, 0);
+                rg_commit(min(1, count - 1), 1);
+                wait_vm_lgkm0<ND + 2>();       // chunk 0's staging
+            } else if constexpr (GW) {
                 gate_issue(0);
                 gate_commit(0);
                 gate_issue(min(1, count - 1));
             }
-            if constexpr (LOADER) {
+            if constexpr (LOADER && !GW) {
 #pragma unroll
                 for (int d = 0; d < Cfg::DIST; ++d) stage(min(d, count - 1));
                 wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();
-            } else if constexpr (QW) {
+            } else if constexpr (!LOADER && QW) {
                 if (!no_out) {
                     q_issue(qreg[0], 0);
                     q_commit(qreg[0], 0);
@@ -953,7 +1026,20 @@ __global__ __launch_bounds__((ColCfg<T, DK, DV, C, DVT, RULE>::BOUND)) void gdn_
             wait_vm_lgkm0<63>();
             barrier();
         };
-        if constexpr (LOADER) {
+        if constexpr (LOADER && GW) {
+            // step cc: the raw gates of chunk cc + 3 and the staging of chunk
+            // cc + 2; then chunk cc + 2's rows from its raw gates (requested a
+            // step before, ahead of chunk cc + 1's staging, so the wait does not
+            // hang on that) into its staging buffer, free since the last barrier
+            for (int cc = 0; cc < count; ++cc) {
+                rg_issue(min(cc + 3, count - 1), cc + 3);
+                stage(min(cc + 2, count - 1));
+                wait_vm_lgkm0<2 * ND + 2>();
+                rg_commit(min(cc + 2, count - 1), cc + 2);
+                wait_vm_lgkm0<ND + 2>();   // chunk cc + 1's staging
+                barrier();
+            }
+        } else if constexpr (LOADER) {
             for (int cc = 0; cc < count; ++cc) {
                 stage(min(cc + Cfg::DIST, count - 1));
                 wait_vm_lgkm0<ND * (Cfg::DIST - 1)>();

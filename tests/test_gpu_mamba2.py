@@ -108,7 +108,8 @@ def test_mamba2_profiled_matches_plain_call():
                                                  d.beta, d.S0)
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(S1, S2)
-    assert ms[1] > 0 and ms[2] > 0
+    # ms[1]: the gates kernel, or 0 where the scan forms the gate rows itself
+    assert ms[1] >= 0 and ms[2] > 0
 
 
 def test_mamba2_wide_slices():
