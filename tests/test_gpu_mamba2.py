@@ -148,3 +148,22 @@ def test_mamba2_wide_varlen_short_and_empty():
     inp = make_inputs(B=1, T=sum(lengths), H=32, Dk=128, Dv=128, dtype="bf16", gated=True,
                       s0=True, seed=670, lengths=lengths)
     check(inp, "bf16", tag=f"64-column slices, varlen {lengths}")
+
+
+# fp32 with C = 64 in 16-column slices (Q staged in LDS): the loading wave forms
+# the gate rows from log alpha and beta it stages itself; packed sequences of
+# every length class and gates at the edges of the exponentials' range
+@pytest.mark.parametrize("case", ["varlen", "decay30", "resets", "beta1"])
+def test_mamba2_f32_loader_gate_rows(case):
+    if case == "varlen":
+        lengths = [0, 1, 63, 64, 65, 200, 0, 7, 130]
+        inp = make_inputs(B=1, T=sum(lengths), H=2, Dk=64, Dv=64, dtype="f32", gated=True,
+                          s0=True, seed=680, lengths=lengths)
+    else:
+        inp = make_inputs(B=2, T=200, H=2, Dk=64, Dv=64, dtype="f32", gated=True, s0=True, seed=681)
+        if case == "decay30":
+            inp.log_alpha = torch.full_like(inp.log_alpha, -30.0)
+        elif case == "resets":
+            inp.log_alpha = torch.zeros_like(inp.log_alpha)
+            inp.log_alpha[:, 5::37] = -80.0
+    check(inp, "f32", beta_none=case == "beta1", tag=f"fp32 D64 16-column slices, {case}")
