@@ -286,8 +286,9 @@ gdn_status gdn_gla_chunk_fwd(const void *q, const void *k, const void *v,
 /* gdn_chunk_fwd_profiled for the entry point of `rule` (same arguments as
  * that entry point, then kernel_ms; kernel_ms[1] is the per-chunk preparation
  * of that rule: prep for GDN_RULE_DELTA, the gates kernel for
- * GDN_RULE_MAMBA2, the GLA prep kernel for GDN_RULE_GLA).  Blocks until the
- * call's work has finished. */
+ * GDN_RULE_MAMBA2 (0 where the scan forms the gate rows itself, as it does
+ * for the 64-column bf16 slices and for fp32 with C = 64), the GLA prep
+ * kernel for GDN_RULE_GLA).  Blocks until the call's work has finished. */
 gdn_status gdn_rule_chunk_fwd_profiled(gdn_rule rule, const void *q, const void *k, const void *v,
                                        const float *log_alpha, const float *beta, const float *S0,
                                        const int32_t *cu_seqlens, int n_seqs,
