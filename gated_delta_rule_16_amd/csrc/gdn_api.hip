@@ -397,7 +397,7 @@ gdn_status launch_split(const FwdArgs& a, int L, KernelTimer* tm) {
         constexpr auto kc = gdn_span_chain_mfma_kernel<DK, DV>;
         allow_smem<kc>(SC::SMEM);
         tm->mark(a.stream);
-        hipLaunchKernelGGL(kc, dim3(DV / SC::ROWS, a.H, a.B), dim3(SC::THREADS), SC::SMEM, a.stream,
+        hipLaunchKernelGGL(kc, dim3(a.H, DV / SC::ROWS, a.B), dim3(SC::THREADS), SC::SMEM, a.stream,
                            maps, a.S0, (int)S.P, a.H, sin, a.S_T);
         if (gdn_status s = check_launch(a.stream)) return s;
         tm->mark(a.stream);
@@ -406,7 +406,7 @@ gdn_status launch_split(const FwdArgs& a, int L, KernelTimer* tm) {
         constexpr auto kc = gdn_span_chain_kernel<DK, DV>;
         allow_smem<kc>(SC::SMEM);
         tm->mark(a.stream);
-        hipLaunchKernelGGL(kc, dim3(DV / SC::ROWS, a.H, a.B), dim3(SC::THREADS), SC::SMEM, a.stream,
+        hipLaunchKernelGGL(kc, dim3(a.H, DV / SC::ROWS, a.B), dim3(SC::THREADS), SC::SMEM, a.stream,
                            maps, a.S0, (int)S.P, a.H, sin, a.S_T);
         if (gdn_status s = check_launch(a.stream)) return s;
         tm->mark(a.stream);

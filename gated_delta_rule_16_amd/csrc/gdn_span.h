@@ -17,6 +17,11 @@
 // M_{p+1} is loaded into registers while the product with M_p runs from LDS,
 // on fp32 FMAs.  bf16 inputs (gdn_span_chain_mfma_kernel, below): 16 rows per
 // workgroup, the product on bf16 MFMAs with split operands.
+//
+// Both grids put the head first (H, row blocks, sequences): workgroups go to
+// the 8 XCDs round-robin by linear id, so the row blocks of one head, H ids
+// apart, share an XCD when H is a multiple of 8 (two XCDs for H = 4), and its
+// L2 fetches each span's map once for all of them.
 #pragma once
 
 #include "gdn_ops.h"
@@ -38,7 +43,7 @@ struct SpanCfg {
 
 // maps: [N * P][H][DK + DV][DK] (rows 0 .. DK-1: M_p, rows DK .. DK+DV-1: b_p);
 // S0 (nullable, zeros) and S_T (nullable): [N][H][DV][DK]; S_in: [N * P][H][DV][DK].
-// Grid (DV / 4, H, N); S_T may alias S0 (each workgroup reads its rows of S0
+// Grid (H, DV / 4, N); S_T may alias S0 (each workgroup reads its rows of S0
 // before it writes the same rows of S_T).
 template <int DK, int DV>
 __global__ __launch_bounds__(256, 2) void gdn_span_chain_kernel(const float* __restrict__ maps,
@@ -51,7 +56,7 @@ __global__ __launch_bounds__(256, 2) void gdn_span_chain_kernel(const float* __r
     float* sS = sM + DK * LM;                          // [ROWS][DK]
     const int tid = (int)threadIdx.x;
     const int r = tid / Cfg::TPR, c0 = (tid % Cfg::TPR) * CPT;
-    const int row = (int)blockIdx.x * Cfg::ROWS + r, h = (int)blockIdx.y, n = (int)blockIdx.z;
+    const int row = (int)blockIdx.y * Cfg::ROWS + r, h = (int)blockIdx.x, n = (int)blockIdx.z;
     const int64_t srow = (((int64_t)n * H + h) * DV + row) * DK + c0;
     const int64_t mstride = (int64_t)H * (DK + DV) * DK;                 // between spans
     const float* m0 = maps + ((int64_t)n * P * H + h) * (int64_t)(DK + DV) * DK;   // span 0
@@ -138,7 +143,7 @@ struct SpanMfmaCfg {
 // columns of four rows d = 4 g + r) fall in 64 different banks
 __device__ __forceinline__ int span_mchunk(int d, int j) { return j ^ (((d >> 2) & 3) << 2); }
 
-// maps, S0, S_in, S_T as for gdn_span_chain_kernel.  Grid (DV / 16, H, N).
+// maps, S0, S_in, S_T as for gdn_span_chain_kernel.  Grid (H, DV / 16, N).
 template <int DK, int DV>
 __global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain_mfma_kernel(
     const float* __restrict__ maps, const float* S0, int P, int H, float* __restrict__ S_in, float* S_T) {
@@ -150,7 +155,7 @@ __global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain
     const int l = lane_id(), w = wave_id();
     const int n = l & 15, g = l >> 4;
     const int t = w;   // this wave's output tile
-    const int row0 = (int)blockIdx.x * Cfg::ROWS, h = (int)blockIdx.y, sq = (int)blockIdx.z;
+    const int row0 = (int)blockIdx.y * Cfg::ROWS, h = (int)blockIdx.x, sq = (int)blockIdx.z;
     const int64_t mstride = (int64_t)H * (DK + DV) * DK;                      // between spans
     const float* m0 = maps + ((int64_t)sq * P * H + h) * (int64_t)(DK + DV) * DK;   // span 0
     // this lane's piece of tile t (row row0 + n, columns 16 t + 4 g .. + 3)
