@@ -216,17 +216,24 @@ __global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain
         // b_p row row0 + n, columns 16 t + 4 g .. + 3 starts the first chain
         f32x4 acc0 = bcur;
         f32x4 acc1 = zero4(), acc2 = zero4();
-#pragma unroll
-        for (int kt = 0; kt < NT; ++kt) {
-            Op bh, bl, ah, al;
-            split(*sx(p & 1, kt), bh, bl);
-            f32x4 a;
+        // the operands of step kt + 1 are requested before the products of
+        // step kt, so that their LDS latency overlaps those
+        f32x4 sv[2], av[2];
+        auto fetch = [&](int kt, int s) __attribute__((always_inline)) {
+            sv[s] = *sx(p & 1, kt);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int d = 16 * kt + 4 * g + r, c = 16 * t + n;
-                a[r] = sm[d * DK + 4 * span_mchunk(d, c >> 2) + (c & 3)];
+                av[s][r] = sm[d * DK + 4 * span_mchunk(d, c >> 2) + (c & 3)];
             }
-            split(a, ah, al);
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int kt = 0; kt < NT; ++kt) {
+            if (kt + 1 < NT) fetch(kt + 1, (kt + 1) & 1);
+            Op bh, bl, ah, al;
+            split(sv[kt & 1], bh, bl);
+            split(av[kt & 1], ah, al);
             acc0 = KO::mma1(ah, bh, acc0);
             acc1 = KO::mma1(ah, bl, acc1);
             acc2 = KO::mma1(al, bh, acc2);
