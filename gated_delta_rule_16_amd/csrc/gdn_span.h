@@ -133,7 +133,8 @@ struct SpanMfmaCfg {
     static constexpr int NLD = MB / 1024 / WAVES;  // 16-byte loads per lane per span
     static constexpr int SXB = NT * 1024;          // one exchange buffer of S^T tiles
     static constexpr size_t OFF_SX = 2 * (size_t)MB;
-    static constexpr size_t SMEM = OFF_SX + 2 * (size_t)SXB;
+    static constexpr size_t OFF_B = OFF_SX + 2 * (size_t)SXB;   // b_p, 16 bytes per lane
+    static constexpr size_t SMEM = OFF_B + 2 * (size_t)THREADS * 16;
     static_assert(DK % 64 == 0 && (MB / 1024) % WAVES == 0 && DV % ROWS == 0 && THREADS <= 1024, "tile shapes");
     static_assert(SMEM <= 160 * 1024, "LDS of one CU");
 };
@@ -166,9 +167,13 @@ __global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain
         return reinterpret_cast<f32x4*>(S_in + ((((int64_t)sq * P + p) * H + h) * DV) * DK + soff);
     };
 
-    // M in registers: piece i of a set is the 16-byte chunk q = (w NLD + i) 64 + l
-    // of M; piece NLD is this lane's piece of b (the first accumulator of its tile)
-    f32x4 m0r[NLD + 1], m1r[NLD + 1];
+    // M in registers: piece i of the set is the 16-byte chunk q = (w NLD + i) 64 + l
+    // of M; piece NLD is this lane's piece of b (the first accumulator of its
+    // tile).  One set, loaded a span ahead and used only to fill LDS (b too):
+    // with two sets, or with b kept in a register, the compiler moved the
+    // newest loads between registers at the loop head, and those moves waited
+    // for loads issued just before the barrier.
+    f32x4 mr[NLD + 1];
     auto m_load = [&](f32x4* mr, int p) __attribute__((always_inline)) {
         const float* mp = m0 + p * mstride;
         mr[NLD] = *reinterpret_cast<const f32x4*>(mp + (int64_t)DK * DK + soff);
@@ -182,6 +187,7 @@ __global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain
             const int q = (w * NLD + i) * 64 + l, d = q / (DK / 4), j = q % (DK / 4);
             *reinterpret_cast<f32x4*>(sm + d * DK + 4 * span_mchunk(d, j)) = mr[i];
         }
+        reinterpret_cast<f32x4*>(smem + Cfg::OFF_B + (size_t)buf * Cfg::THREADS * 16)[w * 64 + l] = mr[NLD];
     };
     auto sx = [&](int buf, int tt) __attribute__((always_inline)) {
         return reinterpret_cast<f32x4*>(smem + Cfg::OFF_SX + (size_t)buf * Cfg::SXB + tt * 1024) + l;
@@ -200,13 +206,10 @@ __global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain
         if (P > 0) *sin_at(0) = s;
         else if (S_T) *reinterpret_cast<f32x4*>(S_T + st_base + soff) = s;
     }
-    f32x4 bcur = zero4();   // b_p of this lane's piece of tile t
     if (P > 0) {
-        m_load(m0r, 0);
-        m_store(m0r, 0);
-        bcur = m0r[NLD];
-        m_load(m1r, min(1, P - 1));
-        m_load(m0r, min(2, P - 1));
+        m_load(mr, 0);
+        m_store(mr, 0);
+        m_load(mr, min(1, P - 1));
     }
     __syncthreads();
 
@@ -214,7 +217,7 @@ __global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain
     auto product = [&](int p) __attribute__((always_inline)) {
         const float* sm = reinterpret_cast<const float*>(smem + (size_t)(p & 1) * Cfg::MB);
         // b_p row row0 + n, columns 16 t + 4 g .. + 3 starts the first chain
-        f32x4 acc0 = bcur;
+        f32x4 acc0 = reinterpret_cast<const f32x4*>(smem + Cfg::OFF_B + (size_t)(p & 1) * Cfg::THREADS * 16)[w * 64 + l];
         f32x4 acc1 = zero4(), acc2 = zero4();
         // the operands of step kt + 1 are requested before the products of
         // step kt, so that their LDS latency overlaps those
@@ -240,17 +243,15 @@ __global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain
         }
         return acc0 + (acc1 + acc2);
     };
-    // a span with a successor: S_in(p + 1) out, M_{p+1} from register set nxt
-    // to the other LDS buffer (its M_{p-1} was read before the last barrier),
-    // the map two spans on into that set (past the end: the last one again).
-    // No branches, so that the waits for each set count only its own loads.
-    auto mid = [&](int p, f32x4* nxt) __attribute__((always_inline)) {
+    // a span with a successor: S_in(p + 1) out, M_{p+1} from the registers to
+    // the other LDS buffer (its M_{p-1} was read before the last barrier), the
+    // next map into the registers (past the end: the last one again)
+    auto mid = [&](int p) __attribute__((always_inline)) {
         const f32x4 s = product(p);
         *sx((p + 1) & 1, t) = s;
         *sin_at(p + 1) = s;
-        m_store(nxt, (p + 1) & 1);
-        bcur = nxt[NLD];
-        m_load(nxt, min(p + 3, P - 1));
+        m_store(mr, (p + 1) & 1);
+        m_load(mr, min(p + 2, P - 1));
         __syncthreads();
     };
     // the last span: S_T
@@ -258,18 +259,8 @@ __global__ __launch_bounds__((SpanMfmaCfg<DK, DV>::THREADS)) void gdn_span_chain
         const f32x4 s = product(p);
         if (S_T) *reinterpret_cast<f32x4*>(S_T + st_base + soff) = s;
     };
-    // two spans per iteration, so that each register set is a fixed one
-    int p = 0;
-    for (; p + 2 < P; p += 2) {
-        mid(p, m1r);
-        mid(p + 1, m0r);
-    }
-    if (p + 1 < P) {
-        mid(p, m1r);
-        last(p + 1);
-    } else if (p < P) {
-        last(p);
-    }
+    for (int p = 0; p + 1 < P; ++p) mid(p);
+    if (P > 0) last(P - 1);
 }
 
 }  // namespace gdn
